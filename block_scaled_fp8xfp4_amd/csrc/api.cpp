@@ -1,0 +1,146 @@
+// C-ABI of the library (include/mxmoe.h): argument validation on the host,
+// then kernel launches on the caller's stream.  Nothing here allocates,
+// synchronizes or reads device memory; every error is reported before the
+// first launch of a call.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "mxmoe.h"
+#include "mx_launch.hpp"
+
+namespace {
+
+thread_local const char* g_variant = "";
+std::atomic<int> g_ffn_path{0};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_EHIP; }
+
+}  // namespace
+
+namespace mx {
+int num_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+}  // namespace mx
+
+extern "C" {
+
+const char* mx_status_string(mx_status s) {
+  switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_EINVAL: return "MX_EINVAL: null pointer, bad shape or value out of range";
+    case MX_EUNSUPPORTED: return "MX_EUNSUPPORTED: valid request that the kernels do not implement";
+    case MX_EWORKSPACE: return "MX_EWORKSPACE: workspace missing or smaller than required";
+    case MX_EHIP: return "MX_EHIP: a HIP launch or runtime call failed";
+    default: return "unknown mx_status";
+  }
+}
+
+const char* mx_last_variant(void) { return g_variant; }
+
+int mx_set_ffn_path(int path) {
+  if (path < 0 || path > 2) return MX_EINVAL;
+  return g_ffn_path.exchange(path);
+}
+
+mx_status mx_quantize(const void* src, int src_dtype, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* sc,
+                      void* stream) {
+  if (!src || !q || !sc) return MX_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return MX_EINVAL;
+  if (src_dtype != MX_IN_F32 && src_dtype != MX_IN_BF16) return MX_EINVAL;
+  if (fmt != MX_FMT_E4M3 && fmt != MX_FMT_E2M1) return MX_EINVAL;
+  if (!aligned(src, 16) || !aligned(q, 16)) return MX_EINVAL;
+  if (rows > 0 && cols / 32 > (int64_t(1) << 40) / rows) return MX_EUNSUPPORTED;
+  const hipError_t e = mx::launch_quantize(src, src_dtype == MX_IN_BF16, rows, cols, fmt == MX_FMT_E2M1, q, sc,
+                                           static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) g_variant = fmt == MX_FMT_E2M1 ? "quantize:e2m1_block32" : "quantize:e4m3_block32";
+  return from_hip(e);
+}
+
+size_t moe_route_workspace_bytes(int T, int E, int k) {
+  (void)k;
+  if (T < 0 || E < 1) return 0;
+  return mx::route_ws_bytes(T, E);
+}
+
+mx_status moe_route(const float* logits, int T, int E, int k, const float* survival, float skip_below,
+                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* perm, int32_t* slot_pos,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || E > mx::MAX_E || k < 1 || k > E || k > mx::MAX_K) return MX_EINVAL;
+  if ((int64_t)T * k >= (int64_t(1) << 31)) return MX_EINVAL;
+  if (!expert_offsets) return MX_EINVAL;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !perm || !slot_pos)) return MX_EINVAL;
+  if (!ws || ws_bytes < mx::route_ws_bytes(T, E)) return MX_EWORKSPACE;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(perm, 4) || !aligned(slot_pos, 4) || !aligned(survival, 4) || !aligned(ws, 256))
+    return MX_EINVAL;
+  const char* v = "";
+  const hipError_t e = mx::launch_route(logits, T, E, k, survival, skip_below, topk_ids, topk_w, expert_offsets, perm,
+                                        slot_pos, ws, static_cast<hipStream_t>(stream), &v);
+  if (e == hipSuccess) g_variant = v;
+  return from_hip(e);
+}
+
+mx_status moe_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h, size_t* off_o) {
+  if (T < 0 || H < 128 || I < 32 || k < 1 || !off_q || !off_q_sc || !off_h || !off_o) return MX_EINVAL;
+  mx::ffn_ws_layout(T, H, I, k, off_q, off_q_sc, off_h, off_o);
+  return MX_OK;
+}
+
+size_t moe_expert_ffn_workspace_bytes(int T, int H, int E, int I, int k) {
+  if (T < 0 || H < 128 || E < 1 || I < 32 || k < 1) return 0;
+  return mx::ffn_ws_bytes(T, H, E, I, k);
+}
+
+mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H, const float* topk_w,
+                         const int32_t* expert_offsets, const int32_t* perm, const int32_t* slot_pos, int k,
+                         const uint8_t* w13, const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int E,
+                         int I, float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > mx::MAX_K || E < 1 || E > mx::MAX_E || H < 128 || I < 32) return MX_EINVAL;
+  if (H % 32 != 0 || I % 32 != 0) return MX_EINVAL;
+  if (H % 128 != 0 || H > 128 * 8 * mx::MAX_PARTS || I > mx::MAX_I) return MX_EUNSUPPORTED;
+  if ((int64_t)T * k >= (int64_t(1) << 31)) return MX_EINVAL;
+  if (!x || !x_sc || !topk_w || !expert_offsets || !perm || !slot_pos || !w13 || !w13_sc || !w2 || !w2_sc || !y)
+    return MX_EINVAL;
+  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(x_sc, 4) ||
+      !aligned(w13_sc, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) || !aligned(perm, 4) ||
+      !aligned(slot_pos, 4))
+    return MX_EINVAL;
+  if (!ws || ws_bytes < mx::ffn_ws_bytes(T, H, E, I, k)) return MX_EWORKSPACE;
+  if (!aligned(ws, 256)) return MX_EINVAL;
+  if (T == 0) { g_variant = "ffn:empty"; return MX_OK; }
+  const mx::FfnArgs a{x, x_sc, T, H, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y};
+  const char* v = "";
+  const hipError_t e = mx::launch_ffn(a, ws, g_ffn_path.load(), static_cast<hipStream_t>(stream), &v);
+  if (e == hipSuccess) g_variant = v;
+  return from_hip(e);
+}
+
+mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc, int M, int N,
+                         int K, void* y, int y_dtype, void* stream) {
+  if (!a || !a_sc || !w || !w_sc || !y) return MX_EINVAL;
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0) return MX_EINVAL;
+  if (y_dtype != MX_OUT_BF16 && y_dtype != MX_OUT_F32) return MX_EINVAL;
+  if (N % 16 != 0 || K % 128 != 0 || K > 128 * 8 * mx::MAX_PARTS) return MX_EUNSUPPORTED;
+  if ((int64_t)M * N >= (int64_t(1) << 31) || (int64_t)M * K >= (int64_t(1) << 40)) return MX_EUNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(a_sc, 4) || !aligned(w_sc, 4) || !aligned(y, 4)) return MX_EINVAL;
+  const char* v = "";
+  const hipError_t e =
+      mx::launch_block_gemm(a, a_sc, w, w_sc, M, N, K, y, y_dtype == MX_OUT_BF16, static_cast<hipStream_t>(stream), &v);
+  if (e == hipSuccess) g_variant = v;
+  return from_hip(e);
+}
+
+}  // extern "C"

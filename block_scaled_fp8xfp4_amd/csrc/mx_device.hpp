@@ -1,0 +1,127 @@
+// Device-side building blocks shared by the HIP kernels of this library.
+//
+// Scaled matrix-core step (gfx950 V_MFMA_SCALE_F32_16X16X128_F8F6F4), as
+// measured on MI355X with a one-tile probe against the definition:
+//   - A is 16 rows x 128 K, B is 128 K x 16 columns, C/D 16 x 16 fp32.
+//   - Lane l serves row (A) / column (B) l % 16 and lane group g = l / 16.
+//   - FP8 operand (8 dwords per lane): bytes 0..15 hold K = 16g + [0,16),
+//     bytes 16..31 hold K = 64 + 16g + [0,16).
+//   - FP4 operand (low 4 dwords per lane): 32 nibbles = K = 32g + [0,32),
+//     element 2i in the low nibble of byte i.
+//   - Scale operand: byte 0 of the lane's scale dword is the E8M0 scale of
+//     K block g (K = 32g + [0,32)) of that lane's row / column; 127 = 1.0.
+//   - D: lane l holds column l % 16, rows 4g + r in register r.
+// The FP8 encoding is OCP E4M3 (bias 7, max 448).
+//
+// Canonical reduction order used by every GEMM here (decode and prefill
+// alike, so that a row's result never depends on the path or the batch):
+//   K is cut into steps of 128 (step m covers K blocks 4m..4m+3 of 32); a
+//   step whose blocks run past K is padded with zero elements in registers.
+//   Steps are grouped in parts of KPART_STEPS consecutive steps; each part is
+//   a chain of MFMAs started from zero, and the parts are added left to
+//   right in fp32: total = ((p0 + p1) + p2) + ...
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+constexpr int KSTEP = 128;        // K per MFMA step
+constexpr int KPART_STEPS = 8;    // steps per part (K = 1024)
+constexpr int KPART = KSTEP * KPART_STEPS;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// E4M3 (A) x E2M1 (B) step.
+__device__ __forceinline__ v4f mfma_fp8_fp4(const v8i& a, const v8i& b, v4f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, (int)sa, 0, (int)sb);
+}
+// E4M3 (A) x E4M3 (B) step.
+__device__ __forceinline__ v4f mfma_fp8_fp8(const v8i& a, const v8i& b, v4f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Block-32 quantization (OCP MX v1.0 conversion): shared scale
+// X = 2^(floor(log2 amax) - emax) as an E8M0 code clamped to [0, 254]
+// (amax == 0 -> 0); elements round to nearest even, saturate, keep the sign.
+__device__ __forceinline__ uint32_t e8m0_code_for_amax(float amax, int emax) {
+  const int be = (int)((__float_as_uint(amax) >> 23) & 0xFF);   // 0 for zero / subnormal
+  int c = be - emax;
+  c = c < 0 ? 0 : c;
+  return (uint32_t)(c > 254 ? 254 : c);
+}
+
+// fp32 -> E4M3 code under scale code sc.
+__device__ __forceinline__ uint32_t encode_e4m3(float v, uint32_t sc) {
+  const float t = __builtin_ldexpf(v, 127 - (int)sc);           // exact power-of-two scaling
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80;
+  const float a = __builtin_fabsf(t);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7E;                                                 // saturate
+  } else if (a < 0.015625f) {                                    // below 2^-6: subnormal grid of 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);                 // 8 -> 0x08 = 2^-6
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);                            // round mantissa to 3 bits, ties even
+    const uint32_t e = (b >> 23) - 127u + 7u;
+    code = (e << 3) | ((b >> 20) & 7u);
+  }
+  return code | sign;
+}
+
+// fp32 -> E2M1 code (0..15) under scale code sc.
+__device__ __forceinline__ uint32_t encode_e2m1(float v, uint32_t sc) {
+  const float t = __builtin_ldexpf(v, 127 - (int)sc);
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8;
+  const float a = __builtin_fabsf(t);
+  uint32_t code;
+  if (a >= 6.0f) {
+    code = 7;
+  } else if (a < 1.0f) {                                         // subnormal grid of 0.5
+    code = (uint32_t)__builtin_rintf(a * 2.0f);                   // 2 -> code 2 = 1.0
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x1FFFFFu + ((b >> 22) & 1u);                           // round mantissa to 1 bit, ties even
+    const uint32_t e = (b >> 23) - 127u + 1u;
+    code = (e << 1) | ((b >> 22) & 1u);
+  }
+  return code | sign;
+}
+
+// SwiGLU of one gate/up pair in fp32: silu(g) * u, silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// Quantize 32 fp32 values to E4M3: writes 32 code bytes as 8 dwords, returns the scale code.
+__device__ __forceinline__ uint32_t quantize32_e4m3(const float* v, uint32_t* out8) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+  const uint32_t sc = e8m0_code_for_amax(amax, 8);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d |= encode_e4m3(v[4 * w + i], sc) << (8 * i);
+    out8[w] = d;
+  }
+  return sc;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace mx

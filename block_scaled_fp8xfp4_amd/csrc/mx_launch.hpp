@@ -1,0 +1,39 @@
+// Internal launchers behind the C-ABI (api.cpp validates, these launch).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mx {
+
+// limits the kernels are built for (checked on the host before any launch)
+constexpr int MAX_E = 1024;      // experts (route LDS lists)
+constexpr int MAX_K = 16;        // top-k
+constexpr int MAX_I = 2048;      // expert intermediate (decode LDS staging)
+constexpr int MAX_PARTS = 16;    // K parts of 1024 -> H, K <= 16384
+constexpr int ROUTE_CHUNK = 256; // rows per bucketing chunk
+
+hipError_t launch_quantize(const void* src, bool bf16, int64_t rows, int64_t cols, bool fp4,
+                           uint8_t* q, uint8_t* sc, hipStream_t stream);
+
+size_t route_ws_bytes(int T, int E);
+hipError_t launch_route(const float* logits, int T, int E, int k, const float* survival, float skip_below,
+                        int32_t* ids, float* w, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                        void* ws, hipStream_t stream, const char** variant);
+
+struct FfnArgs {
+  const uint8_t* x; const uint8_t* x_sc; int T; int H;
+  const float* topk_w; const int32_t* offsets; const int32_t* perm; const int32_t* slot_pos; int k;
+  const uint8_t* w13; const uint8_t* w13_sc; const uint8_t* w2; const uint8_t* w2_sc; int E; int I;
+  float* y;
+};
+size_t ffn_ws_bytes(int T, int H, int E, int I, int k);
+void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h, size_t* off_o);
+hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant);
+
+hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,
+                             int M, int N, int K, void* y, bool bf16_out, hipStream_t stream, const char** variant);
+
+int num_cus();
+
+}  // namespace mx

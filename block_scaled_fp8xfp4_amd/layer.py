@@ -1,0 +1,77 @@
+"""Device-side convenience wrapper around the C-ABI: uploads and quantizes a
+MoE layer on the GPU (with the library's own quantizer kernel) and owns the
+route / FFN workspaces.  Every computation is a libmxmoe.so call."""
+import numpy as np
+import torch
+
+from . import mxmoe
+
+
+def _dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)) if isinstance(a, np.ndarray) else a
+    return t.to("cuda", dtype=dtype) if dtype is not None else t.to("cuda")
+
+
+def quantize(v, fmt):
+    """fp32/bf16 device tensor [..., cols] -> (codes, scales) device uint8 tensors."""
+    cols = v.shape[-1]
+    rows = v.numel() // cols
+    qcols = cols if fmt == mxmoe.MX_FMT_E4M3 else cols // 2
+    q = torch.empty(v.shape[:-1] + (qcols,), dtype=torch.uint8, device=v.device)
+    sc = torch.empty(v.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=v.device)
+    if rows:
+        mxmoe.mx_quantize(v.contiguous(), q, sc, fmt)
+    return q, sc
+
+
+def quantize_experts(w_host, chunk=16):
+    """fp32 host weights [E, R, C] -> packed E2M1 [E, R, C/2] + E8M0 [E, R, C/32] on the GPU."""
+    E, R, C = w_host.shape
+    q = torch.empty((E, R, C // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((E, R, C // 32), dtype=torch.uint8, device="cuda")
+    for e0 in range(0, E, chunk):
+        e1 = min(E, e0 + chunk)
+        src = _dev(w_host[e0:e1])
+        mxmoe.mx_quantize(src, q[e0:e1], sc[e0:e1], mxmoe.MX_FMT_E2M1)
+    torch.cuda.synchronize()
+    return q, sc
+
+
+class Route:
+    def __init__(self, T, E, k):
+        dev = "cuda"
+        self.T, self.E, self.k = T, E, k
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+        self.slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.ws = torch.empty(mxmoe.moe_route_workspace_bytes(T, E, k), dtype=torch.uint8, device=dev)
+
+    def __call__(self, logits, survival=None, skip_below=0.2, stream=None):
+        mxmoe.moe_route(logits, self.k, survival, skip_below, self.ids, self.w, self.offsets, self.perm,
+                        self.slot_pos, self.ws, stream)
+        return self
+
+
+class ExpertFFN:
+    def __init__(self, T, H, E, I, k):
+        self.T, self.H, self.E, self.I, self.k = T, H, E, I, k
+        self.ws = torch.empty(mxmoe.moe_expert_ffn_workspace_bytes(T, H, E, I, k), dtype=torch.uint8, device="cuda")
+        self.y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+
+    def __call__(self, x, x_sc, route, w13, w13_sc, w2, w2_sc, stream=None):
+        mxmoe.moe_expert_ffn(x, x_sc, route.w, route.offsets, route.perm, route.slot_pos, self.k, w13, w13_sc,
+                             w2, w2_sc, self.E, self.I, self.y, self.ws, stream)
+        return self.y
+
+    def ws_views(self):
+        """Workspace regions as tensors: q [T*k, I], q_sc [T*k, I/32] (uint8),
+        h [T*k, 2I] (fp32, decode path only) and o [T*k, H] (fp32)."""
+        Tk, H, I = self.T * self.k, self.H, self.I
+        oq, oqs, oh, oo = mxmoe.moe_ws_layout(self.T, H, I, self.k)
+        q = self.ws[oq:oq + Tk * I].view(Tk, I)
+        sc = self.ws[oqs:oqs + Tk * (I // 32)].view(Tk, I // 32)
+        h = self.ws[oh:oh + Tk * 2 * I * 4].view(torch.float32).view(Tk, 2 * I)
+        o = self.ws[oo:oo + Tk * H * 4].view(torch.float32).view(Tk, H)
+        return q, sc, h, o

@@ -1,0 +1,141 @@
+"""Thin ctypes binding of libmxmoe.so (include/mxmoe.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's kernels.  The
+binding raises if the library is missing, never falls back to another path.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxmoe.so")
+
+MX_OK, MX_EINVAL, MX_EUNSUPPORTED, MX_EWORKSPACE, MX_EHIP = 0, -1, -2, -3, -4
+MX_FMT_E4M3, MX_FMT_E2M1 = 0, 1
+MX_IN_F32, MX_IN_BF16 = 0, 1
+MX_OUT_BF16, MX_OUT_F32 = 0, 1
+
+# every entry point declared in include/mxmoe.h
+EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "moe_expert_ffn_workspace_bytes",
+           "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
+           "mx_last_variant", "mx_set_ffn_path")
+
+_lib = None
+
+
+class MXError(RuntimeError):
+    def __init__(self, status, name):
+        self.status = status
+        super().__init__(f"{name}: {status_string(status)} ({status})")
+
+
+def load():
+    """Load libmxmoe.so (built by block_scaled_fp8xfp4_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m block_scaled_fp8xfp4_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    lib.mx_quantize.restype = I32
+    lib.mx_quantize.argtypes = [P, I32, I64, I64, I32, P, P, P]
+    lib.moe_route_workspace_bytes.restype = SZ
+    lib.moe_route_workspace_bytes.argtypes = [I32, I32, I32]
+    lib.moe_route.restype = I32
+    lib.moe_route.argtypes = [P, I32, I32, I32, P, F32, P, P, P, P, P, P, SZ, P]
+    lib.moe_expert_ffn_workspace_bytes.restype = SZ
+    lib.moe_expert_ffn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.moe_ws_layout.restype = I32
+    lib.moe_ws_layout.argtypes = [I32, I32, I32, I32, P, P, P, P]
+    lib.moe_expert_ffn.restype = I32
+    lib.moe_expert_ffn.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, P, I32, I32, P, P, SZ, P]
+    lib.fp8_block_gemm.restype = I32
+    lib.fp8_block_gemm.argtypes = [P, P, P, P, I32, I32, I32, P, I32, P]
+    lib.mx_status_string.restype = ctypes.c_char_p
+    lib.mx_status_string.argtypes = [I32]
+    lib.mx_last_variant.restype = ctypes.c_char_p
+    lib.mx_last_variant.argtypes = []
+    lib.mx_set_ffn_path.restype = I32
+    lib.mx_set_ffn_path.argtypes = [I32]
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().mx_status_string(status).decode()
+
+
+def last_variant():
+    return load().mx_last_variant().decode()
+
+
+def set_ffn_path(path):
+    """0 = automatic, 1 = decode kernels, 2 = prefill kernels; returns the previous setting."""
+    r = load().mx_set_ffn_path(int(path))
+    if r < 0:
+        raise MXError(r, "mx_set_ffn_path")
+    return r
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status, name):
+    if status != MX_OK:
+        raise MXError(status, name)
+
+
+# ------------------------------------------------------------------ calls
+def mx_quantize(src, q, sc, fmt, stream=None):
+    """Quantize src [rows, cols] (fp32 or bf16 tensor) into q / sc (uint8 tensors)."""
+    import torch
+    dt = {torch.float32: MX_IN_F32, torch.bfloat16: MX_IN_BF16}[src.dtype]
+    cols = src.shape[-1]
+    rows = src.numel() // cols if cols else 0
+    _check(load().mx_quantize(_ptr(src), dt, rows, cols, fmt, _ptr(q), _ptr(sc), _stream(stream)), "mx_quantize")
+
+
+def moe_route_workspace_bytes(T, E, k):
+    return load().moe_route_workspace_bytes(T, E, k)
+
+
+def moe_route(logits, k, survival, skip_below, topk_ids, topk_w, expert_offsets, perm, slot_pos, ws, stream=None):
+    T, E = logits.shape
+    _check(load().moe_route(_ptr(logits), T, E, k, _ptr(survival), float(skip_below), _ptr(topk_ids), _ptr(topk_w),
+                            _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream)), "moe_route")
+
+
+def moe_expert_ffn_workspace_bytes(T, H, E, I, k):
+    return load().moe_expert_ffn_workspace_bytes(T, H, E, I, k)
+
+
+def moe_ws_layout(T, H, I, k):
+    """Byte offsets (q, q_sc, h, o) of the FFN workspace regions."""
+    offs = [ctypes.c_size_t() for _ in range(4)]
+    _check(load().moe_ws_layout(T, H, I, k, *[ctypes.byref(o) for o in offs]), "moe_ws_layout")
+    return tuple(o.value for o in offs)
+
+
+def moe_expert_ffn(x, x_sc, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y, ws,
+                   stream=None):
+    T, H = x.shape
+    _check(load().moe_expert_ffn(_ptr(x), _ptr(x_sc), T, H, _ptr(topk_w), _ptr(expert_offsets), _ptr(perm),
+                                 _ptr(slot_pos), k, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), E, I, _ptr(y),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_expert_ffn")
+
+
+def fp8_block_gemm(a, a_sc, w, w_sc, y, y_dtype, stream=None):
+    M, K = a.shape
+    N = w.shape[0]
+    _check(load().fp8_block_gemm(_ptr(a), _ptr(a_sc), _ptr(w), _ptr(w_sc), M, N, K, _ptr(y), y_dtype,
+                                 _stream(stream)), "fp8_block_gemm")

@@ -1,0 +1,176 @@
+/*
+ * mxmoe.h -- block-scaled routed-expert MoE layer and dense block-32 FP8
+ * projection for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * What is computed (sources are the three web pages on serving DeepSeek V4.1
+ * Flash on DGX Spark; the element/scale encodings are those of the OCP
+ * Microscaling Formats v1.0 specification, which the pages' "MXFP8"/"MXFP4"
+ * names refer to):
+ *   - "New Deepseek 4.1 flash recipe" forum thread, post #6, "How it works":
+ *     routed experts with FP8 activations x FP4 weights on block-scaled MMAs,
+ *     dense MXFP8 projections; post #6, "Why TileLang": MoE top-k gate,
+ *     SwiGLU and per-block FP8/FP4 quantization casts, reductions in a fixed
+ *     order so a row's result does not depend on its batch.
+ *   - same thread, post #2, "What changed": verification rows whose estimated
+ *     survival is below 0.2 skip the expert weight reads.
+ *   - spark-ds41f README, "Current baseline": block-32 FP8 projections,
+ *     FP8 x FP4 routed experts, batch-independent results, decode and prefill.
+ *   - DeepSeek-V4.1-Flash-4x-DGX-Spark-TP4 README, settings table, row
+ *     "Experts": per-slot buffer and a fixed-order sum instead of atomics.
+ *
+ * Encodings (all byte arrays are row-major, contiguous):
+ *   FP8  = E4M3 (bias 7, max 448, S.1111.111 NaN), one byte per element.
+ *   FP4  = E2M1 (values 0, .5, 1, 1.5, 2, 3, 4, 6 and negatives), two per
+ *          byte, element 2j in the LOW nibble of byte j.
+ *   SC   = E8M0 scale 2^(c-127), one byte per 32 consecutive elements along
+ *          the reduction (K) dimension; code 255 (NaN) is not supported.
+ *   Value of an element = decode(element) * decode(its block's SC).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory),
+ *     16-byte aligned unless stated; the caller owns every buffer.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *     are asynchronous: they validate on the host, launch kernels on
+ *     `stream` and return.  They never allocate, free, synchronize or read
+ *     device memory on the host, so they can be captured in a HIP graph.
+ *   - Every argument is checked on the host BEFORE any launch; on error
+ *     nothing is launched and a negative status is returned.  There is no
+ *     fallback path and no printing; mx_status_string() names the error.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified (but
+ *     deterministic) results.
+ *   - Results are deterministic: the same inputs give the same bits, and
+ *     each output row is bitwise independent of the other rows in the batch.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int mx_status;
+#define MX_OK            0
+#define MX_EINVAL       -1   /* null pointer, bad shape or range */
+#define MX_EUNSUPPORTED -2   /* valid request the kernels do not implement */
+#define MX_EWORKSPACE   -3   /* workspace missing or too small */
+#define MX_EHIP         -4   /* a HIP launch or runtime call failed */
+
+#define MX_FMT_E4M3 0        /* FP8 elements */
+#define MX_FMT_E2M1 1        /* FP4 elements, packed two per byte */
+
+#define MX_IN_F32  0         /* fp32 source values */
+#define MX_IN_BF16 1         /* bf16 source values (uint16 bit patterns) */
+
+#define MX_OUT_BF16 0        /* bf16 output, round to nearest even from fp32 */
+#define MX_OUT_F32  1        /* fp32 output */
+
+/*
+ * Block-32 quantizer (the per-block FP8/FP4 casts of post #6, "Why TileLang").
+ * src: [rows][cols] fp32 or bf16 (src_dtype).  cols % 32 == 0.
+ * q:   E4M3 [rows][cols] bytes, or E2M1 [rows][cols/2] packed bytes.
+ * sc:  E8M0 [rows][cols/32].
+ * Scale rule (OCP MX v1.0): X = 2^(floor(log2(amax)) - emax) with emax = 8
+ * (E4M3) or 2 (E2M1), clamped to codes 0..254; amax == 0 gives code 0.
+ * Elements: round to nearest, ties to even, saturate to +-448 / +-6, sign
+ * kept (negative values that round to zero give -0).  The routed-expert FFN
+ * uses the same device routine for its FP8 requant of the intermediate.
+ * src and q must be 16-byte aligned; sc needs no alignment.
+ */
+mx_status mx_quantize(const void* src, int src_dtype, int64_t rows, int64_t cols, int fmt,
+                      uint8_t* q, uint8_t* sc, void* stream);
+
+/*
+ * Top-k gate + bucketing (post #6 "How it works" item 3: the MoE top-k gate;
+ * post #2 "What changed": dead verification rows; TP4 README "Experts": the
+ * route planner and per-slot buffer).
+ * logits:   fp32 [T][E].  1 <= k <= min(E, 16), E <= 1024, T >= 0.
+ * survival: fp32 [T] or NULL (all rows live).  Row t is dead iff
+ *           survival[t] < skip_below (strict).  Dead rows keep their ids and
+ *           weights but join no bucket; their MoE output rows are +0.
+ * Outputs (all device):
+ *   topk_ids       int32 [T][k]: experts ordered by (logit descending,
+ *                  expert index ascending); exact ties go to the lower index.
+ *   topk_w         fp32 [T][k]: softmax over the k selected logits,
+ *                  w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+ *   expert_offsets int32 [E+1]: first bucket position of each expert;
+ *                  expert_offsets[E] = P, the number of live pairs.
+ *   perm           int32 [T*k]: perm[p] = t*k + j for p < P (pairs sorted by
+ *                  expert, then token ascending), -1 for p >= P.
+ *   slot_pos       int32 [T][k]: the bucket position p of pair (t, j), or -1.
+ * ws: device scratch of at least moe_route_workspace_bytes(T, E, k) bytes
+ *     (256-byte aligned); contents on entry are ignored.
+ */
+size_t    moe_route_workspace_bytes(int T, int E, int k);
+mx_status moe_route(const float* logits, int T, int E, int k,
+                    const float* survival, float skip_below,
+                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                    int32_t* perm, int32_t* slot_pos,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Routed-expert FFN + fixed-order combine (post #6 "How it works" item 2:
+ * routed experts, FP8 activations x FP4 weights; "Why TileLang": SwiGLU,
+ * FP8 quantization, fixed-order reductions; TP4 README "Experts").
+ * x      FP8 [T][H],  x_sc  SC [T][H/32]          activations
+ * w13    FP4 [E][2I][H/2], w13_sc SC [E][2I][H/32] rows [0, I) gate, [I, 2I) up
+ * w2     FP4 [E][H][I/2],  w2_sc  SC [E][H][I/32]  down projection
+ * topk_w, expert_offsets, perm, slot_pos: as written by moe_route (k slots).
+ * y      fp32 [T][H]: y_t = sum_{j=0..k-1} w_tj * o_tj, added in slot order,
+ *        where o_tj = down(requant_fp8(silu(gate) * up)) of pair (t, j);
+ *        rows with no live pair are +0.
+ * Every product is accumulated in fp32 on the matrix cores in one fixed
+ * order per output element, the same for every batch size and path.
+ * Supported: H % 128 == 0, I % 32 == 0, 1 <= k <= 16, T*k < 2^31.
+ * ws: device scratch of at least moe_expert_ffn_workspace_bytes(T,H,E,I,k)
+ *     bytes (256-byte aligned).  Its layout is documented for diagnostics
+ *     and filled in by moe_ws_layout(): the FP8 intermediate q [T*k][I] and
+ *     its scales SC [T*k][I/32] (row p = bucket position, written by every
+ *     path), the fp32 gate/up values h [T*k][2I] (written by the decode
+ *     path only) and the fp32 per-slot outputs o [T*k][H] (every path).
+ */
+size_t    moe_expert_ffn_workspace_bytes(int T, int H, int E, int I, int k);
+mx_status moe_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h,
+                        size_t* off_o);
+mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H,
+                         const float* topk_w, const int32_t* expert_offsets,
+                         const int32_t* perm, const int32_t* slot_pos, int k,
+                         const uint8_t* w13, const uint8_t* w13_sc,
+                         const uint8_t* w2, const uint8_t* w2_sc, int E, int I,
+                         float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense block-32 FP8 GEMM (post #2 "Known issues and next steps": dense FP8
+ * GEMMs are the largest remaining decode lever; post #6 "How it works":
+ * MXFP8 projections, decode rows on small row tiles).
+ * a FP8 [M][K] + a_sc SC [M][K/32];  w FP8 [N][K] + w_sc SC [N][K/32].
+ * y[m][n] = sum_k a[m][k] * w[n][k] (decoded), fp32 accumulate in one fixed
+ * order per element; y is [M][N] bf16 (MX_OUT_BF16, RNE of the fp32 result)
+ * or fp32 (MX_OUT_F32).  Supported: K % 128 == 0, N % 16 == 0, M >= 1.
+ */
+mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc,
+                         const uint8_t* w, const uint8_t* w_sc,
+                         int M, int N, int K, void* y, int y_dtype, void* stream);
+
+/* Name of a status code (static string). */
+const char* mx_status_string(mx_status s);
+
+/* Kernel variants launched by this thread's last successful call (static,
+ * thread-local string), so that a caller can check which path ran. */
+const char* mx_last_variant(void);
+
+/*
+ * Path selection for moe_expert_ffn: 0 = automatic (by T*k), 1 = decode
+ * kernels (16-row tiles, weights streamed straight to registers), 2 =
+ * prefill kernels (64-row tiles staged through LDS).  Both paths give
+ * bitwise identical results; this exists so tests can prove it.  Process-
+ * wide; returns the previous setting, or MX_EINVAL for other values.
+ */
+int mx_set_ffn_path(int path);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXMOE_H */

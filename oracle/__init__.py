@@ -52,7 +52,11 @@ def _load():
     lib.or_moe_rows.restype = i32
     lib.or_moe_rows.argtypes = [P, P, i32, P, P, P, i32, P, P, P, P, i32, i32, P, i32, P, i32]
     lib.or_pair_ffn.restype = i32
-    lib.or_pair_ffn.argtypes = [P, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P]
+    lib.or_pair_ffn.argtypes = [P, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P]
+    lib.or_down_combine.restype = i32
+    lib.or_down_combine.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, P, i32, P, i32]
+    lib.or_swiglu_requant.restype = i32
+    lib.or_swiglu_requant.argtypes = [P, i64, i32, P, P, P]
     lib.or_block_gemm.restype = i32
     lib.or_block_gemm.argtypes = [P, P, P, P, i32, i32, P, i32, P, i32]
     lib.or_f32_to_bf16.restype = None
@@ -164,18 +168,47 @@ def moe_rows(x, x_sc, ids, w, live, w13, w13_sc, w2, w2_sc, rows=None, threads=0
 
 
 def pair_ffn(x, x_sc, t, e, w13, w13_sc, w2, w2_sc):
-    """One (token, expert) pair with intermediates: dict(h, q, q_sc, o)."""
+    """One (token, expert) pair with intermediates: dict(h, a, q, q_sc, o)."""
     x, x_sc = _c(x, np.uint8), _c(x_sc, np.uint8)
     H = x.shape[1]
     I = w13.shape[1] // 2
     w13, w13_sc, w2, w2_sc = (_c(a, np.uint8) for a in (w13, w13_sc, w2, w2_sc))
     h = np.empty(2 * I, np.float32)
+    a = np.empty(I, np.float32)
     q = np.empty(I, np.uint8)
     q_sc = np.empty(I // 32, np.uint8)
     o = np.empty(H, np.float32)
     _load().or_pair_ffn(_p(x), _p(x_sc), H, int(t), int(e), _p(w13), _p(w13_sc), _p(w2), _p(w2_sc),
-                        I, _p(h), _p(q), _p(q_sc), _p(o))
-    return dict(h=h, q=q, q_sc=q_sc, o=o)
+                        I, _p(h), _p(a), _p(q), _p(q_sc), _p(o))
+    return dict(h=h, a=a, q=q, q_sc=q_sc, o=o)
+
+
+def swiglu_requant(h):
+    """fp32 gate/up rows h [n, 2I] -> (q [n, I], q_sc [n, I/32], a [n, I])."""
+    h = _c(h, np.float32)
+    n, twoI = h.shape
+    I = twoI // 2
+    q = np.empty((n, I), np.uint8)
+    q_sc = np.empty((n, I // 32), np.uint8)
+    a = np.empty((n, I), np.float32)
+    if _load().or_swiglu_requant(_p(h), n, I, _p(q), _p(q_sc), _p(a)):
+        raise ValueError("I must be a multiple of 32")
+    return q, q_sc, a
+
+
+def down_combine(q, q_sc, slot_pos, ids, w, w2, w2_sc, rows=None, threads=0):
+    """y [len(rows), H] from a given FP8 intermediate q [P, I] (bucket-position rows)."""
+    q, q_sc = _c(q, np.uint8), _c(q_sc, np.uint8)
+    slot_pos, ids, w = _c(slot_pos, np.int32), _c(ids, np.int32), _c(w, np.float32)
+    w2, w2_sc = _c(w2, np.uint8), _c(w2_sc, np.uint8)
+    E, H, I = w2.shape[0], w2.shape[1], 2 * w2.shape[2]
+    T, k = ids.shape
+    rows = np.arange(T, dtype=np.int32) if rows is None else _c(rows, np.int32)
+    y = np.empty((len(rows), H), np.float32)
+    if _load().or_down_combine(_p(q), _p(q_sc), _p(slot_pos), _p(ids), _p(w), k, _p(w2), _p(w2_sc), H, E, I,
+                               _p(rows), len(rows), _p(y), threads):
+        raise ValueError("bad down_combine arguments")
+    return y
 
 
 # ------------------------------------------------------------- dense GEMM

@@ -165,18 +165,14 @@ struct Layer {
   const uint8_t* w2; const uint8_t* w2_sc; int I;
 };
 
-// One routed pair (token t, expert e): gate/up projection, SwiGLU, FP8 requant
-// of the intermediate in blocks of 32, down projection.  Outputs o[H] (fp32)
-// and, when non-null, the diagnostics h[2I], q[I], q_sc[I/32].
-void pair_ffn(const Layer& L, int t, int e, float* o, float* h_out, uint8_t* q_out, uint8_t* qsc_out) {
+// Gate/up projection of token t through expert e: h[2I] (fp32), rows [0, I)
+// of W13 are the gate, rows [I, 2I) the up projection.
+void gate_up(const Layer& L, int t, int e, float* h) {
   const int H = L.H, I = L.I;
   std::vector<double> xv(H);
   const uint8_t* xr = L.x + int64_t(t) * H;
   const uint8_t* xs = L.x_sc + int64_t(t) * (H / 32);
   for (int k = 0; k < H; ++k) xv[k] = e4m3_value(xr[k]) * e8m0_value(xs[k / 32]);
-
-  // gate/up: rows [0, I) of W13 are the gate, rows [I, 2I) the up projection.
-  std::vector<float> h(2 * I);
   for (int n = 0; n < 2 * I; ++n) {
     const int64_t row = int64_t(e) * 2 * I + n;
     const uint8_t* wr = L.w13 + row * (H / 2);
@@ -185,21 +181,26 @@ void pair_ffn(const Layer& L, int t, int e, float* o, float* h_out, uint8_t* q_o
     for (int k = 0; k < H; ++k) acc += xv[k] * (e2m1_value(fp4_nibble(wr, k)) * e8m0_value(ws[k / 32]));
     h[n] = float(acc);
   }
+}
 
-  // SwiGLU: a = silu(gate) * up, silu(g) = g / (1 + exp(-g)), evaluated in double.
+// SwiGLU of h (a = silu(gate) * up, silu(g) = g / (1 + exp(-g)), in double,
+// rounded to fp32), then the requant of the intermediate to FP8 E4M3 with one
+// E8M0 scale per 32 values.  a_out (optional) receives the fp32 a.
+void swiglu_requant(const float* h, int I, uint8_t* q, uint8_t* qsc, float* a_out) {
   std::vector<float> a(I);
   for (int i = 0; i < I; ++i) {
     const double g = h[i], u = h[I + i];
     a[i] = float(g / (1.0 + std::exp(-g)) * u);
   }
-
-  // Requant of the intermediate to FP8 E4M3 with one E8M0 scale per 32 values.
-  std::vector<uint8_t> q(I), qsc(I / 32);
   for (int b = 0; b < I / 32; ++b) qsc[b] = quantize_block(&a[b * 32], 32, grid_e4m3(), &q[b * 32]);
+  if (a_out) std::memcpy(a_out, a.data(), sizeof(float) * I);
+}
+
+// Down projection of one intermediate row (codes q, scales qsc) through expert e: o[H].
+void down(const Layer& L, const uint8_t* q, const uint8_t* qsc, int e, float* o) {
+  const int H = L.H, I = L.I;
   std::vector<double> av(I);
   for (int i = 0; i < I; ++i) av[i] = e4m3_value(q[i]) * e8m0_value(qsc[i / 32]);
-
-  // down projection over K = I.
   for (int n = 0; n < H; ++n) {
     const int64_t row = int64_t(e) * H + n;
     const uint8_t* wr = L.w2 + row * (I / 2);
@@ -208,9 +209,28 @@ void pair_ffn(const Layer& L, int t, int e, float* o, float* h_out, uint8_t* q_o
     for (int k = 0; k < I; ++k) acc += av[k] * (e2m1_value(fp4_nibble(wr, k)) * e8m0_value(ws[k / 32]));
     o[n] = float(acc);
   }
+}
+
+// One routed pair (token t, expert e): gate/up, SwiGLU, requant, down.
+// Outputs o[H] and, when non-null, the diagnostics h[2I], a[I], q[I], q_sc[I/32].
+void pair_ffn(const Layer& L, int t, int e, float* o, float* h_out, float* a_out, uint8_t* q_out, uint8_t* qsc_out) {
+  const int I = L.I;
+  std::vector<float> h(2 * I);
+  std::vector<uint8_t> q(I), qsc(I / 32);
+  gate_up(L, t, e, h.data());
+  swiglu_requant(h.data(), I, q.data(), qsc.data(), a_out);
+  down(L, q.data(), qsc.data(), e, o);
   if (h_out) std::memcpy(h_out, h.data(), sizeof(float) * 2 * I);
   if (q_out) std::memcpy(q_out, q.data(), I);
   if (qsc_out) std::memcpy(qsc_out, qsc.data(), I / 32);
+}
+
+// y_t = sum over slots j = 0..k-1 of w_tj * o_tj in double, rounded to fp32.
+float combine(const float* w, const float* const* o, int k, int n) {
+  double acc = 0.0;
+  for (int j = 0; j < k; ++j)
+    if (o[j]) acc += double(w[j]) * double(o[j][n]);
+  return float(acc);
 }
 
 }  // namespace
@@ -321,27 +341,57 @@ int or_moe_rows(const uint8_t* x, const uint8_t* x_sc, int H,
     const int r = int(idx / k), j = int(idx % k);
     const int t = rows[r];
     if (!live[t]) return;
-    pair_ffn(L, t, ids[int64_t(t) * k + j], &o[idx * H], nullptr, nullptr, nullptr);
+    pair_ffn(L, t, ids[int64_t(t) * k + j], &o[idx * H], nullptr, nullptr, nullptr, nullptr);
   });
   parallel_for(nrows, threads, [&](int64_t r) {
     const int t = rows[r];
-    for (int n = 0; n < H; ++n) {
-      if (!live[t]) { y[r * H + n] = 0.0f; continue; }
-      double acc = 0.0;
-      for (int j = 0; j < k; ++j) acc += double(w[int64_t(t) * k + j]) * double(o[(r * k + j) * H + n]);
-      y[r * H + n] = float(acc);
-    }
+    std::vector<const float*> op(k);
+    for (int j = 0; j < k; ++j) op[j] = live[t] ? &o[(r * k + j) * H] : nullptr;
+    for (int n = 0; n < H; ++n) y[r * H + n] = live[t] ? combine(w + int64_t(t) * k, op.data(), k, n) : 0.0f;
   });
   return 0;
 }
 
-// One pair with its intermediates (diagnostics): h[2I], q[I], q_sc[I/32], o[H].
+// The second half of the layer from a given FP8 intermediate: q [P][I] and
+// q_sc [P][I/32] indexed by bucket position p (slot_pos[t][j] = p, -1 when the
+// pair is dead).  o_tj = down(q[p]) and y_t as in or_moe_rows.  y [nrows][H].
+int or_down_combine(const uint8_t* q, const uint8_t* q_sc, const int32_t* slot_pos, const int32_t* ids,
+                    const float* w, int k, const uint8_t* w2, const uint8_t* w2_sc, int H, int E, int I,
+                    const int32_t* rows, int nrows, float* y, int threads) {
+  if (H % 32 || I % 32 || k < 1 || E < 1) return -1;
+  const Layer L{nullptr, nullptr, H, nullptr, nullptr, w2, w2_sc, I};
+  std::vector<float> o(int64_t(nrows) * k * H, 0.0f);
+  parallel_for(int64_t(nrows) * k, threads, [&](int64_t idx) {
+    const int r = int(idx / k), j = int(idx % k);
+    const int t = rows[r];
+    const int p = slot_pos[int64_t(t) * k + j];
+    if (p < 0) return;
+    down(L, q + int64_t(p) * I, q_sc + int64_t(p) * (I / 32), ids[int64_t(t) * k + j], &o[idx * H]);
+  });
+  parallel_for(nrows, threads, [&](int64_t r) {
+    const int t = rows[r];
+    std::vector<const float*> op(k);
+    for (int j = 0; j < k; ++j) op[j] = slot_pos[int64_t(t) * k + j] >= 0 ? &o[(r * k + j) * H] : nullptr;
+    for (int n = 0; n < H; ++n) y[r * H + n] = combine(w + int64_t(t) * k, op.data(), k, n);
+  });
+  return 0;
+}
+
+// SwiGLU + requant of given fp32 gate/up rows h [n][2I] -> q [n][I], q_sc [n][I/32], a [n][I].
+int or_swiglu_requant(const float* h, int64_t n, int I, uint8_t* q, uint8_t* q_sc, float* a) {
+  if (I % 32) return -1;
+  for (int64_t r = 0; r < n; ++r)
+    swiglu_requant(h + r * 2 * I, I, q + r * I, q_sc + r * (I / 32), a ? a + r * I : nullptr);
+  return 0;
+}
+
+// One pair with its intermediates (diagnostics): h[2I], a[I], q[I], q_sc[I/32], o[H].
 int or_pair_ffn(const uint8_t* x, const uint8_t* x_sc, int H, int t, int e,
                 const uint8_t* w13, const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I,
-                float* h, uint8_t* q, uint8_t* q_sc, float* o) {
+                float* h, float* a, uint8_t* q, uint8_t* q_sc, float* o) {
   if (H % 32 || I % 32) return -1;
   const Layer L{x, x_sc, H, w13, w13_sc, w2, w2_sc, I};
-  pair_ffn(L, t, e, o, h, q, q_sc);
+  pair_ffn(L, t, e, o, h, a, q, q_sc);
   return 0;
 }
 

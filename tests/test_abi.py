@@ -1,0 +1,128 @@
+"""The C-ABI library loads without a GPU, exports every entry point that
+include/mxmoe.h declares, and rejects bad arguments on the host, before any
+HIP call, with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_fp8xfp4_amd import mxmoe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mxmoe.LIB_PATH):
+        import block_scaled_fp8xfp4_amd.build as b
+        b.build()
+    return mxmoe.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("moe_route", "moe_expert_ffn", "fp8_block_gemm", "mx_quantize"):
+        assert required in names
+    assert sorted(mxmoe.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4):
+        assert mxmoe.status_string(s).startswith("MX_")
+    assert "unknown" in mxmoe.status_string(7)
+
+
+def test_workspace_sizes_are_pure_host_functions(lib):
+    assert mxmoe.moe_route_workspace_bytes(8192, 256, 8) >= 32 * 256 * 4
+    b = mxmoe.moe_expert_ffn_workspace_bytes(8192, 4096, 256, 576, 8)
+    assert b >= 65536 * 4096 * 4 + 65536 * 576
+    oq, oqs, oh, oo = mxmoe.moe_ws_layout(8192, 4096, 576, 8)
+    assert oq == 0 and oqs >= 65536 * 576 and oh >= oqs + 65536 * 18 and oo >= oh + 65536 * 1152 * 4
+    assert oo + 65536 * 4096 * 4 <= b
+    assert mxmoe.moe_expert_ffn_workspace_bytes(1, 64, 1, 32, 1) == 0       # H < 128: invalid
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced: validation fails first
+FAKE_WS = ctypes.c_void_p(1 << 24)
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    q = lib.mx_quantize
+    assert q(None, 0, 4, 64, 0, FAKE, FAKE, None) == mxmoe.MX_EINVAL
+    assert q(FAKE, 0, 4, 48, 0, FAKE, FAKE, None) == mxmoe.MX_EINVAL              # cols % 32
+    assert q(FAKE, 2, 4, 64, 0, FAKE, FAKE, None) == mxmoe.MX_EINVAL              # dtype
+    assert q(FAKE, 0, 4, 64, 3, FAKE, FAKE, None) == mxmoe.MX_EINVAL              # format
+    assert q(ctypes.c_void_p((1 << 20) + 4), 0, 4, 64, 0, FAKE, FAKE, None) == mxmoe.MX_EINVAL  # alignment
+    assert q(FAKE, 0, -1, 64, 0, FAKE, FAKE, None) == mxmoe.MX_EINVAL
+
+
+def route(lib, T=4, E=8, k=2, ws=FAKE_WS, ws_bytes=1 << 20, logits=FAKE, ids=FAKE):
+    return lib.moe_route(logits, T, E, k, None, 0.2, ids, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_route_rejects_bad_arguments(lib):
+    assert route(lib, k=0) == mxmoe.MX_EINVAL
+    assert route(lib, k=9, E=8) == mxmoe.MX_EINVAL
+    assert route(lib, k=17, E=64) == mxmoe.MX_EINVAL
+    assert route(lib, E=0) == mxmoe.MX_EINVAL
+    assert route(lib, E=1025) == mxmoe.MX_EINVAL
+    assert route(lib, T=-1) == mxmoe.MX_EINVAL
+    assert route(lib, T=1 << 28, k=16, E=64) == mxmoe.MX_EINVAL                 # T*k overflows int32
+    assert route(lib, logits=None) == mxmoe.MX_EINVAL
+    assert route(lib, ids=None) == mxmoe.MX_EINVAL
+    assert route(lib, ws=None) == mxmoe.MX_EWORKSPACE
+    assert route(lib, T=8192, E=256, k=8, ws_bytes=100) == mxmoe.MX_EWORKSPACE
+
+
+def ffn(lib, T=4, H=256, E=8, I=64, k=2, ws=FAKE_WS, ws_bytes=1 << 34, x=FAKE, w13=FAKE):
+    return lib.moe_expert_ffn(x, FAKE, T, H, FAKE, FAKE, FAKE, FAKE, k, w13, FAKE, FAKE, FAKE, E, I, FAKE,
+                              ws, ws_bytes, None)
+
+
+def test_ffn_rejects_bad_arguments(lib):
+    assert ffn(lib, k=0) == mxmoe.MX_EINVAL
+    assert ffn(lib, k=17) == mxmoe.MX_EINVAL
+    assert ffn(lib, H=100) == mxmoe.MX_EINVAL                                   # H < 128
+    assert ffn(lib, H=300) == mxmoe.MX_EINVAL                                   # H % 32
+    assert ffn(lib, H=320) == mxmoe.MX_EUNSUPPORTED                             # H % 128
+    assert ffn(lib, I=48) == mxmoe.MX_EINVAL                                    # I % 32
+    assert ffn(lib, I=4096) == mxmoe.MX_EUNSUPPORTED                            # I > 2048
+    assert ffn(lib, x=None) == mxmoe.MX_EINVAL
+    assert ffn(lib, w13=ctypes.c_void_p((1 << 20) + 8)) == mxmoe.MX_EINVAL      # alignment
+    assert ffn(lib, ws=None) == mxmoe.MX_EWORKSPACE
+    assert ffn(lib, ws_bytes=1000) == mxmoe.MX_EWORKSPACE
+    assert ffn(lib, E=0) == mxmoe.MX_EINVAL
+
+
+def gemm(lib, M=1, N=64, K=256, ydt=0, a=FAKE):
+    return lib.fp8_block_gemm(a, FAKE, FAKE, FAKE, M, N, K, FAKE, ydt, None)
+
+
+def test_gemm_rejects_bad_arguments(lib):
+    assert gemm(lib, M=0) == mxmoe.MX_EINVAL
+    assert gemm(lib, K=100) == mxmoe.MX_EINVAL
+    assert gemm(lib, K=96) == mxmoe.MX_EUNSUPPORTED
+    assert gemm(lib, N=40) == mxmoe.MX_EUNSUPPORTED
+    assert gemm(lib, ydt=5) == mxmoe.MX_EINVAL
+    assert gemm(lib, a=None) == mxmoe.MX_EINVAL
+
+
+def test_path_switch(lib):
+    old = mxmoe.set_ffn_path(1)
+    assert mxmoe.set_ffn_path(old) == 1
+    with pytest.raises(mxmoe.MXError):
+        mxmoe.set_ffn_path(3)

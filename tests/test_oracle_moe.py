@@ -217,6 +217,43 @@ def test_moe_thread_count_independent():
     assert np.array_equal(oracle.moe_rows(*args, threads=1), oracle.moe_rows(*args, threads=6))
 
 
+def test_swiglu_requant_matches_independent_computation():
+    rng = np.random.default_rng(13)
+    h = (rng.standard_normal((9, 2 * 96)) * 3).astype(np.float32)
+    h[2, :5] = 0.0
+    q, q_sc, a = oracle.swiglu_requant(h)
+    g, u = h[:, :96].astype(np.float64), h[:, 96:].astype(np.float64)
+    a_ref = (g / (1 + np.exp(-g)) * u).astype(np.float32)
+    assert np.array_equal(a, a_ref)
+    A = dec_e4m3(q, q_sc).reshape(-1)
+    assert np.array_equal(A, requant_e4m3_independent(a_ref))
+
+
+def test_down_combine_matches_brute_force_and_full_layer():
+    inp = synth.small_moe(seed=14, T=6, H=96, E=5, k=3, I=64, skip_frac=0.3)
+    L = quantized_layer(inp)
+    r = oracle.route(inp.logits, 3, inp.survival)
+    P = int(r["offsets"][-1])
+    q = np.zeros((6 * 3, 64), np.uint8)
+    q_sc = np.zeros((6 * 3, 2), np.uint8)
+    for p in range(P):
+        t, j = divmod(int(r["perm"][p]), 3)
+        res = oracle.pair_ffn(L["x"], L["x_sc"], t, int(r["ids"][t, j]), L["w13"], L["w13_sc"], L["w2"], L["w2_sc"])
+        q[p], q_sc[p] = res["q"], res["q_sc"]
+    y = oracle.down_combine(q, q_sc, r["slot_pos"], r["ids"], r["w"], L["w2"], L["w2_sc"])
+    full = oracle.moe_rows(L["x"], L["x_sc"], r["ids"], r["w"], r["live"], L["w13"], L["w13_sc"], L["w2"], L["w2_sc"])
+    assert np.array_equal(y, full)
+    W2 = dec_e2m1(L["w2"], L["w2_sc"])
+    A = dec_e4m3(q, q_sc)
+    for t in range(6):
+        acc = np.zeros(96)
+        for j in range(3):
+            p = r["slot_pos"][t, j]
+            if p >= 0:
+                acc += float(r["w"][t, j]) * (W2[r["ids"][t, j]] @ A[p]).astype(np.float32)
+        assert np.max(np.abs(y[t] - acc.astype(np.float32))) <= 1e-6 * max(1e-30, np.abs(acc).max())
+
+
 def test_moe_quantization_error_is_in_the_pages_band():
     """Sanity band, not a pin: the routed output against a float64 evaluation with
     unquantized activations and intermediate on the same FP4 weights lands near
