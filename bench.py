@@ -1,0 +1,298 @@
+"""Benchmark of the block-scaled MoE hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|verify|prefill]
+                    [--no-cpu-baseline] [--no-prefill]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+top-k gate + bucketing (moe_route), the routed-expert FFN with its combine
+(moe_expert_ffn) and, for the decode workloads, the dense block-32 FP8
+projection (fp8_block_gemm, M = rows, K = N = 4096).  Inputs are resident in
+HBM before timing starts.  Weights rotate over R distinct copies so that the
+bytes a step touches are never served by the 256 MB MALL or the L2s.
+
+Default workload "decode": one token, hidden 4096, 256 experts, top-8,
+intermediate 576 (MXFP4 experts, FP8 block-32 activations), plus the dense
+projection at M = 1.  value = algorithmic bytes per step / step time (GB/s).
+Unless --no-prefill, the line also carries the 8192-token prefill layer's
+expert-GEMM throughput (TFLOP/s) measured in the same run.
+
+Prints ONE JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense FP8 matrix rate (the FP8 x FP4 MFMA issues at this rate)
+MFMA_FP4_PEAK_TFLOPS = 10100.0
+
+EXPERT_BYTES = lambda H, I: 2 * I * (H // 2 + H // 32) + H * (I // 2 + I // 32)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_fp8xfp4_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_sha") != kernel_sources_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=["decode", "verify", "prefill"], default="decode")
+    ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to exceed 1.5 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode "
+              "(the layer shards by rows or by the intermediate dimension; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_scaled_fp8xfp4_amd import mxmoe, synth
+    from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route, quantize, quantize_experts
+
+    mxmoe.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    result = {}
+
+    def dense_layer(cfg):
+        d = synth.dense_inputs()
+        w = torch.from_numpy(d.w).to(dev)
+        wq, wsc = quantize(w, mxmoe.MX_FMT_E4M3)
+        del w
+        return d, wq, wsc
+
+    def moe_layer(cfg):
+        inp = synth.moe_inputs(cfg)
+        t0 = time.time()
+        w13q, w13s = quantize_experts(inp.w13())
+        w2q, w2s = quantize_experts(inp.w2())
+        log(f"{cfg.name}: generated and quantized the expert weights in {time.time() - t0:.1f} s")
+        x = torch.from_numpy(inp.x).to(dev).to(torch.bfloat16)
+        xq, xsc = quantize(x, mxmoe.MX_FMT_E4M3)
+        return inp, xq, xsc, (w13q, w13s, w2q, w2s)
+
+    # ------------------------------------------------------------ decode step
+    def run_decode(cfg):
+        inp, xq, xsc, W = moe_layer(cfg)
+        T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+        dense, gq, gsc = dense_layer(synth.DENSE)
+        a = torch.from_numpy(dense.a[:T] if T <= dense.a.shape[0] else np.resize(dense.a, (T, dense.cfg.K)))
+        aq, asc = quantize(a.to(dev).to(torch.bfloat16).contiguous(), mxmoe.MX_FMT_E4M3)
+        logits = torch.from_numpy(inp.logits).to(dev)
+        surv = None if inp.survival is None else torch.from_numpy(inp.survival).to(dev)
+        route = Route(T, E, k)
+        ffn = ExpertFFN(T, H, E, I, k)
+        yg = torch.empty((T, dense.cfg.N), dtype=torch.bfloat16, device=dev)
+        # bytes one step streams: touched experts, activations, logits, outputs, dense weights
+        route(logits, surv)
+        torch.cuda.synchronize()
+        offs = route.offsets.cpu().numpy()
+        touched = int(np.count_nonzero(np.diff(offs)))
+        all_ids = np.unique(route.ids.cpu().numpy())
+        moe_bytes = touched * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * E * 4 + T * H * 4
+        dense_bytes = dense.cfg.N * (dense.cfg.K + dense.cfg.K // 32) + T * (dense.cfg.K + dense.cfg.K // 32) \
+            + T * dense.cfg.N * 2
+        step_bytes = moe_bytes + dense_bytes
+        per_copy = touched * EXPERT_BYTES(H, I) + dense_bytes
+        R = args.rotate or max(2, int(np.ceil(1.5e9 / per_copy)))
+        log(f"{cfg.name}: touched experts {touched} (all slots {len(all_ids)}), bytes/step {step_bytes}, "
+            f"rotating {R} weight copies")
+        copies = [W] + [tuple(t.clone() for t in W) for _ in range(R - 1)]
+        gcopies = [(gq, gsc)] + [(gq.clone(), gsc.clone()) for _ in range(R - 1)]
+        torch.cuda.synchronize()
+
+        def step(i):
+            w13q, w13s, w2q, w2s = copies[i % R]
+            route(logits, surv)
+            ffn(xq, xsc, route, w13q, w13s, w2q, w2s)
+            g, gs = gcopies[i % R]
+            mxmoe.fp8_block_gemm(aq, asc, g, gs, yg, mxmoe.MX_OUT_BF16)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        # per-call events on the launch stream bracket the FFN call of every step
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(args.steps):
+            w13q, w13s, w2q, w2s = copies[i % R]
+            route(logits, surv)
+            ev[i][0].record()
+            ffn(xq, xsc, route, w13q, w13s, w2q, w2s)
+            ev[i][1].record()
+            ffn_variant = mxmoe.last_variant()
+            g, gs = gcopies[i % R]
+            mxmoe.fp8_block_gemm(aq, asc, g, gs, yg, mxmoe.MX_OUT_BF16)
+        t_end.record()
+        torch.cuda.synchronize()
+        total_ms = t_start.elapsed_time(t_end)
+        ffn_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+        ms = total_ms / args.steps
+        ffn_bytes = touched * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * H * 4
+        achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+        result.update({
+            "metric": "decode weight-stream GB/s (% HBM peak) + prefill expert TFLOP/s (% MFMA peak)",
+            "value": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "ms_per_step": round(ms, 5),
+            "pct_hbm_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (" + ffn_variant + ")",
+                         "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(cfg.name),
+                         "bytes_per_launch": ffn_bytes, "avg_launch_ms": round(ffn_ms, 5)},
+            "config": {"workload": f"{cfg.name} MoE layer step: T={T}, H={H}, E={E}, top-{k}, I={I}, MXFP4 experts, "
+                                   f"FP8 block-32 activations, + dense FP8 block-32 projection M={T}, K=N=4096",
+                       "rows": T, "hidden": H, "experts": E, "top_k": k, "intermediate": I,
+                       "touched_experts": touched, "bytes_per_step": step_bytes, "weight_copies": R},
+        })
+        return inp, touched
+
+    # ------------------------------------------------------------ prefill
+    def run_prefill(steps, warmup):
+        cfg = synth.PREFILL
+        inp, xq, xsc, W = moe_layer(cfg)
+        T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+        logits = torch.from_numpy(inp.logits).to(dev)
+        route = Route(T, E, k)
+        ffn = ExpertFFN(T, H, E, I, k)
+        copies = [W, tuple(t.clone() for t in W)]
+        for i in range(warmup):
+            route(logits)
+            ffn(xq, xsc, route, *copies[i % 2])
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            route(logits)
+            ev[i][0].record()
+            ffn(xq, xsc, route, *copies[i % 2])
+            ev[i][1].record()
+        t1.record()
+        torch.cuda.synchronize()
+        ffn_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+        P = int(route.offsets[-1].item())
+        flop = P * (2 * 2 * I * H + 2 * H * I)
+        tflops = flop / (ffn_ms * 1e-3) / 1e12
+        return dict(tflops=round(tflops, 2), pct_fp8_peak=round(100 * tflops / MFMA_FP8_PEAK_TFLOPS, 2),
+                    pct_fp4_peak=round(100 * tflops / MFMA_FP4_PEAK_TFLOPS, 2), ffn_ms=round(ffn_ms, 4),
+                    step_ms=round(t0.elapsed_time(t1) / steps, 4), flop_per_call=flop,
+                    variant=mxmoe.last_variant(), pairs=P), inp
+
+    if args.workload == "prefill":
+        pre, inp = run_prefill(args.steps, args.warmup)
+        result.update({
+            "metric": "decode weight-stream GB/s (% HBM peak) + prefill expert TFLOP/s (% MFMA peak)",
+            "value": pre["tflops"], "unit": "TFLOP/s", "ms_per_step": pre["step_ms"],
+            "roofline": {"bound": "mfma", "kernel": "moe_expert_ffn (" + pre["variant"] + ")",
+                         "achieved": pre["tflops"], "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pre["tflops"] / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": recorded_traffic("prefill"),
+                         "flop_per_launch": pre["flop_per_call"], "avg_launch_ms": pre["ffn_ms"]},
+            "config": {"workload": "prefill MoE chunk: T=8192, H=4096, E=256, top-8, I=576, MXFP4 experts, "
+                                   "FP8 block-32 activations", "pairs": pre["pairs"]},
+        })
+        cpu_cfg = synth.PREFILL
+    else:
+        cfg = synth.DECODE if args.workload == "decode" else synth.VERIFY
+        inp, touched = run_decode(cfg)
+        cpu_cfg = cfg
+        if not args.no_prefill:
+            pre, _ = run_prefill(5, 2)
+            result["prefill"] = pre
+
+    result.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                   "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic"})
+
+    # ------------------------------------------------------------ CPU baseline: the oracle itself
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cpu_cfg, args.workload)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, workload):
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload (same shapes and distributions)."""
+    import oracle
+    from block_scaled_fp8xfp4_amd import synth
+
+    threads = min(16, oracle.hardware_threads())
+    inp = synth.moe_inputs(cfg)
+    r = oracle.route(inp.logits, cfg.k, inp.survival)
+    rows = np.arange(min(cfg.T, 4 if workload == "prefill" else cfg.T), dtype=np.int32)
+    need = np.unique(r["ids"][rows][r["live"][rows].astype(bool)])
+    H, I, E = cfg.H, cfg.I, cfg.E
+    w13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+    w13s = np.full((E, 2 * I, H // 32), 127, np.uint8)
+    w2 = np.zeros((E, H, I // 2), np.uint8)
+    w2s = np.full((E, H, I // 32), 127, np.uint8)
+    q, s = oracle.quantize_e2m1(inp.w13(need).reshape(-1, H), threads)
+    w13[need], w13s[need] = q.reshape(len(need), 2 * I, H // 2), s.reshape(len(need), 2 * I, H // 32)
+    q, s = oracle.quantize_e2m1(inp.w2(need).reshape(-1, I), threads)
+    w2[need], w2s[need] = q.reshape(len(need), H, I // 2), s.reshape(len(need), H, I // 32)
+    xq, xs = oracle.quantize_e4m3(inp.x, threads)
+    d = synth.dense_inputs()
+    aq, asc = oracle.quantize_e4m3(d.a[:1], threads)
+    wq, wsc = oracle.quantize_e4m3(d.w, threads)
+    live_pairs = int(r["live"][rows].sum()) * cfg.k
+    t0 = time.time()
+    reps = 0
+    while True:
+        oracle.route(inp.logits[rows], cfg.k, None if inp.survival is None else inp.survival[rows])
+        oracle.moe_rows(xq, xs, r["ids"], r["w"], r["live"], w13, w13s, w2, w2s, rows=rows, threads=threads)
+        if workload != "prefill":
+            oracle.block_gemm(aq, asc, wq, wsc, threads=threads)
+        reps += 1
+        if time.time() - t0 > 10.0 or reps >= 2000:
+            break
+    dt = (time.time() - t0) / reps
+    if workload == "prefill":
+        flop = live_pairs * (2 * 2 * I * H + 2 * H * I)
+        return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{len(rows)} of {cfg.T} prefill rows ({live_pairs} routed pairs), {reps} reps, "
+                          f"{dt:.2f} s per rep"}
+    touched = len(need)
+    step_bytes = touched * EXPERT_BYTES(H, I) + len(rows) * (H + H // 32) + len(rows) * E * 4 \
+        + len(rows) * H * 4 + d.cfg.N * (d.cfg.K + d.cfg.K // 32) + (d.cfg.K + d.cfg.K // 32) + d.cfg.N * 2
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full {workload} step ({len(rows)} rows, {touched} experts, dense M=1), {reps} reps, "
+                      f"{dt:.3f} s per rep"}
+
+
+if __name__ == "__main__":
+    main()
