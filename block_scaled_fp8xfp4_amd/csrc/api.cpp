@@ -120,10 +120,12 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H, co
     return MX_EINVAL;
   if (!ws || ws_bytes < mx::ffn_ws_bytes(T, H, E, I, k)) return MX_EWORKSPACE;
   if (!aligned(ws, 256)) return MX_EINVAL;
+  const int path = g_ffn_path.load();
+  if (!mx::ffn_path_supported(path, H, I)) return MX_EUNSUPPORTED;
   if (T == 0) { g_variant = "ffn:empty"; return MX_OK; }
   const mx::FfnArgs a{x, x_sc, T, H, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y};
   const char* v = "";
-  const hipError_t e = mx::launch_ffn(a, ws, g_ffn_path.load(), static_cast<hipStream_t>(stream), &v);
+  const hipError_t e = mx::launch_ffn(a, ws, path, static_cast<hipStream_t>(stream), &v);
   if (e == hipSuccess) g_variant = v;
   return from_hip(e);
 }

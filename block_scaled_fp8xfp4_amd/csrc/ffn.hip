@@ -1,40 +1,115 @@
 // Routed-expert FFN kernels: gate/up GEMM, SwiGLU + FP8 requant, down GEMM
 // and the fixed-order weighted combine ("New Deepseek 4.1 flash recipe"
 // thread, post #6, "How it works": routed experts with FP8 activations x FP4
-// weights, decode rows on small tiles; "Why TileLang": SwiGLU, per-block FP8
-// quantization, reductions in a fixed order; DeepSeek-V4.1-Flash-4x-DGX-
-// Spark-TP4 README, settings table, row "Experts": per-slot buffer and a
-// fixed-order sum instead of atomics).
+// weights, decode rows on small tiles, prefill on 64-row tiles; "Why
+// TileLang": SwiGLU with per-block FP8 quantization, reductions in a fixed
+// order; DeepSeek-V4.1-Flash-4x-DGX-Spark-TP4 README, settings table, row
+// "Experts": per-slot buffer and a fixed-order sum instead of atomics, 64-row
+// tiles for 576-wide experts at prefill sizes).
 //
-// Decode path (few rows per expert): a work item is (expert with live pairs,
-// 16-wide tile of weight rows).  A workgroup's four wavefronts split K into
-// the canonical parts and stream their share of the weight tile straight
-// from HBM into registers; the parts meet in LDS and are added in part order.
-// Gate/up writes h = [gate | up] in fp32 per bucket position; the down kernel
-// stages SwiGLU + requant of its rows in LDS (every down workgroup of an
-// expert recomputes the same values with the same device routine), then
-// streams W2 the same way and writes the per-slot output o.
-// The combine adds w_tj * o_tj over the slots in order j = 0..k-1.
+// Both paths evaluate every output element with the same MFMA chain (all K
+// steps in order, see mx_device.hpp) and the same SwiGLU/requant routine, so
+// they give the same bits; they differ only in how rows and weights reach the
+// matrix cores.
+//
+// Decode path (few rows per expert, weight streaming):
+//   gu_decode_kernel    one workgroup per (expert, 64 W13 rows): each
+//                       wavefront loads the whole K of its 16 weight rows
+//                       into registers at once; the expert's activation rows
+//                       are staged in LDS 16 at a time; writes fp32
+//                       h = [gate | up] per bucket position.
+//   down_decode_kernel  one workgroup per (expert, 64 W2 rows): W2 first,
+//                       then SwiGLU + requant of the rows' h into LDS (8
+//                       lanes per block of 32), then the down chain.
+// Prefill path (hundreds of rows per expert, matrix-core bound):
+//   gu_prefill_kernel   64-row expert tile x 128 intermediate columns (256
+//                       W13 rows) per workgroup; gathered activation rows are
+//                       staged through LDS two steps at a time, each
+//                       wavefront streams its own 64 weight rows straight to
+//                       registers; SwiGLU + requant in the epilogue.
+//   down_prefill_kernel 64-row tile x 256 W2 rows per workgroup; the tile's
+//                       whole intermediate (K = I) sits in LDS.
+//   Both run persistent grids whose blocks are remapped so that each XCD
+//   walks a contiguous range of (expert, row tile, column tile) items and
+//   shares weights and activations in its own L2.
+// combine_kernel adds w_tj * o_tj over the slots in order j = 0..k-1.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
 namespace mx {
 
-// Experts that own at least one live pair, ascending, listed by wavefront 0.
-__device__ void list_active_experts(const int32_t* __restrict__ offsets, int E, int* list, int* n_out) {
+constexpr int DEC_MAX_STEPS = 32;                 // decode gate/up: H <= 4096 held in registers
+constexpr int DOWN_MAX_STEPS = MAX_I / KSTEP;     // 16
+constexpr int PF_ROWS = 64;                       // prefill expert tile rows
+constexpr int PF_ICOLS = 128;                     // prefill gate/up: intermediate columns per workgroup
+constexpr int PF_KCH = 2;                         // prefill gate/up: MFMA steps per LDS stage
+constexpr int PF_AROW = PF_KCH * KSTEP + 16;      // LDS row pitch of the staged activations (padded)
+constexpr int PF_NCOLS = 256;                     // prefill down: W2 rows per workgroup
+constexpr int PF_MAX_I = 640;                     // prefill down: intermediate held in LDS (5 steps)
+constexpr int XCDS = 8;
+
+// ---------------------------------------------------------------- work lists
+__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x - v;
+}
+
+// Wavefront 0 writes tile_start[e] (e = 0..E): the first tile index of each
+// expert, where an expert with n live pairs owns ceil(n / rows) tiles
+// (rows == 0: one tile per expert with any pair).  All offsets are read in
+// one round of independent loads.
+__device__ void build_tiles(const int32_t* __restrict__ offsets, int E, int rows, int* tile_start) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int base = 0;
-    for (int c = 0; c < E; c += 64) {
-      const int e = c + lane;
-      const bool nz = e < E && offsets[e + 1] > offsets[e];
-      const unsigned long long m = __ballot(nz);
-      if (nz) list[base + __popcll(m & ((1ull << lane) - 1ull))] = e;
-      base += __popcll(m);
+    const int per = (E + 63) / 64;                  // <= MAX_E / 64 = 16
+    int o[17];
+#pragma unroll
+    for (int i = 0; i < 17; ++i) {
+      const int e = lane * per + i;
+      o[i] = (i <= per && e <= E) ? offsets[e] : 0;
     }
-    if (lane == 0) *n_out = base;
+    int cnt[16], local = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane * per + i;
+      int n = (i < per && e < E) ? o[i + 1] - o[i] : 0;
+      n = n < 0 ? 0 : n;
+      cnt[i] = rows > 0 ? (n + rows - 1) / rows : (n > 0 ? 1 : 0);
+      local += cnt[i];
+    }
+    int run = wave_excl_scan(local, lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane * per + i;
+      if (i < per && e < E) tile_start[e] = run;
+      run += cnt[i];
+    }
+    if (lane == 63) tile_start[E] = run;
   }
   __syncthreads();
+}
+
+// The expert that owns tile `tile` (tile_start non-decreasing, tile < tile_start[E]).
+__device__ __forceinline__ int tile_expert(const int* tile_start, int E, int tile) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_start[mid] <= tile) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Logical item of a persistent block in a round: each XCD (blocks b with the
+// same b % 8) takes a contiguous range of items.  G is a multiple of 8.
+__device__ __forceinline__ int xcd_item(int round, int b, int G) {
+  const int per = G / XCDS;
+  return round * G + (b % XCDS) * per + b / XCDS;
 }
 
 __device__ __forceinline__ v8i fp8_operand(const u32x4& lo, const u32x4& hi) {
@@ -44,147 +119,150 @@ __device__ __forceinline__ v8i fp4_operand(const u32x4& b) {
   return v8i{(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
 }
 
-// --------------------------------------------------------------------------
-// Gate/up, decode tiles.  h[p][n] for the expert's pairs p and W13 rows n.
-__global__ __launch_bounds__(256) void gu_decode_kernel(FfnArgs a, float* __restrict__ h, int Tk) {
-  __shared__ int active[MAX_E];
-  __shared__ int n_active;
-  __shared__ float red[MAX_PARTS][16][16];
-  list_active_experts(a.offsets, a.E, active, &n_active);
+// =========================================================== decode path ==
+// Gate/up: a workgroup takes (expert, 64 W13 rows); wavefront w streams the
+// whole K of W13 rows [16w, 16w + 16) of that group into registers, while
+// the workgroup stages the expert's activation rows (16 at a time) in LDS.
+constexpr int DEC_AROW = KSTEP * DEC_MAX_STEPS + 16;   // LDS pitch of a staged activation row
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, float* __restrict__ h, int Tk) {
+  __shared__ int tile_start[MAX_E + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t xlds[16][DEC_AROW];
+  __shared__ uint32_t xslds[16][DEC_MAX_STEPS];
+  build_tiles(a.offsets, a.E, 0, tile_start);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int H = a.H, twoI = 2 * a.I;
-  const int nsteps = H / KSTEP, nparts = (nsteps + KPART_STEPS - 1) / KPART_STEPS;
-  const int ntiles = twoI / 16;
-  const int nitems = n_active * ntiles;
-
+  const int nsteps = H / KSTEP;
+  const int ngroups = (twoI + 63) / 64;
+  const int nitems = tile_start[a.E] * ngroups;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int e = active[item / ntiles], nt = item % ntiles;
+    const int e = tile_expert(tile_start, a.E, item / ngroups), grp = item % ngroups;
     const int p0 = a.offsets[e];
     int cnt = a.offsets[e + 1] - p0;
     if (p0 < 0 || p0 + cnt > Tk) cnt = 0;                       // malformed route: skip
-    const int64_t wrow = (int64_t)e * twoI + nt * 16 + col;     // B column served by this lane
+    const int nrow13 = grp * 64 + wave * 16;                    // first W13 row of this wavefront
+    const bool wact = nrow13 < twoI;
+    const int64_t wrow = (int64_t)e * twoI + (wact ? nrow13 : 0) + col;   // B column of this lane
     const uint8_t* wp = a.w13 + wrow * (H / 2);
     const uint32_t* wsp = reinterpret_cast<const uint32_t*>(a.w13_sc + wrow * (H / 32));
-    for (int rt = 0; rt * 16 < cnt; ++rt) {
-      const int r = rt * 16 + col;                               // A row served by this lane
-      int tok = 0;
-      bool rv = r < cnt;
-      if (rv) {
-        const int pr = a.perm[p0 + r];
-        rv = pr >= 0 && pr < Tk;
-        tok = rv ? pr / a.k : 0;
+    u32x4 bw[DEC_MAX_STEPS];
+    uint32_t bs[DEC_MAX_STEPS];
+#pragma unroll
+    for (int s = 0; s < DEC_MAX_STEPS; ++s) {
+      if (s < nsteps) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        bw[s] = wact ? ldg16(wp + s * 64 + g * 16) : z;
+        bs[s] = wact ? (wsp[s] >> (8 * g)) : 0x7F7F7F7Fu;
       }
-      const uint8_t* xp = a.x + (int64_t)tok * H;
-      const uint32_t* xsp = reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)tok * (H / 32));
-      for (int q = wave; q < nparts; q += 4) {
-        const int s0 = q * KPART_STEPS;
-        u32x4 bw[KPART_STEPS], alo[KPART_STEPS], ahi[KPART_STEPS];
-        uint32_t bs[KPART_STEPS], as[KPART_STEPS];
-#pragma unroll
-        for (int m = 0; m < KPART_STEPS; ++m) {
-          const int s = s0 + m;
-          if (s < nsteps) {
-            bw[m] = ldg16(wp + s * 64 + g * 16);
-            bs[m] = wsp[s] >> (8 * g);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < KPART_STEPS; ++m) {
-          const int s = s0 + m;
-          if (s < nsteps) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            alo[m] = rv ? ldg16(xp + s * KSTEP + g * 16) : z;
-            ahi[m] = rv ? ldg16(xp + s * KSTEP + 64 + g * 16) : z;
-            as[m] = rv ? (xsp[s] >> (8 * g)) : bs[m];
-          }
-        }
+    }
+    for (int rt = 0; rt * 16 < cnt; ++rt) {
+      const int nrows = min(16, cnt - rt * 16);
+      __syncthreads();                                          // previous row tile's LDS reads are done
+      // stage the rows: 16 bytes per thread per pass, rows in order
+      const int q16 = H / 16;
+      for (int idx = tid; idx < nrows * q16; idx += 256) {
+        const int r = idx / q16, c16 = idx % q16;
+        const int pr = a.perm[p0 + rt * 16 + r];
+        const int tok = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&xlds[r][c16 * 16]) = tok >= 0 ? ldg16(a.x + (int64_t)tok * H + c16 * 16) : z;
+      }
+      for (int idx = tid; idx < nrows * nsteps; idx += 256) {
+        const int r = idx / nsteps, st = idx % nsteps;
+        const int pr = a.perm[p0 + rt * 16 + r];
+        const int tok = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
+        xslds[r][st] = tok >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)tok * (H / 32))[st] : 0x7F7F7F7Fu;
+      }
+      __syncthreads();
+      if (wact) {
+        const bool rv = col < nrows;
         v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < KPART_STEPS; ++m) {
-          if (s0 + m < nsteps) acc = mfma_fp8_fp4(fp8_operand(alo[m], ahi[m]), fp4_operand(bw[m]), acc, as[m], bs[m]);
+        for (int s = 0; s < DEC_MAX_STEPS; ++s) {
+          if (s < nsteps) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const uint8_t* ap = &xlds[col][s * KSTEP + g * 16];
+            const u32x4 alo = rv ? *reinterpret_cast<const u32x4*>(ap) : z;
+            const u32x4 ahi = rv ? *reinterpret_cast<const u32x4*>(ap + 64) : z;
+            const uint32_t sa = rv ? (xslds[col][s] >> (8 * g)) : bs[s];
+            acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, sa, bs[s]);
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[q][4 * g + i][col] = acc[i];
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * g + i;
+          if (row < nrows) h[(int64_t)(p0 + rt * 16 + row) * twoI + nrow13 + col] = acc[i];
+        }
       }
-      __syncthreads();
-      {
-        const int row = threadIdx.x >> 4, c = threadIdx.x & 15;
-        float v = red[0][row][c];
-        for (int q = 1; q < nparts; ++q) v = v + red[q][row][c];
-        if (rt * 16 + row < cnt) h[(int64_t)(p0 + rt * 16 + row) * twoI + nt * 16 + c] = v;
-      }
-      __syncthreads();
     }
   }
 }
 
-// --------------------------------------------------------------------------
-// SwiGLU + FP8 requant of pair rows [p0, p0 + n) (n <= 16) into LDS (and the
-// workspace copy when `publish`).  Block-wide.
+// SwiGLU + requant of pair rows [p0, p0 + n) (n <= 16) from h into LDS, and
+// into the workspace when `publish`.  Block-wide; 8 consecutive lanes share
+// a block of 32 intermediate values (4 each), the block maximum is a
+// butterfly over those 8 lanes.
 __device__ void stage_intermediate(const float* __restrict__ h, int p0, int n, int I, uint8_t (*qlds)[MAX_I + 16],
                                    uint8_t (*slds)[MAX_I / 32], uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws,
                                    bool publish) {
-  const int nb = I / 32;
-  for (int idx = threadIdx.x; idx < 16 * nb; idx += blockDim.x) {
-    const int r = idx / nb, b = idx % nb;
-    if (r >= n) continue;
-    const float* hp = h + (int64_t)(p0 + r) * 2 * I + b * 32;
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 32; i += 4) {
-      const float4 gg = *reinterpret_cast<const float4*>(hp + i);
-      const float4 uu = *reinterpret_cast<const float4*>(hp + I + i);
-      v[i] = swiglu(gg.x, uu.x);
-      v[i + 1] = swiglu(gg.y, uu.y);
-      v[i + 2] = swiglu(gg.z, uu.z);
-      v[i + 3] = swiglu(gg.w, uu.w);
+  const int q4 = I / 4, nb = I / 32;
+  const int total = 16 * q4;                                     // multiple of 128
+  for (int base = 0; base < total; base += blockDim.x) {
+    const int idx = base + (int)threadIdx.x;
+    const int r = idx / q4, c4 = idx % q4;
+    const bool in = idx < total && r < n;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (in) {
+      const float* hp = h + (int64_t)(p0 + r) * 2 * I + 4 * c4;
+      const float4 gg = *reinterpret_cast<const float4*>(hp);
+      const float4 uu = *reinterpret_cast<const float4*>(hp + I);
+      v[0] = swiglu(gg.x, uu.x);
+      v[1] = swiglu(gg.y, uu.y);
+      v[2] = swiglu(gg.z, uu.z);
+      v[3] = swiglu(gg.w, uu.w);
     }
-    uint32_t out[8];
-    const uint32_t sc = quantize32_e4m3(v, out);
-    u32x4* dst = reinterpret_cast<u32x4*>(&qlds[r][b * 32]);
-    dst[0] = u32x4{out[0], out[1], out[2], out[3]};
-    dst[1] = u32x4{out[4], out[5], out[6], out[7]};
-    slds[r][b] = (uint8_t)sc;
-    if (publish) {
-      u32x4* gdst = reinterpret_cast<u32x4*>(qws + (int64_t)(p0 + r) * I + b * 32);
-      gdst[0] = u32x4{out[0], out[1], out[2], out[3]};
-      gdst[1] = u32x4{out[4], out[5], out[6], out[7]};
-      qsc_ws[(int64_t)(p0 + r) * nb + b] = (uint8_t)sc;
+    float m = fmaxf(fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])), fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    if (in) {
+      const uint32_t sc = e8m0_code_for_amax(m, 8);
+      const uint32_t d = requant_e4m3(v[0], sc) | (requant_e4m3(v[1], sc) << 8) | (requant_e4m3(v[2], sc) << 16) |
+                         (requant_e4m3(v[3], sc) << 24);
+      *reinterpret_cast<uint32_t*>(&qlds[r][4 * c4]) = d;
+      if ((c4 & 7) == 0) slds[r][c4 >> 3] = (uint8_t)sc;
+      if (publish) {
+        *reinterpret_cast<uint32_t*>(qws + (int64_t)(p0 + r) * I + 4 * c4) = d;
+        if ((c4 & 7) == 0) qsc_ws[(int64_t)(p0 + r) * nb + (c4 >> 3)] = (uint8_t)sc;
+      }
     }
   }
 }
 
-constexpr int DOWN_MAX_STEPS = MAX_I / KSTEP;   // 16
-
-// Down projection, decode tiles: o[p][n] for the expert's pairs and a 64-row
-// tile of W2 (16 rows per wavefront, full K = I per wavefront).
 __global__ __launch_bounds__(256) void down_decode_kernel(FfnArgs a, const float* __restrict__ h,
                                                           uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws,
                                                           float* __restrict__ o, int Tk) {
-  __shared__ int active[MAX_E];
-  __shared__ int n_active;
+  __shared__ int tile_start[MAX_E + 1];
   __shared__ __attribute__((aligned(16))) uint8_t qlds[16][MAX_I + 16];   // padded rows: fewer bank conflicts
   __shared__ uint8_t slds[16][MAX_I / 32];
-  list_active_experts(a.offsets, a.E, active, &n_active);
+  build_tiles(a.offsets, a.E, 0, tile_start);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int H = a.H, I = a.I, nb = I / 32;
   const int nsteps = (I + KSTEP - 1) / KSTEP;
   const int ntiles = H / 64;
-  const int nitems = n_active * ntiles;
+  const int nitems = tile_start[a.E] * ntiles;
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int e = active[item / ntiles], tile = item % ntiles;
+    const int e = tile_expert(tile_start, a.E, item / ntiles), tile = item % ntiles;
     const int p0 = a.offsets[e];
     int cnt = a.offsets[e + 1] - p0;
     if (p0 < 0 || p0 + cnt > Tk) cnt = 0;
     const int n = tile * 64 + wave * 16 + col;                  // W2 row = output column of this lane
     const uint8_t* wp = a.w2 + ((int64_t)e * H + n) * (I / 2);
     const uint8_t* wsp = a.w2_sc + ((int64_t)e * H + n) * nb;
-    // weights first: the whole K = I of this lane's column stays in registers
     u32x4 bw[DOWN_MAX_STEPS];
     uint32_t bs[DOWN_MAX_STEPS];
 #pragma unroll
@@ -201,35 +279,289 @@ __global__ __launch_bounds__(256) void down_decode_kernel(FfnArgs a, const float
       stage_intermediate(h, p0 + rt * 16, nrows, I, qlds, slds, qws, qsc_ws, tile == 0);
       __syncthreads();
       const bool rv = col < nrows;
-      v4f total = {0.f, 0.f, 0.f, 0.f};
-      for (int q = 0; q * KPART_STEPS < nsteps; ++q) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < KPART_STEPS; ++m) {
-          const int s = q * KPART_STEPS + m;
-          if (s < nsteps && s < DOWN_MAX_STEPS) {
-            const int klo = s * KSTEP + g * 16, khi = klo + 64;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 alo = (rv && klo < I) ? *reinterpret_cast<const u32x4*>(&qlds[col][klo]) : z;
-            const u32x4 ahi = (rv && khi < I) ? *reinterpret_cast<const u32x4*>(&qlds[col][khi]) : z;
-            const uint32_t sa = (rv && 4 * s + g < nb) ? (uint32_t)slds[col][4 * s + g] : bs[s];
-            acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, sa, bs[s]);
-          }
+      for (int s = 0; s < DOWN_MAX_STEPS; ++s) {
+        if (s < nsteps) {
+          const int klo = s * KSTEP + g * 16, khi = klo + 64;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 alo = (rv && klo < I) ? *reinterpret_cast<const u32x4*>(&qlds[col][klo]) : z;
+          const u32x4 ahi = (rv && khi < I) ? *reinterpret_cast<const u32x4*>(&qlds[col][khi]) : z;
+          const uint32_t sa = (rv && 4 * s + g < nb) ? (uint32_t)slds[col][4 * s + g] : bs[s];
+          acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, sa, bs[s]);
         }
-        if (q == 0) total = acc;
-        else total = total + acc;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * g + i;
-        if (row < nrows) o[(int64_t)(p0 + rt * 16 + row) * H + n] = total[i];
+        if (row < nrows) o[(int64_t)(p0 + rt * 16 + row) * H + n] = acc[i];
       }
       __syncthreads();
     }
   }
 }
 
-// --------------------------------------------------------------------------
+// ========================================================== prefill path ==
+// Gate/up over a 64-row expert tile and 128 intermediate columns; wavefront w
+// owns intermediate columns [32w, 32w + 32) of the tile: W13 rows gate c0 +
+// [0,32) and up I + c0 + [0,32), i.e. four 16-row B tiles, against the four
+// 16-row A tiles of the expert tile (16 accumulators).
+__global__ __launch_bounds__(256, 2) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
+                                                            uint8_t* __restrict__ qsc_ws, int Tk) {
+  __shared__ int tile_start[MAX_E + 1];
+  __shared__ int tok[PF_ROWS];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf[2][PF_ROWS][PF_AROW];
+  __shared__ uint32_t asbuf[2][PF_ROWS][PF_KCH];
+  build_tiles(a.offsets, a.E, PF_ROWS, tile_start);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int H = a.H, I = a.I, nb = I / 32;
+  const int nsteps = H / KSTEP, nchunks = (nsteps + PF_KCH - 1) / PF_KCH;
+  const int nct = (I + PF_ICOLS - 1) / PF_ICOLS;
+  const int nitems = tile_start[a.E] * nct;
+  // cooperative activation loads: thread -> (row, 64-byte segment of a 256-byte stage)
+  const int lr = tid >> 2, lseg = tid & 3;
+
+  for (int round = 0;; ++round) {
+    const int item = xcd_item(round, blockIdx.x, gridDim.x);
+    if (item >= nitems) break;
+    const int tile = item / nct, ct = item % nct;
+    const int e = tile_expert(tile_start, a.E, tile);
+    const int p0 = a.offsets[e] + (tile - tile_start[e]) * PF_ROWS;
+    int nrows = a.offsets[e + 1] - p0;
+    nrows = nrows > PF_ROWS ? PF_ROWS : nrows;
+    if (p0 < 0 || p0 + nrows > Tk) nrows = 0;
+    __syncthreads();                                            // previous item's LDS reads are done
+    if (tid < PF_ROWS) {
+      int t = -1;
+      if (tid < nrows) {
+        const int pr = a.perm[p0 + tid];
+        t = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
+      }
+      tok[tid] = t;
+    }
+    __syncthreads();
+    const int my_tok = tok[lr];
+    const uint8_t* xrow = a.x + (int64_t)(my_tok < 0 ? 0 : my_tok) * H;
+    const uint32_t* xsrow = reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)(my_tok < 0 ? 0 : my_tok) * (H / 32));
+
+    const int c0 = ct * PF_ICOLS + wave * 32;                   // first intermediate column of this wavefront
+    const bool wact = c0 < I;
+    // B columns of this lane: gate lo/hi and up lo/hi W13 rows
+    const uint8_t* wb[4];
+    const uint32_t* wsb[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int r13 = (n < 2 ? 0 : I) + (wact ? c0 : 0) + (n & 1) * 16 + col;
+      const int64_t row = (int64_t)e * 2 * I + r13;
+      wb[n] = a.w13 + row * (H / 2);
+      wsb[n] = reinterpret_cast<const uint32_t*>(a.w13_sc + row * (H / 32));
+    }
+
+    u32x4 xa[4];
+    uint32_t xs[PF_KCH];
+    auto load_a = [&](int c) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = c * PF_KCH * KSTEP + lseg * 64 + j * 16;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        xa[j] = (my_tok >= 0 && kb < H) ? ldg16(xrow + kb) : z;
+      }
+#pragma unroll
+      for (int s = 0; s < PF_KCH; ++s) {
+        const int step = c * PF_KCH + s;
+        xs[s] = (my_tok >= 0 && step < nsteps) ? xsrow[step] : 0x7F7F7F7Fu;
+      }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&abuf[buf][lr][lseg * 64 + j * 16]) = xa[j];
+      if (lseg == 0) {
+#pragma unroll
+        for (int s = 0; s < PF_KCH; ++s) asbuf[buf][lr][s] = xs[s];
+      }
+    };
+    u32x4 bcur[4][PF_KCH], bnext[4][PF_KCH];
+    uint32_t scur[4][PF_KCH], snext[4][PF_KCH];
+    auto load_b = [&](int c, u32x4 (&bw)[4][PF_KCH], uint32_t (&bsc)[4][PF_KCH]) {
+#pragma unroll
+      for (int s = 0; s < PF_KCH; ++s) {
+        const int step = c * PF_KCH + s;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const bool ok = wact && step < nsteps;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          bw[n][s] = ok ? ldg16(wb[n] + step * 64 + g * 16) : z;
+          bsc[n][s] = ok ? (wsb[n][step] >> (8 * g)) : 0x7F7F7F7Fu;
+        }
+      }
+    };
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    load_a(0);
+    load_b(0, bcur, scur);
+    store_a(0);
+    for (int c = 0; c < nchunks; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < nchunks) {
+        load_a(c + 1);
+        load_b(c + 1, bnext, snext);
+      }
+      __syncthreads();                                          // stage c is in LDS; stage c-1 reads are done
+#pragma unroll
+      for (int s = 0; s < PF_KCH; ++s) {
+        if (c * PF_KCH + s < nsteps) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint8_t* ap = &abuf[buf][m * 16 + col][s * KSTEP + g * 16];
+            const u32x4 alo = *reinterpret_cast<const u32x4*>(ap);
+            const u32x4 ahi = *reinterpret_cast<const u32x4*>(ap + 64);
+            const uint32_t sa = asbuf[buf][m * 16 + col][s] >> (8 * g);
+            const v8i av = fp8_operand(alo, ahi);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[m][n] = mfma_fp8_fp4(av, fp4_operand(bcur[n][s]), acc[m][n], sa, scur[n][s]);
+          }
+        }
+      }
+      if (c + 1 < nchunks) {
+        store_a(buf ^ 1);
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+          for (int s = 0; s < PF_KCH; ++s) {
+            bcur[n][s] = bnext[n][s];
+            scur[n][s] = snext[n][s];
+          }
+      }
+    }
+
+    // epilogue: SwiGLU + requant, block of 32 = this wavefront's columns of one row
+    if (wact) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v0 = swiglu(acc[m][0][i], acc[m][2][i]);
+          const float v1 = swiglu(acc[m][1][i], acc[m][3][i]);
+          float mx = fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
+          mx = fmaxf(mx, __shfl_xor(mx, 1));
+          mx = fmaxf(mx, __shfl_xor(mx, 2));
+          mx = fmaxf(mx, __shfl_xor(mx, 4));
+          mx = fmaxf(mx, __shfl_xor(mx, 8));
+          const uint32_t sc = e8m0_code_for_amax(mx, 8);
+          const int row = m * 16 + 4 * g + i;
+          if (row < nrows) {
+            uint8_t* qrow = qws + (int64_t)(p0 + row) * I;
+            qrow[c0 + col] = (uint8_t)requant_e4m3(v0, sc);
+            qrow[c0 + 16 + col] = (uint8_t)requant_e4m3(v1, sc);
+            if (col == 0) qsc_ws[(int64_t)(p0 + row) * nb + c0 / 32] = (uint8_t)sc;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Down over a 64-row expert tile and 256 W2 rows (64 per wavefront, four
+// 16-row B tiles); the tile's intermediate rows are contiguous bucket rows.
+__global__ __launch_bounds__(256, 2) void down_prefill_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
+                                                              const uint8_t* __restrict__ qsc_ws,
+                                                              float* __restrict__ o, int Tk) {
+  __shared__ int tile_start[MAX_E + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[PF_ROWS][PF_MAX_I + 16];
+  __shared__ uint8_t slds[PF_ROWS][PF_MAX_I / 32 + 4];
+  build_tiles(a.offsets, a.E, PF_ROWS, tile_start);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int H = a.H, I = a.I, nb = I / 32;
+  const int nsteps = (I + KSTEP - 1) / KSTEP;                   // <= 5
+  const int nnt = H / PF_NCOLS;
+  const int nitems = tile_start[a.E] * nnt;
+
+  for (int round = 0;; ++round) {
+    const int item = xcd_item(round, blockIdx.x, gridDim.x);
+    if (item >= nitems) break;
+    const int tile = item / nnt, nt = item % nnt;
+    const int e = tile_expert(tile_start, a.E, tile);
+    const int p0 = a.offsets[e] + (tile - tile_start[e]) * PF_ROWS;
+    int nrows = a.offsets[e + 1] - p0;
+    nrows = nrows > PF_ROWS ? PF_ROWS : nrows;
+    if (p0 < 0 || p0 + nrows > Tk) nrows = 0;
+
+    // W2 of this lane's four columns first (whole K = I in registers)
+    const int n0 = nt * PF_NCOLS + wave * 64;
+    u32x4 bw[4][5];
+    uint32_t bs[4][5];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int64_t row = (int64_t)e * H + n0 + n * 16 + col;
+      const uint8_t* wp = a.w2 + row * (I / 2);
+      const uint8_t* wsp = a.w2_sc + row * nb;
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const bool bv = s < nsteps && 4 * s + g < nb;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        bw[n][s] = bv ? ldg16(wp + s * 64 + g * 16) : z;
+        bs[n][s] = wsp[bv ? 4 * s + g : 0];
+      }
+    }
+    __syncthreads();                                            // previous item's LDS reads are done
+    const int q16 = I / 16;
+    for (int idx = tid; idx < PF_ROWS * q16; idx += 256) {
+      const int r = idx / q16, c16 = idx % q16;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&qlds[r][c16 * 16]) = r < nrows ? ldg16(qws + (int64_t)(p0 + r) * I + c16 * 16) : z;
+    }
+    for (int idx = tid; idx < PF_ROWS * nb; idx += 256) {
+      const int r = idx / nb, b = idx % nb;
+      slds[r][b] = r < nrows ? qsc_ws[(int64_t)(p0 + r) * nb + b] : (uint8_t)127;
+    }
+    __syncthreads();
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+      if (s < nsteps) {
+        const int klo = s * KSTEP + g * 16, khi = klo + 64;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int r = m * 16 + col;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 alo = klo < I ? *reinterpret_cast<const u32x4*>(&qlds[r][klo]) : z;
+          const u32x4 ahi = khi < I ? *reinterpret_cast<const u32x4*>(&qlds[r][khi]) : z;
+          const uint32_t sa = (4 * s + g < nb) ? (uint32_t)slds[r][4 * s + g] : bs[0][s];
+          const v8i av = fp8_operand(alo, ahi);
+#pragma unroll
+          for (int n = 0; n < 4; ++n) acc[m][n] = mfma_fp8_fp4(av, fp4_operand(bw[n][s]), acc[m][n], sa, bs[n][s]);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + 4 * g + i;
+        if (row < nrows) {
+          float* orow = o + (int64_t)(p0 + row) * H + n0 + col;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) orow[n * 16] = acc[m][n][i];
+        }
+      }
+  }
+}
+
+// ============================================================== combine ===
 // y_t = sum_j w_tj * o[slot_pos[t][j]], j = 0..k-1 in order; 4 columns per thread.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const float* __restrict__ w,
                                                       const int32_t* __restrict__ slot_pos, int T, int H, int k, int Tk,
@@ -237,22 +569,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (n >= H) return;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int p = slot_pos[(int64_t)t * k + j];
-    if (p < 0 || p >= Tk) continue;
-    const float wj = w[(int64_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)p * H + n);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
-  }
-  *reinterpret_cast<float4*>(y + (int64_t)t * H + n) = acc;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int p = slot_pos[(int64_t)t * k + j];
+      if (p < 0 || p >= Tk) continue;
+      const float wj = w[(int64_t)t * k + j];
+      const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)p * H + n);
+      acc.x = fmaf(wj, v.x, acc.x);
+      acc.y = fmaf(wj, v.y, acc.y);
+      acc.z = fmaf(wj, v.z, acc.z);
+      acc.w = fmaf(wj, v.w, acc.w);
+    }
+    *reinterpret_cast<float4*>(y + (int64_t)t * H + n) = acc;
   }
 }
 
-// --------------------------------------------------------------------------
+// ================================================================= host ===
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // workspace: [q: Tk*I][q_sc: Tk*I/32][h: Tk*2I fp32][o: Tk*H fp32], each 256-byte aligned
@@ -272,6 +604,15 @@ size_t ffn_ws_bytes(int T, int H, int E, int I, int k) {
   return o + align256((size_t)T * k * H * 4) + 256;
 }
 
+// Row pairs at or below which the decode kernels are chosen.
+constexpr int DECODE_MAX_PAIRS = 1024;
+
+bool ffn_path_supported(int path, int H, int I) {
+  if (path == 1) return H <= KSTEP * DEC_MAX_STEPS;
+  if (path == 2) return I <= PF_MAX_I && H % PF_NCOLS == 0;
+  return true;
+}
+
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant) {
   const int Tk = a.T * a.k;
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -281,18 +622,34 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
   uint8_t* qsc = base + oqs;
   float* h = reinterpret_cast<float*>(base + oh);
   float* o = reinterpret_cast<float*>(base + oo);
-  (void)path;
-  const int cap = num_cus() * 4;
+  const int cus = num_cus();
   const int max_active = a.E < Tk ? a.E : Tk;
-  const int gu_items = max_active * (2 * a.I / 16);
-  const int dn_items = max_active * (a.H / 64);
-  const int gu_grid = gu_items < cap ? gu_items : cap;
-  const int dn_grid = dn_items < cap ? dn_items : cap;
-  if (gu_grid > 0) hipLaunchKernelGGL(gu_decode_kernel, dim3(gu_grid), dim3(256), 0, stream, a, h, Tk);
-  if (dn_grid > 0) hipLaunchKernelGGL(down_decode_kernel, dim3(dn_grid), dim3(256), 0, stream, a, h, qws, qsc, o, Tk);
+  if (path == 0) {
+    const bool dec_ok = ffn_path_supported(1, a.H, a.I), pre_ok = ffn_path_supported(2, a.H, a.I);
+    path = ((Tk <= DECODE_MAX_PAIRS && dec_ok) || !pre_ok) ? 1 : 2;
+  }
+  if (path == 1) {
+    const int gu_items = max_active * ((2 * a.I + 63) / 64);
+    const int dn_items = max_active * (a.H / 64);
+    const int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
+    const int dn_grid = dn_items < cus * 4 ? dn_items : cus * 4;
+    hipLaunchKernelGGL(gu_decode_kernel, dim3(gu_grid), dim3(256), 0, stream, a, h, Tk);
+    hipLaunchKernelGGL(down_decode_kernel, dim3(dn_grid), dim3(256), 0, stream, a, h, qws, qsc, o, Tk);
+    *variant = "ffn:gu_decode+down_decode+combine";
+  } else {
+    const int tiles_bound = Tk / PF_ROWS + max_active;
+    const int nct = (a.I + PF_ICOLS - 1) / PF_ICOLS;
+    const int gu_items = tiles_bound * nct, dn_items = tiles_bound * (a.H / PF_NCOLS);
+    int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
+    int dn_grid = dn_items < cus * 2 ? dn_items : cus * 2;
+    gu_grid = (gu_grid + XCDS - 1) / XCDS * XCDS;
+    dn_grid = (dn_grid + XCDS - 1) / XCDS * XCDS;
+    hipLaunchKernelGGL(gu_prefill_kernel, dim3(gu_grid), dim3(256), 0, stream, a, qws, qsc, Tk);
+    hipLaunchKernelGGL(down_prefill_kernel, dim3(dn_grid), dim3(256), 0, stream, a, qws, qsc, o, Tk);
+    *variant = "ffn:gu_prefill64+down_prefill64+combine";
+  }
   const dim3 cgrid((a.H / 4 + 255) / 256, a.T < 65535 ? a.T : 65535);
   hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, o, a.topk_w, a.slot_pos, a.T, a.H, a.k, Tk, a.y);
-  *variant = "ffn:gu_decode16+down_decode16+combine";
   return hipGetLastError();
 }
 

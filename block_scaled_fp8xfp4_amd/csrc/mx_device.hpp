@@ -13,13 +13,18 @@
 //   - D: lane l holds column l % 16, rows 4g + r in register r.
 // The FP8 encoding is OCP E4M3 (bias 7, max 448).
 //
-// Canonical reduction order used by every GEMM here (decode and prefill
-// alike, so that a row's result never depends on the path or the batch):
+// Canonical reduction orders (one per GEMM, the same for every batch size
+// and every path, so that a row's result never depends on either):
 //   K is cut into steps of 128 (step m covers K blocks 4m..4m+3 of 32); a
 //   step whose blocks run past K is padded with zero elements in registers.
-//   Steps are grouped in parts of KPART_STEPS consecutive steps; each part is
-//   a chain of MFMAs started from zero, and the parts are added left to
-//   right in fp32: total = ((p0 + p1) + p2) + ...
+//   - Routed-expert gate/up and down: one MFMA chain over all steps in
+//     order, accumulator started from zero and carried through C.
+//   - Dense projection: steps grouped in parts of KPART_STEPS; each part is
+//     a chain started from zero, and the parts are added left to right in
+//     fp32: total = ((p0 + p1) + p2) + ...  (lets four wavefronts split K).
+// The scaled MFMA does not round its 128-product sum exactly (measured on
+// MI355X: a few 1e-6 relative), identically for every chaining tried, so the
+// chain choice is about parallelism, not accuracy.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -97,9 +102,17 @@ __device__ __forceinline__ uint32_t encode_e2m1(float v, uint32_t sc) {
 }
 
 // SwiGLU of one gate/up pair in fp32: silu(g) * u, silu(g) = g / (1 + e^-g).
+// Contraction is off so every kernel that inlines it rounds identically.
 __device__ __forceinline__ float swiglu(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
+#pragma clang fp contract(off)
+  const float d = 1.0f + expf(-g);
+  const float s = g / d;
+  return s * u;
 }
+
+// E4M3 code of one element of a block whose shared scale code is sc (the
+// requant of the intermediate): identical in every kernel that uses it.
+__device__ __forceinline__ uint32_t requant_e4m3(float a, uint32_t sc) { return encode_e4m3(a, sc); }
 
 // Quantize 32 fp32 values to E4M3: writes 32 code bytes as 8 dwords, returns the scale code.
 __device__ __forceinline__ uint32_t quantize32_e4m3(const float* v, uint32_t* out8) {

@@ -29,6 +29,8 @@ struct FfnArgs {
 };
 size_t ffn_ws_bytes(int T, int H, int E, int I, int k);
 void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h, size_t* off_o);
+// path: 0 automatic, 1 decode kernels, 2 prefill kernels
+bool ffn_path_supported(int path, int H, int I);
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant);
 
 hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,

@@ -1,0 +1,77 @@
+"""Batch invariance and determinism on the GPU (no oracle): every row's
+output is bitwise the same whichever path (decode or prefill kernels) ran it,
+whatever other rows shared its batch, and on every repetition."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_fp8xfp4_amd import mxmoe
+from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route
+from gpu_common import dev, host, moe_workload, say, small_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def run(layer, rows=None, path=0):
+    old = mxmoe.set_ffn_path(path)
+    try:
+        y, route, ffn = layer.gpu_y(rows)
+        q, qsc, _, o = ffn.ws_views()
+        variant = mxmoe.last_variant()
+        return host(y), host(q), host(qsc), route, variant
+    finally:
+        mxmoe.set_ffn_path(old)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(seed=41, T=300, H=512, E=16, k=4, I=96, skip=0.2),     # ragged 64-row tiles, I < 128
+    dict(seed=42, T=97, H=256, E=4, k=2, I=160, skip=0.0),      # ~48 rows per expert, two column tiles
+    dict(seed=43, T=130, H=1024, E=8, k=8, I=576, skip=0.0),    # every expert hit by every row: 130 rows
+])
+def test_decode_and_prefill_paths_are_bitwise_equal(shape):
+    inp, r, layer = small_workload(**shape)
+    yd, qd, sd, _, vd = run(layer, path=1)
+    yp, qp, sp, _, vp = run(layer, path=2)
+    assert "decode" in vd and "prefill" in vp
+    P = int(r["offsets"][-1])
+    assert np.array_equal(qd[:P], qp[:P]) and np.array_equal(sd[:P], sp[:P])
+    assert np.array_equal(yd.view(np.uint32), yp.view(np.uint32))
+
+
+def test_verify_workload_paths_are_bitwise_equal():
+    inp, r, layer = moe_workload("verify")
+    yd, qd, _, _, _ = run(layer, path=1)
+    yp, qp, _, _, _ = run(layer, path=2)
+    assert np.array_equal(yd.view(np.uint32), yp.view(np.uint32))
+
+
+def test_prefill_rows_rerun_in_batches_of_1_to_64():
+    """Rows 0..255 of the 8192-token chunk, rerun in every batch size 1..64
+    (decode kernels) and in seeded random row subsets, equal the full-chunk run
+    (prefill kernels) bit for bit."""
+    inp, r, layer = moe_workload("prefill")
+    full, _, _, _, vfull = run(layer)
+    assert "prefill" in vfull
+    ref = full.view(np.uint32)
+    checked = 0
+    for b in range(1, 65):
+        for s in range(0, 256, b):
+            rows = np.arange(s, min(256, s + b))
+            y, _, _, _, v = run(layer, rows)
+            assert "decode" in v
+            assert np.array_equal(y.view(np.uint32), ref[rows]), (b, s)
+            checked += 1
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        rows = np.sort(rng.choice(inp.cfg.T, rng.integers(1, 200), replace=False))
+        y, _, _, _, _ = run(layer, rows)
+        assert np.array_equal(y.view(np.uint32), ref[rows])
+    say(f"batch invariance: {checked} batched calls + 20 random subsets bitwise equal")
+
+
+def test_repeated_calls_are_bitwise_identical():
+    inp, r, layer = moe_workload("verify")
+    first, _, _, _, _ = run(layer)
+    for _ in range(50):
+        again, _, _, _, _ = run(layer)
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
