@@ -13,11 +13,11 @@
 // matrix cores.
 //
 // Decode path (few rows per expert, weight streaming):
-//   gu_decode_kernel    one workgroup per (expert, 64 W13 rows): each
-//                       wavefront loads the whole K of its 16 weight rows
-//                       into registers at once; the expert's activation rows
-//                       are staged in LDS 16 at a time; writes fp32
-//                       h = [gate | up] per bucket position.
+//   gu_decode_kernel    one wavefront per (expert, 16 W13 rows): the whole K
+//                       of its weight rows is loaded into registers at once;
+//                       the expert's activation rows are staged in LDS, at
+//                       most min(16, T) at a time; writes fp32 h = [gate |
+//                       up] per bucket position.
 //   down_decode_kernel  one workgroup per (expert, 64 W2 rows): W2 first,
 //                       then SwiGLU + requant of the rows' h into LDS (8
 //                       lanes per block of 32), then the down chain.
@@ -120,79 +120,104 @@ __device__ __forceinline__ v8i fp4_operand(const u32x4& b) {
 }
 
 // =========================================================== decode path ==
-// Gate/up: a workgroup takes (expert, 64 W13 rows); wavefront w streams the
-// whole K of W13 rows [16w, 16w + 16) of that group into registers, while
-// the workgroup stages the expert's activation rows (16 at a time) in LDS.
-constexpr int DEC_AROW = KSTEP * DEC_MAX_STEPS + 16;   // LDS pitch of a staged activation row
-
-__global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, float* __restrict__ h, int Tk) {
+// Gate/up: one wavefront per (expert, 16 W13 rows).  It first issues the
+// loads of the whole K of its 16 weight rows (registers), then stages the
+// expert's activation rows, at most R = min(16, T) at a time, in its own LDS
+// (dynamic, R * (H + 16) + R * H / 32 bytes) and runs the chain.
+__global__ __launch_bounds__(64) void gu_decode_kernel(FfnArgs a, float* __restrict__ h, int Tk, int R) {
   __shared__ int tile_start[MAX_E + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t xlds[16][DEC_AROW];
-  __shared__ uint32_t xslds[16][DEC_MAX_STEPS];
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   build_tiles(a.offsets, a.E, 0, tile_start);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
   const int H = a.H, twoI = 2 * a.I;
   const int nsteps = H / KSTEP;
-  const int ngroups = (twoI + 63) / 64;
-  const int nitems = tile_start[a.E] * ngroups;
+  const int pitch = H + 16;
+  uint8_t* xlds = dyn_lds;                                      // [R][H + 16]
+  uint32_t* xslds = reinterpret_cast<uint32_t*>(dyn_lds + (size_t)R * pitch);   // [R][nsteps]
+  const int ntiles = twoI / 16;
+  const int nitems = tile_start[a.E] * ntiles;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int e = tile_expert(tile_start, a.E, item / ngroups), grp = item % ngroups;
+    const int e = tile_expert(tile_start, a.E, item / ntiles), nt = item % ntiles;
     const int p0 = a.offsets[e];
     int cnt = a.offsets[e + 1] - p0;
     if (p0 < 0 || p0 + cnt > Tk) cnt = 0;                       // malformed route: skip
-    const int nrow13 = grp * 64 + wave * 16;                    // first W13 row of this wavefront
-    const bool wact = nrow13 < twoI;
-    const int64_t wrow = (int64_t)e * twoI + (wact ? nrow13 : 0) + col;   // B column of this lane
+    const int64_t wrow = (int64_t)e * twoI + nt * 16 + col;     // B column of this lane
     const uint8_t* wp = a.w13 + wrow * (H / 2);
     const uint32_t* wsp = reinterpret_cast<const uint32_t*>(a.w13_sc + wrow * (H / 32));
+    // every weight load of the 16 rows is issued before anything waits on one;
+    // scale dwords stay raw (the lane's byte is picked at the MFMA)
     u32x4 bw[DEC_MAX_STEPS];
-    uint32_t bs[DEC_MAX_STEPS];
+    uint32_t bsr[DEC_MAX_STEPS];
 #pragma unroll
-    for (int s = 0; s < DEC_MAX_STEPS; ++s) {
-      if (s < nsteps) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        bw[s] = wact ? ldg16(wp + s * 64 + g * 16) : z;
-        bs[s] = wact ? (wsp[s] >> (8 * g)) : 0x7F7F7F7Fu;
+    for (int c = 0; c < DEC_MAX_STEPS / 8; ++c) {
+      if (c * 8 + 8 <= nsteps) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          bw[c * 8 + m] = ldg16(wp + (c * 8 + m) * 64 + g * 16);
+          bsr[c * 8 + m] = wsp[c * 8 + m];
+        }
+      } else if (c * 8 < nsteps) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          if (c * 8 + m < nsteps) {
+            bw[c * 8 + m] = ldg16(wp + (c * 8 + m) * 64 + g * 16);
+            bsr[c * 8 + m] = wsp[c * 8 + m];
+          }
       }
     }
-    for (int rt = 0; rt * 16 < cnt; ++rt) {
-      const int nrows = min(16, cnt - rt * 16);
-      __syncthreads();                                          // previous row tile's LDS reads are done
-      // stage the rows: 16 bytes per thread per pass, rows in order
-      const int q16 = H / 16;
-      for (int idx = tid; idx < nrows * q16; idx += 256) {
-        const int r = idx / q16, c16 = idx % q16;
-        const int pr = a.perm[p0 + rt * 16 + r];
-        const int tok = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
+    for (int r0 = 0; r0 < cnt; r0 += R) {
+      const int nrows = min(R, cnt - r0);
+      // token of staged row `lane` (lanes < nrows), read once
+      int my_tok = -1;
+      if (lane < nrows) {
+        const int pr = a.perm[p0 + r0 + lane];
+        my_tok = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
+      }
+      lds_barrier();                                            // previous rows' LDS reads are done
+      for (int r = 0; r < nrows; ++r) {
+        const int tok = __shfl(my_tok, r);
+        const uint8_t* src = a.x + (int64_t)(tok < 0 ? 0 : tok) * H;
+        uint8_t* dst = xlds + (size_t)r * pitch;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&xlds[r][c16 * 16]) = tok >= 0 ? ldg16(a.x + (int64_t)tok * H + c16 * 16) : z;
+        u32x4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int off = (j * 64 + lane) * 16;
+          v[j] = (tok >= 0 && off < H) ? ldg16(src + off) : z;
+        }
+        const int sidx = lane;
+        const uint32_t sv = (tok >= 0 && sidx < nsteps)
+                                ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)tok * (H / 32))[sidx]
+                                : 0x7F7F7F7Fu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int off = (j * 64 + lane) * 16;
+          if (off < H) *reinterpret_cast<u32x4*>(dst + off) = v[j];
+        }
+        if (sidx < nsteps) xslds[r * nsteps + sidx] = sv;
       }
-      for (int idx = tid; idx < nrows * nsteps; idx += 256) {
-        const int r = idx / nsteps, st = idx % nsteps;
-        const int pr = a.perm[p0 + rt * 16 + r];
-        const int tok = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
-        xslds[r][st] = tok >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)tok * (H / 32))[st] : 0x7F7F7F7Fu;
-      }
-      __syncthreads();
-      if (wact) {
-        const bool rv = col < nrows;
+      lds_barrier();
+      for (int rt = 0; rt < nrows; rt += 16) {
+        const int rr = rt + col;                                // staged row of this lane
+        const bool rv = rr < nrows;
+        const uint8_t* arow = xlds + (size_t)(rv ? rr : 0) * pitch;
+        const uint32_t* asrow = xslds + (rv ? rr : 0) * nsteps;
         v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < DEC_MAX_STEPS; ++s) {
           if (s < nsteps) {
             const u32x4 z = {0u, 0u, 0u, 0u};
-            const uint8_t* ap = &xlds[col][s * KSTEP + g * 16];
-            const u32x4 alo = rv ? *reinterpret_cast<const u32x4*>(ap) : z;
-            const u32x4 ahi = rv ? *reinterpret_cast<const u32x4*>(ap + 64) : z;
-            const uint32_t sa = rv ? (xslds[col][s] >> (8 * g)) : bs[s];
-            acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, sa, bs[s]);
+            const u32x4 alo = rv ? *reinterpret_cast<const u32x4*>(arow + s * KSTEP + g * 16) : z;
+            const u32x4 ahi = rv ? *reinterpret_cast<const u32x4*>(arow + s * KSTEP + 64 + g * 16) : z;
+            const uint32_t sb = bsr[s] >> (8 * g);
+            const uint32_t sa = rv ? (asrow[s] >> (8 * g)) : sb;
+            acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, sa, sb);
           }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 4 * g + i;
-          if (row < nrows) h[(int64_t)(p0 + rt * 16 + row) * twoI + nrow13 + col] = acc[i];
+          const int row = rt + 4 * g + i;
+          if (row < nrows) h[(int64_t)(p0 + r0 + row) * twoI + nt * 16 + col] = acc[i];
         }
       }
     }
@@ -277,7 +302,7 @@ __global__ __launch_bounds__(256) void down_decode_kernel(FfnArgs a, const float
     for (int rt = 0; rt * 16 < cnt; ++rt) {
       const int nrows = min(16, cnt - rt * 16);
       stage_intermediate(h, p0 + rt * 16, nrows, I, qlds, slds, qws, qsc_ws, tile == 0);
-      __syncthreads();
+      lds_barrier();
       const bool rv = col < nrows;
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -296,7 +321,7 @@ __global__ __launch_bounds__(256) void down_decode_kernel(FfnArgs a, const float
         const int row = 4 * g + i;
         if (row < nrows) o[(int64_t)(p0 + rt * 16 + row) * H + n] = acc[i];
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 }
@@ -332,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void gu_prefill_kernel(FfnArgs a, uint8_t* 
     int nrows = a.offsets[e + 1] - p0;
     nrows = nrows > PF_ROWS ? PF_ROWS : nrows;
     if (p0 < 0 || p0 + nrows > Tk) nrows = 0;
-    __syncthreads();                                            // previous item's LDS reads are done
+    lds_barrier();                                              // previous item's LDS reads are done
     if (tid < PF_ROWS) {
       int t = -1;
       if (tid < nrows) {
@@ -341,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void gu_prefill_kernel(FfnArgs a, uint8_t* 
       }
       tok[tid] = t;
     }
-    __syncthreads();
+    lds_barrier();
     const int my_tok = tok[lr];
     const uint8_t* xrow = a.x + (int64_t)(my_tok < 0 ? 0 : my_tok) * H;
     const uint32_t* xsrow = reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)(my_tok < 0 ? 0 : my_tok) * (H / 32));
@@ -383,18 +408,28 @@ __global__ __launch_bounds__(256, 2) void gu_prefill_kernel(FfnArgs a, uint8_t* 
       }
     };
     u32x4 bcur[4][PF_KCH], bnext[4][PF_KCH];
-    uint32_t scur[4][PF_KCH], snext[4][PF_KCH];
+    uint32_t scur[4][PF_KCH], snext[4][PF_KCH];                // raw scale dwords
     auto load_b = [&](int c, u32x4 (&bw)[4][PF_KCH], uint32_t (&bsc)[4][PF_KCH]) {
+      if (!wact) return;                                        // wavefront-uniform
+      if (c * PF_KCH + PF_KCH <= nsteps) {
 #pragma unroll
-      for (int s = 0; s < PF_KCH; ++s) {
-        const int step = c * PF_KCH + s;
+        for (int s = 0; s < PF_KCH; ++s)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const bool ok = wact && step < nsteps;
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          bw[n][s] = ok ? ldg16(wb[n] + step * 64 + g * 16) : z;
-          bsc[n][s] = ok ? (wsb[n][step] >> (8 * g)) : 0x7F7F7F7Fu;
-        }
+          for (int n = 0; n < 4; ++n) {
+            const int step = c * PF_KCH + s;
+            bw[n][s] = ldg16(wb[n] + step * 64 + g * 16);
+            bsc[n][s] = wsb[n][step];
+          }
+      } else {
+#pragma unroll
+        for (int s = 0; s < PF_KCH; ++s)
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            const int step = c * PF_KCH + s;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            bw[n][s] = step < nsteps ? ldg16(wb[n] + step * 64 + g * 16) : z;
+            bsc[n][s] = step < nsteps ? wsb[n][step] : 0x7F7F7F7Fu;
+          }
       }
     };
 
@@ -409,11 +444,11 @@ __global__ __launch_bounds__(256, 2) void gu_prefill_kernel(FfnArgs a, uint8_t* 
     store_a(0);
     for (int c = 0; c < nchunks; ++c) {
       const int buf = c & 1;
-      if (c + 1 < nchunks) {
+      lds_barrier();                                            // stage c is in LDS; stage c-1 reads are done
+      if (c + 1 < nchunks) {                                    // next stage's loads stay in flight during the MFMAs
         load_a(c + 1);
         load_b(c + 1, bnext, snext);
       }
-      __syncthreads();                                          // stage c is in LDS; stage c-1 reads are done
 #pragma unroll
       for (int s = 0; s < PF_KCH; ++s) {
         if (c * PF_KCH + s < nsteps) {
@@ -425,7 +460,8 @@ __global__ __launch_bounds__(256, 2) void gu_prefill_kernel(FfnArgs a, uint8_t* 
             const uint32_t sa = asbuf[buf][m * 16 + col][s] >> (8 * g);
             const v8i av = fp8_operand(alo, ahi);
 #pragma unroll
-            for (int n = 0; n < 4; ++n) acc[m][n] = mfma_fp8_fp4(av, fp4_operand(bcur[n][s]), acc[m][n], sa, scur[n][s]);
+            for (int n = 0; n < 4; ++n)
+              acc[m][n] = mfma_fp8_fp4(av, fp4_operand(bcur[n][s]), acc[m][n], sa, scur[n][s] >> (8 * g));
           }
         }
       }
@@ -512,7 +548,7 @@ __global__ __launch_bounds__(256, 2) void down_prefill_kernel(FfnArgs a, const u
         bs[n][s] = wsp[bv ? 4 * s + g : 0];
       }
     }
-    __syncthreads();                                            // previous item's LDS reads are done
+    lds_barrier();                                              // previous item's LDS reads are done
     const int q16 = I / 16;
     for (int idx = tid; idx < PF_ROWS * q16; idx += 256) {
       const int r = idx / q16, c16 = idx % q16;
@@ -523,7 +559,7 @@ __global__ __launch_bounds__(256, 2) void down_prefill_kernel(FfnArgs a, const u
       const int r = idx / nb, b = idx % nb;
       slds[r][b] = r < nrows ? qsc_ws[(int64_t)(p0 + r) * nb + b] : (uint8_t)127;
     }
-    __syncthreads();
+    lds_barrier();
 
     v4f acc[4][4];
 #pragma unroll
@@ -629,11 +665,13 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     path = ((Tk <= DECODE_MAX_PAIRS && dec_ok) || !pre_ok) ? 1 : 2;
   }
   if (path == 1) {
-    const int gu_items = max_active * ((2 * a.I + 63) / 64);
+    const int R = a.T < 16 ? a.T : 16;                          // rows of one expert never exceed T
+    const size_t lds = (size_t)R * (a.H + 16) + (size_t)R * (a.H / KSTEP) * 4;
+    const int gu_items = max_active * (2 * a.I / 16);
     const int dn_items = max_active * (a.H / 64);
-    const int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
+    const int gu_grid = gu_items < cus * 8 ? gu_items : cus * 8;
     const int dn_grid = dn_items < cus * 4 ? dn_items : cus * 4;
-    hipLaunchKernelGGL(gu_decode_kernel, dim3(gu_grid), dim3(256), 0, stream, a, h, Tk);
+    hipLaunchKernelGGL(gu_decode_kernel, dim3(gu_grid), dim3(64), lds, stream, a, h, Tk, R);
     hipLaunchKernelGGL(down_decode_kernel, dim3(dn_grid), dim3(256), 0, stream, a, h, qws, qsc, o, Tk);
     *variant = "ffn:gu_decode+down_decode+combine";
   } else {

@@ -41,29 +41,44 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint8_t* __restr
       const int s0 = q * KPART_STEPS;
       u32x4 blo[KPART_STEPS], bhi[KPART_STEPS], alo[KPART_STEPS], ahi[KPART_STEPS];
       uint32_t bs[KPART_STEPS], as[KPART_STEPS];
+      // weights then activations: every load of the part is in flight before
+      // any is used; scale dwords stay raw until the MFMA
+      if (s0 + KPART_STEPS <= nsteps) {
 #pragma unroll
-      for (int m = 0; m < KPART_STEPS; ++m) {
-        const int s = s0 + m;
-        if (s < nsteps) {
+        for (int m = 0; m < KPART_STEPS; ++m) {
+          const int s = s0 + m;
           blo[m] = ldg16(wp + s * KSTEP + g * 16);
           bhi[m] = ldg16(wp + s * KSTEP + 64 + g * 16);
-          bs[m] = wsp[s] >> (8 * g);
+          bs[m] = wsp[s];
         }
-      }
 #pragma unroll
-      for (int m = 0; m < KPART_STEPS; ++m) {
-        const int s = s0 + m;
-        if (s < nsteps) {
+        for (int m = 0; m < KPART_STEPS; ++m) {
+          const int s = s0 + m;
           const u32x4 z = {0u, 0u, 0u, 0u};
           alo[m] = rv ? ldg16(ap + s * KSTEP + g * 16) : z;
           ahi[m] = rv ? ldg16(ap + s * KSTEP + 64 + g * 16) : z;
-          as[m] = rv ? (asp[s] >> (8 * g)) : bs[m];
+          as[m] = rv ? asp[s] : bs[m];
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < KPART_STEPS; ++m) {
+          const int s = s0 + m;
+          if (s < nsteps) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            blo[m] = ldg16(wp + s * KSTEP + g * 16);
+            bhi[m] = ldg16(wp + s * KSTEP + 64 + g * 16);
+            bs[m] = wsp[s];
+            alo[m] = rv ? ldg16(ap + s * KSTEP + g * 16) : z;
+            ahi[m] = rv ? ldg16(ap + s * KSTEP + 64 + g * 16) : z;
+            as[m] = rv ? asp[s] : bs[m];
+          }
         }
       }
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < KPART_STEPS; ++m)
-        if (s0 + m < nsteps) acc = mfma_fp8_fp8(fp8_pair(alo[m], ahi[m]), fp8_pair(blo[m], bhi[m]), acc, as[m], bs[m]);
+        if (s0 + m < nsteps)
+          acc = mfma_fp8_fp8(fp8_pair(alo[m], ahi[m]), fp8_pair(blo[m], bhi[m]), acc, as[m] >> (8 * g), bs[m] >> (8 * g));
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[q][4 * g + i][col] = acc[i];
     }

@@ -52,6 +52,15 @@ __device__ __forceinline__ u32x4 ldg16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also releases
+// global memory, which on gfx9-class hardware waits for every outstanding
+// global load (vmcnt(0)) and would drain the prefetches that are meant to
+// stay in flight across the barrier; this one waits for LDS operations only.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Block-32 quantization (OCP MX v1.0 conversion): shared scale
 // X = 2^(floor(log2 amax) - emax) as an E8M0 code clamped to [0, 254]
