@@ -22,11 +22,11 @@
 //                       then SwiGLU + requant of the rows' h into LDS (8
 //                       lanes per block of 32), then the down chain.
 // Prefill path (hundreds of rows per expert, matrix-core bound):
-//   gu_prefill_kernel   64-row expert tile x 128 intermediate columns (256
-//                       W13 rows) per workgroup; gathered activation rows are
-//                       staged through LDS two steps at a time, each
-//                       wavefront streams its own 64 weight rows straight to
-//                       registers; SwiGLU + requant in the epilogue.
+//   gu_prefill_kernel   expert tile of up to 128 rows x 128 intermediate
+//                       columns (256 W13 rows) per workgroup, 2 x 2
+//                       wavefronts; gathered activation rows and weight rows
+//                       staged through swizzled, double-buffered LDS one MFMA
+//                       step at a time; SwiGLU + requant in the epilogue.
 //   down_prefill_kernel 64-row tile x 256 W2 rows per workgroup; the tile's
 //                       whole intermediate (K = I) sits in LDS.
 //   Both run persistent grids whose blocks are remapped so that each XCD
@@ -327,38 +327,57 @@ __global__ __launch_bounds__(256) void down_decode_kernel(FfnArgs a, const float
 }
 
 // ========================================================== prefill path ==
-// Gate/up over a 64-row expert tile and 128 intermediate columns; wavefront w
-// owns intermediate columns [32w, 32w + 32) of the tile: W13 rows gate c0 +
-// [0,32) and up I + c0 + [0,32), i.e. four 16-row B tiles, against the four
-// 16-row A tiles of the expert tile (16 accumulators).
-__global__ __launch_bounds__(256, 2) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
+// Gate/up over an expert tile of up to 128 rows and 128 intermediate columns
+// (256 W13 rows: the 128 gate rows, then the 128 up rows).  Wavefront (wm,
+// wn) computes rows [64 wm, 64 wm + 64) x intermediate columns [64 wn, 64 wn
+// + 64): four 16-row A tiles against eight 16-row B tiles (4 gate + 4 up).
+// One MFMA step (K = 128) per stage: the gathered activation rows (16 KB),
+// the weight rows (16 KB) and their scale dwords go global -> registers ->
+// LDS, double-buffered, the next stage's loads in flight during the MFMAs.
+// LDS rows are XOR-swizzled by 16-byte chunk so that the 16 rows one MFMA
+// operand read touches fall in distinct banks.
+constexpr int GU_BM = 128;
+constexpr int GU_BN = 256;                        // W13 rows per tile (128 intermediate columns)
+constexpr int GU_ICOLS = GU_BN / 2;
+
+__device__ __forceinline__ int a_phys(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }   // 16-byte chunk
+__device__ __forceinline__ int b_phys(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+struct GuStage {
+  u32x4 a[GU_BM * 8];                             // [row][8 chunks] swizzled
+  u32x4 b[GU_BN * 4];                             // [row][4 chunks] swizzled
+  uint32_t as[GU_BM];
+  uint32_t bs[GU_BN];
+};
+
+__global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
                                                             uint8_t* __restrict__ qsc_ws, int Tk) {
   __shared__ int tile_start[MAX_E + 1];
-  __shared__ int tok[PF_ROWS];
-  __shared__ __attribute__((aligned(16))) uint8_t abuf[2][PF_ROWS][PF_AROW];
-  __shared__ uint32_t asbuf[2][PF_ROWS][PF_KCH];
-  build_tiles(a.offsets, a.E, PF_ROWS, tile_start);
+  __shared__ int tok[GU_BM];
+  __shared__ GuStage st[2];
+  build_tiles(a.offsets, a.E, GU_BM, tile_start);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
   const int H = a.H, I = a.I, nb = I / 32;
-  const int nsteps = H / KSTEP, nchunks = (nsteps + PF_KCH - 1) / PF_KCH;
-  const int nct = (I + PF_ICOLS - 1) / PF_ICOLS;
+  const int nsteps = H / KSTEP;
+  const int nct = (I + GU_ICOLS - 1) / GU_ICOLS;
   const int nitems = tile_start[a.E] * nct;
-  // cooperative activation loads: thread -> (row, 64-byte segment of a 256-byte stage)
-  const int lr = tid >> 2, lseg = tid & 3;
 
   for (int round = 0;; ++round) {
     const int item = xcd_item(round, blockIdx.x, gridDim.x);
     if (item >= nitems) break;
     const int tile = item / nct, ct = item % nct;
     const int e = tile_expert(tile_start, a.E, tile);
-    const int p0 = a.offsets[e] + (tile - tile_start[e]) * PF_ROWS;
+    const int p0 = a.offsets[e] + (tile - tile_start[e]) * GU_BM;
     int nrows = a.offsets[e + 1] - p0;
-    nrows = nrows > PF_ROWS ? PF_ROWS : nrows;
+    nrows = nrows > GU_BM ? GU_BM : nrows;
     if (p0 < 0 || p0 + nrows > Tk) nrows = 0;
+    const int c0 = ct * GU_ICOLS;                               // first intermediate column of the tile
+    const int ncols = min(GU_ICOLS, I - c0);
     lds_barrier();                                              // previous item's LDS reads are done
-    if (tid < PF_ROWS) {
+    if (tid < GU_BM) {
       int t = -1;
       if (tid < nrows) {
         const int pr = a.perm[p0 + tid];
@@ -367,136 +386,122 @@ __global__ __launch_bounds__(256, 2) void gu_prefill_kernel(FfnArgs a, uint8_t* 
       tok[tid] = t;
     }
     lds_barrier();
-    const int my_tok = tok[lr];
-    const uint8_t* xrow = a.x + (int64_t)(my_tok < 0 ? 0 : my_tok) * H;
-    const uint32_t* xsrow = reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)(my_tok < 0 ? 0 : my_tok) * (H / 32));
 
-    const int c0 = ct * PF_ICOLS + wave * 32;                   // first intermediate column of this wavefront
-    const bool wact = c0 < I;
-    // B columns of this lane: gate lo/hi and up lo/hi W13 rows
-    const uint8_t* wb[4];
-    const uint32_t* wsb[4];
+    // this thread's staging slots: 4 activation chunks, 4 weight chunks, one scale dword each
+    const uint8_t* asrc[4];
+    const uint8_t* bsrc[4];
+    bool aok[4], bok[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int r13 = (n < 2 ? 0 : I) + (wact ? c0 : 0) + (n & 1) * 16 + col;
-      const int64_t row = (int64_t)e * 2 * I + r13;
-      wb[n] = a.w13 + row * (H / 2);
-      wsb[n] = reinterpret_cast<const uint32_t*>(a.w13_sc + row * (H / 32));
+    for (int j = 0; j < 4; ++j) {
+      const int qa = tid + 256 * j, r = qa >> 3, c = qa & 7;
+      const int t = tok[r];
+      aok[j] = t >= 0;
+      asrc[j] = a.x + (int64_t)(t < 0 ? 0 : t) * H + c * 16;
+      const int qb = tid + 256 * j, rb = qb >> 2, cb = qb & 3;
+      const int icol = (rb & 127);                              // intermediate column within the tile
+      bok[j] = icol < ncols;
+      const int r13 = (rb < 128 ? 0 : I) + c0 + (bok[j] ? icol : 0);
+      bsrc[j] = a.w13 + ((int64_t)e * 2 * I + r13) * (H / 2) + cb * 16;
     }
+    const int tas = tok[tid & (GU_BM - 1)];
+    const uint32_t* asc_src = reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)(tas < 0 ? 0 : tas) * (H / 32));
+    const bool asc_ok = tid < GU_BM && tas >= 0;
+    const int icol_s = tid & 127;
+    const bool bsc_ok = icol_s < ncols;
+    const uint32_t* bsc_src = reinterpret_cast<const uint32_t*>(
+        a.w13_sc + ((int64_t)e * 2 * I + (tid < 128 ? 0 : I) + c0 + (bsc_ok ? icol_s : 0)) * (H / 32));
 
-    u32x4 xa[4];
-    uint32_t xs[PF_KCH];
-    auto load_a = [&](int c) {
+    // two register sets of staged loads: stage s + 2 is requested while stage
+    // s is multiplied and stage s + 1 waits in registers for its LDS buffer
+    struct Regs { u32x4 a[4], b[4]; uint32_t as, bs; };
+    Regs R0, R1;                                                // named, never indexed: they stay in registers
+    auto load_stage = [&](int s, Regs& r) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int kb = c * PF_KCH * KSTEP + lseg * 64 + j * 16;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        xa[j] = (my_tok >= 0 && kb < H) ? ldg16(xrow + kb) : z;
+        r.a[j] = aok[j] ? ldg16(asrc[j] + s * KSTEP) : z;
+        r.b[j] = bok[j] ? ldg16(bsrc[j] + s * 64) : z;
       }
-#pragma unroll
-      for (int s = 0; s < PF_KCH; ++s) {
-        const int step = c * PF_KCH + s;
-        xs[s] = (my_tok >= 0 && step < nsteps) ? xsrow[step] : 0x7F7F7F7Fu;
-      }
+      r.as = asc_ok ? asc_src[s] : 0x7F7F7F7Fu;
+      r.bs = bsc_ok ? bsc_src[s] : 0x7F7F7F7Fu;
     };
-    auto store_a = [&](int buf) {
+    auto store_stage = [&](GuStage& S, const Regs& r) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&abuf[buf][lr][lseg * 64 + j * 16]) = xa[j];
-      if (lseg == 0) {
-#pragma unroll
-        for (int s = 0; s < PF_KCH; ++s) asbuf[buf][lr][s] = xs[s];
+      for (int j = 0; j < 4; ++j) {
+        const int qa = tid + 256 * j;
+        S.a[a_phys(qa >> 3, qa & 7)] = r.a[j];
+        S.b[b_phys(qa >> 2, qa & 3)] = r.b[j];
       }
-    };
-    u32x4 bcur[4][PF_KCH], bnext[4][PF_KCH];
-    uint32_t scur[4][PF_KCH], snext[4][PF_KCH];                // raw scale dwords
-    auto load_b = [&](int c, u32x4 (&bw)[4][PF_KCH], uint32_t (&bsc)[4][PF_KCH]) {
-      if (!wact) return;                                        // wavefront-uniform
-      if (c * PF_KCH + PF_KCH <= nsteps) {
-#pragma unroll
-        for (int s = 0; s < PF_KCH; ++s)
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const int step = c * PF_KCH + s;
-            bw[n][s] = ldg16(wb[n] + step * 64 + g * 16);
-            bsc[n][s] = wsb[n][step];
-          }
-      } else {
-#pragma unroll
-        for (int s = 0; s < PF_KCH; ++s)
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const int step = c * PF_KCH + s;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            bw[n][s] = step < nsteps ? ldg16(wb[n] + step * 64 + g * 16) : z;
-            bsc[n][s] = step < nsteps ? wsb[n][step] : 0x7F7F7F7Fu;
-          }
-      }
+      if (tid < GU_BM) S.as[tid] = r.as;
+      S.bs[tid] = r.bs;
     };
 
-    v4f acc[4][4];
+    v4f acc[4][8];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < 8; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+    // waves whose rows or columns fall outside the tile skip the matrix work
+    const bool wact = wm * 64 < nrows && wn * 64 < ncols;
 
-    load_a(0);
-    load_b(0, bcur, scur);
-    store_a(0);
-    for (int c = 0; c < nchunks; ++c) {
-      const int buf = c & 1;
-      lds_barrier();                                            // stage c is in LDS; stage c-1 reads are done
-      if (c + 1 < nchunks) {                                    // next stage's loads stay in flight during the MFMAs
-        load_a(c + 1);
-        load_b(c + 1, bnext, snext);
-      }
+    // one MFMA step from LDS buffer s & 1; `nxt` holds stage s + 1, `fut` receives stage s + 2
+    auto step = [&](int s, Regs& nxt, Regs& fut) {
+      GuStage& S = st[s & 1];
+      lds_barrier();                                            // stage s is in LDS; stage s-1 reads are done
+      if (s + 2 < nsteps) load_stage(s + 2, fut);               // in flight during two steps of MFMAs
+      if (wact) {
+        v8i bf[8];
+        uint32_t bsv[8];
 #pragma unroll
-      for (int s = 0; s < PF_KCH; ++s) {
-        if (c * PF_KCH + s < nsteps) {
+        for (int n = 0; n < 8; ++n) {
+          const int r = (n < 4 ? 0 : 128) + wn * 64 + (n & 3) * 16 + col;
+          const u32x4 v = S.b[b_phys(r, g)];
+          bf[n] = fp4_operand(v);
+          bsv[n] = S.bs[r] >> (8 * g);
+        }
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint8_t* ap = &abuf[buf][m * 16 + col][s * KSTEP + g * 16];
-            const u32x4 alo = *reinterpret_cast<const u32x4*>(ap);
-            const u32x4 ahi = *reinterpret_cast<const u32x4*>(ap + 64);
-            const uint32_t sa = asbuf[buf][m * 16 + col][s] >> (8 * g);
-            const v8i av = fp8_operand(alo, ahi);
+        for (int m = 0; m < 4; ++m) {
+          const int r = wm * 64 + m * 16 + col;
+          const v8i af = fp8_operand(S.a[a_phys(r, g)], S.a[a_phys(r, 4 + g)]);
+          const uint32_t sa = S.as[r] >> (8 * g);
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-              acc[m][n] = mfma_fp8_fp4(av, fp4_operand(bcur[n][s]), acc[m][n], sa, scur[n][s] >> (8 * g));
-          }
+          for (int n = 0; n < 8; ++n) acc[m][n] = mfma_fp8_fp4(af, bf[n], acc[m][n], sa, bsv[n]);
         }
       }
-      if (c + 1 < nchunks) {
-        store_a(buf ^ 1);
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-#pragma unroll
-          for (int s = 0; s < PF_KCH; ++s) {
-            bcur[n][s] = bnext[n][s];
-            scur[n][s] = snext[n][s];
-          }
-      }
+      if (s + 1 < nsteps) store_stage(st[(s + 1) & 1], nxt);
+    };
+    load_stage(0, R0);
+    if (nsteps > 1) load_stage(1, R1);
+    store_stage(st[0], R0);
+    for (int s = 0; s < nsteps; s += 2) {
+      step(s, R1, R0);
+      if (s + 1 < nsteps) step(s + 1, R0, R1);
     }
 
-    // epilogue: SwiGLU + requant, block of 32 = this wavefront's columns of one row
+    // epilogue: SwiGLU + requant; one block of 32 = two 16-column subtiles of one row
     if (wact) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v0 = swiglu(acc[m][0][i], acc[m][2][i]);
-          const float v1 = swiglu(acc[m][1][i], acc[m][3][i]);
-          float mx = fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
-          mx = fmaxf(mx, __shfl_xor(mx, 1));
-          mx = fmaxf(mx, __shfl_xor(mx, 2));
-          mx = fmaxf(mx, __shfl_xor(mx, 4));
-          mx = fmaxf(mx, __shfl_xor(mx, 8));
-          const uint32_t sc = e8m0_code_for_amax(mx, 8);
-          const int row = m * 16 + 4 * g + i;
-          if (row < nrows) {
-            uint8_t* qrow = qws + (int64_t)(p0 + row) * I;
-            qrow[c0 + col] = (uint8_t)requant_e4m3(v0, sc);
-            qrow[c0 + 16 + col] = (uint8_t)requant_e4m3(v1, sc);
-            if (col == 0) qsc_ws[(int64_t)(p0 + row) * nb + c0 / 32] = (uint8_t)sc;
+        for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v0 = swiglu(acc[m][2 * blk][i], acc[m][4 + 2 * blk][i]);
+            const float v1 = swiglu(acc[m][2 * blk + 1][i], acc[m][5 + 2 * blk][i]);
+            float mx = fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
+            mx = fmaxf(mx, __shfl_xor(mx, 1));
+            mx = fmaxf(mx, __shfl_xor(mx, 2));
+            mx = fmaxf(mx, __shfl_xor(mx, 4));
+            mx = fmaxf(mx, __shfl_xor(mx, 8));
+            const uint32_t sc = e8m0_code_for_amax(mx, 8);
+            const int row = wm * 64 + m * 16 + 4 * g + i;
+            const int cb = c0 + wn * 64 + blk * 32;           // first column of the block
+            if (row < nrows && cb < I) {
+              uint8_t* qrow = qws + (int64_t)(p0 + row) * I;
+              qrow[cb + col] = (uint8_t)requant_e4m3(v0, sc);
+              qrow[cb + 16 + col] = (uint8_t)requant_e4m3(v1, sc);
+              if (col == 0) qsc_ws[(int64_t)(p0 + row) * nb + cb / 32] = (uint8_t)sc;
+            }
           }
         }
       }
@@ -676,9 +681,9 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     *variant = "ffn:gu_decode+down_decode+combine";
   } else {
     const int tiles_bound = Tk / PF_ROWS + max_active;
-    const int nct = (a.I + PF_ICOLS - 1) / PF_ICOLS;
-    const int gu_items = tiles_bound * nct, dn_items = tiles_bound * (a.H / PF_NCOLS);
-    int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
+    const int gu_items = (Tk / GU_BM + max_active) * ((a.I + GU_ICOLS - 1) / GU_ICOLS);
+    const int dn_items = tiles_bound * (a.H / PF_NCOLS);
+    int gu_grid = gu_items < cus ? gu_items : cus;             // one 4-wavefront workgroup per CU
     int dn_grid = dn_items < cus * 2 ? dn_items : cus * 2;
     gu_grid = (gu_grid + XCDS - 1) / XCDS * XCDS;
     dn_grid = (dn_grid + XCDS - 1) / XCDS * XCDS;
