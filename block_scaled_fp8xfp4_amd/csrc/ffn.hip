@@ -13,14 +13,17 @@
 // matrix cores.
 //
 // Decode path (few rows per expert, weight streaming):
-//   gu_decode_kernel    one wavefront per (expert, 16 W13 rows): the whole K
-//                       of its weight rows is loaded into registers at once;
-//                       the expert's activation rows are staged in LDS, at
-//                       most min(16, T) at a time; writes fp32 h = [gate |
-//                       up] per bucket position.
-//   down_decode_kernel  one workgroup per (expert, 64 W2 rows): W2 first,
-//                       then SwiGLU + requant of the rows' h into LDS (8
-//                       lanes per block of 32), then the down chain.
+//   gu_decode_kernel    one workgroup per (expert, block of 32 intermediate
+//                       columns) = 64 W13 rows, 16 per wavefront: the whole K
+//                       of the weight rows is loaded into registers at once,
+//                       the expert's activation rows are staged in LDS, and
+//                       the gate/up tile is turned into the requantized
+//                       intermediate block in the same workgroup.
+//   down_decode_kernel  one workgroup per (expert, 128 W2 rows); intermediate
+//                       rows from the workspace through LDS; writes o.
+//   down_combine1_kernel  one row (T = 1): one workgroup per 16 output
+//                       columns runs the down chains of all k slots and the
+//                       combine, so o never leaves the chip.
 // Prefill path (hundreds of rows per expert, matrix-core bound):
 //   gu_prefill_kernel   expert tile of up to 128 rows x 128 intermediate
 //                       columns (256 W13 rows) per workgroup, 2 x 2
@@ -41,9 +44,6 @@ namespace mx {
 constexpr int DEC_MAX_STEPS = 32;                 // decode gate/up: H <= 4096 held in registers
 constexpr int DOWN_MAX_STEPS = MAX_I / KSTEP;     // 16
 constexpr int PF_ROWS = 64;                       // prefill expert tile rows
-constexpr int PF_ICOLS = 128;                     // prefill gate/up: intermediate columns per workgroup
-constexpr int PF_KCH = 2;                         // prefill gate/up: MFMA steps per LDS stage
-constexpr int PF_AROW = PF_KCH * KSTEP + 16;      // LDS row pitch of the staged activations (padded)
 constexpr int PF_NCOLS = 256;                     // prefill down: W2 rows per workgroup
 constexpr int PF_MAX_I = 640;                     // prefill down: intermediate held in LDS (5 steps)
 constexpr int XCDS = 8;
@@ -105,6 +105,64 @@ __device__ __forceinline__ int tile_expert(const int* tile_start, int E, int til
   return lo;
 }
 
+// The expert list seen by one wavefront, from its own registers (no LDS, no
+// barrier): lane l holds offsets[l * per + i], i = 0..per (per = ceil(E / 64)).
+// A "tile" here is an expert with at least one live pair, in expert order.
+struct WaveExperts {
+  int o[17];
+  int per, cnt, incl;                             // this lane's tiles and their inclusive prefix
+};
+
+__device__ __forceinline__ void wave_experts_load(const int32_t* __restrict__ offsets, int E, WaveExperts& w) {
+  const int lane = threadIdx.x & 63;
+  w.per = (E + 63) / 64;                          // <= MAX_E / 64 = 16
+#pragma unroll
+  for (int i = 0; i < 17; ++i) {                  // branch-free: entries past per are never used
+    const int e = lane * w.per + i;
+    w.o[i] = offsets[e < E ? e : E];
+  }
+}
+
+// Count this lane's tiles and scan them over the wavefront; returns the total.
+__device__ __forceinline__ int wave_experts_scan(int E, WaveExperts& w) {
+  const int lane = threadIdx.x & 63;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < w.per && lane * w.per + i < E && w.o[i + 1] > w.o[i]) ++c;
+  w.cnt = c;
+  w.incl = c + wave_excl_scan(c, lane);
+  return __builtin_amdgcn_readlane(w.incl, 63);
+}
+
+// Tile t (< total): its expert, first bucket position and pair count.
+__device__ __forceinline__ void wave_tile(const WaveExperts& w, int E, int t, int& e, int& p0, int& cnt) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long past = __ballot(w.incl > t);
+  const int L = __builtin_ctzll(past);            // lowest lane whose tiles reach past t
+  int k = t - (w.incl - w.cnt), ei = 0, pe = 0, ce = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool live = i < w.per && lane * w.per + i < E && w.o[i + 1] > w.o[i];
+    if (live && k == 0) { ei = lane * w.per + i; pe = w.o[i]; ce = w.o[i + 1] - w.o[i]; }
+    if (live) --k;
+  }
+  e = __builtin_amdgcn_readlane(ei, L);
+  p0 = __builtin_amdgcn_readlane(pe, L);
+  cnt = __builtin_amdgcn_readlane(ce, L);
+}
+
+// The expert whose bucket holds position p (offsets[e] <= p < offsets[e + 1]), or -1.
+__device__ __forceinline__ int wave_owner(const WaveExperts& w, int E, int p) {
+  const int lane = threadIdx.x & 63;
+  int ei = -1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < w.per && lane * w.per + i < E && w.o[i] <= p && p < w.o[i + 1]) ei = lane * w.per + i;
+  const unsigned long long has = __ballot(ei >= 0);
+  return has ? __builtin_amdgcn_readlane(ei, __builtin_ctzll(has)) : -1;
+}
+
 // Logical item of a persistent block in a round: each XCD (blocks b with the
 // same b % 8) takes a contiguous range of items.  G is a multiple of 8.
 __device__ __forceinline__ int xcd_item(int round, int b, int G) {
@@ -120,209 +178,410 @@ __device__ __forceinline__ v8i fp4_operand(const u32x4& b) {
 }
 
 // =========================================================== decode path ==
-// Gate/up: one wavefront per (expert, 16 W13 rows).  It first issues the
-// loads of the whole K of its 16 weight rows (registers), then stages the
-// expert's activation rows, at most R = min(16, T) at a time, in its own LDS
-// (dynamic, R * (H + 16) + R * H / 32 bytes) and runs the chain.
-__global__ __launch_bounds__(64) void gu_decode_kernel(FfnArgs a, float* __restrict__ h, int Tk, int R) {
-  __shared__ int tile_start[MAX_E + 1];
+constexpr int DEC_ROWS = 8;                       // gate/up: activation rows per pass
+constexpr int DN_ROWS = 16;                       // down: intermediate rows per pass
+constexpr int DEC_HPITCH = 64 + 4;                // LDS pitch (floats) of one pass's gate|up tile
+constexpr int DEC_SPITCH = DEC_MAX_STEPS + 1;     // LDS pitch (dwords) of the staged weight scales
+
+// Weight loads of the decode kernels are branch-free: a step past the end of
+// K reloads the last step (never used), so a wavefront's loads issue back to
+// back.  Whatever a pass needs besides the weights (activation rows, scales)
+// is requested before the weights, so waiting for it never waits for them
+// (vector-memory counters drain in issue order).
+
+// Gate/up + SwiGLU + requant: one workgroup per (expert, block of 32
+// intermediate columns), i.e. 64 W13 rows: wavefronts 0, 1 take gate rows
+// 32 b + [0, 16) and + [16, 32), wavefronts 2, 3 the matching up rows.  Per
+// pass of at most R = min(8, T) rows of the expert, the activation rows are
+// gathered into LDS; each wavefront's 16 weight rows (whole K, NS >= H / 128
+// steps) stay in registers for all passes and their block scales are staged
+// in LDS (16 rows x H / 32 bytes, one coalesced span).  The four 16 x 16
+// results meet in LDS, where one pass turns each row's 32 gate/up pairs into
+// one requantized block.  Writes q, its scale, and the fp32 h = [gate | up]
+// of every pair.  ONE (T = 1): every pair is row 0, whose activations are
+// requested before the route is read.
+template <int NS, bool ONE>
+__global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* __restrict__ qws,
+                                                           uint8_t* __restrict__ qsc_ws, float* __restrict__ h,
+                                                           int Tk, int R) {
+  __shared__ int tok[DEC_ROWS];
+  __shared__ float hb[16 * DEC_HPITCH];
+  __shared__ uint32_t bsc[4][16 * DEC_SPITCH];                 // per wavefront: [row][step] scale dwords
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
-  build_tiles(a.offsets, a.E, 0, tile_start);
-  const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
-  const int H = a.H, twoI = 2 * a.I;
-  const int nsteps = H / KSTEP;
-  const int pitch = H + 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int H = a.H, I = a.I, nb = I / 32;
+  const int nsteps = H / KSTEP, chunks = H / 16;
+  const int pitch = H + 16, spitch = nsteps | 1;              // odd dword pitch: the 16 rows hit 16 banks
   uint8_t* xlds = dyn_lds;                                      // [R][H + 16]
   uint32_t* xslds = reinterpret_cast<uint32_t*>(dyn_lds + (size_t)R * pitch);   // [R][nsteps]
-  const int ntiles = twoI / 16;
-  const int nitems = tile_start[a.E] * ntiles;
+  u32x4 xv[DEC_ROWS];
+  uint32_t xsv = 0x7F7F7F7Fu;
+  if (ONE) {
+    xv[0] = tid < chunks ? ldg16(a.x + tid * 16) : u32x4{0u, 0u, 0u, 0u};
+    if (tid < nsteps) xsv = reinterpret_cast<const uint32_t*>(a.x_sc)[tid];
+  }
+  WaveExperts we;                                               // every wavefront reads the expert list itself
+  wave_experts_load(a.offsets, a.E, we);
+  const int nitems = wave_experts_scan(a.E, we) * nb;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int e = tile_expert(tile_start, a.E, item / ntiles), nt = item % ntiles;
-    const int p0 = a.offsets[e];
-    int cnt = a.offsets[e + 1] - p0;
+    const int blk = item % nb;
+    int e, p0, cnt;
+    wave_tile(we, a.E, item / nb, e, p0, cnt);
     if (p0 < 0 || p0 + cnt > Tk) cnt = 0;                       // malformed route: skip
-    const int64_t wrow = (int64_t)e * twoI + nt * 16 + col;     // B column of this lane
-    const uint8_t* wp = a.w13 + wrow * (H / 2);
-    const uint32_t* wsp = reinterpret_cast<const uint32_t*>(a.w13_sc + wrow * (H / 32));
-    // every weight load of the 16 rows is issued before anything waits on one;
-    // scale dwords stay raw (the lane's byte is picked at the MFMA)
-    u32x4 bw[DEC_MAX_STEPS];
-    uint32_t bsr[DEC_MAX_STEPS];
-#pragma unroll
-    for (int c = 0; c < DEC_MAX_STEPS / 8; ++c) {
-      if (c * 8 + 8 <= nsteps) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          bw[c * 8 + m] = ldg16(wp + (c * 8 + m) * 64 + g * 16);
-          bsr[c * 8 + m] = wsp[c * 8 + m];
-        }
-      } else if (c * 8 < nsteps) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-          if (c * 8 + m < nsteps) {
-            bw[c * 8 + m] = ldg16(wp + (c * 8 + m) * 64 + g * 16);
-            bsr[c * 8 + m] = wsp[c * 8 + m];
-          }
+    const int n0 = min(R, cnt);
+    lds_barrier();                                              // the previous item's LDS reads are done
+    if (!ONE) {
+      if (tid < n0) {
+        const int pr = a.perm[p0 + tid];
+        tok[tid] = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
       }
+      lds_barrier();
+      // first pass's rows: requested before the weights
+#pragma unroll
+      for (int r = 0; r < DEC_ROWS; ++r) {
+        const int t = r < n0 ? tok[r] : -1;
+        xv[r] = (t >= 0 && tid < chunks) ? ldg16(a.x + (int64_t)t * H + tid * 16) : u32x4{0u, 0u, 0u, 0u};
+      }
+      {
+        const int r = tid / nsteps, s = tid % nsteps;
+        const int t = (tid < n0 * nsteps) ? tok[r] : -1;
+        xsv = t >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)t * (H / 32))[s] : 0x7F7F7F7Fu;
+      }
+    }
+    // this wavefront's 16 rows of scales: one contiguous span of 16 * nsteps dwords
+    const int64_t wrow0 = (int64_t)e * 2 * I + (wave < 2 ? 0 : I) + blk * 32 + (wave & 1) * 16;
+    const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.w13_sc + wrow0 * (H / 32));
+    uint32_t bsv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = lane + 64 * i;
+      bsv[i] = idx < 16 * nsteps ? ssrc[idx] : 0u;
+    }
+    const uint8_t* wp = a.w13 + (wrow0 + col) * (H / 2) + g * 16;
+    u32x4 bw[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (s < nsteps ? s : nsteps - 1) * 64);
+    // stage what the first pass needs (its loads were issued before the weights)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = lane + 64 * i;
+      if (idx < 16 * nsteps) bsc[wave][(idx / nsteps) * spitch + idx % nsteps] = bsv[i];
+    }
+    if (ONE) {
+      if (tid < chunks) *reinterpret_cast<u32x4*>(xlds + tid * 16) = xv[0];
+      if (tid < nsteps) xslds[tid] = xsv;
+    } else {
+#pragma unroll
+      for (int r = 0; r < DEC_ROWS; ++r)
+        if (r < n0 && tid < chunks) *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + tid * 16) = xv[r];
+      if (tid < n0 * nsteps) xslds[tid] = xsv;
+    }
+    lds_barrier();
+    const uint32_t* bsrow = &bsc[wave][col * spitch];
+    // One pass over rows [r0, r0 + nrows) whose activations are in LDS.  Every
+    // LDS read is unconditional: lanes of rows past nrows read row 0 again and
+    // their output rows are discarded (rows of the matrix product are
+    // independent), so nothing here waits behind a branch.
+    auto run_pass = [&](int r0, int nrows) {
+      const int ar = col < nrows ? col : 0;
+      const uint8_t* arow = xlds + (size_t)ar * pitch + g * 16;
+      const uint32_t* asrow = xslds + ar * nsteps;
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s < nsteps) {
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(arow + s * KSTEP);
+          const u32x4 ahi = *reinterpret_cast<const u32x4*>(arow + s * KSTEP + 64);
+          // byte g of the row's scale dword is block 4 s + g; the matrix core
+          // reads only the low byte of the scale operand
+          const uint32_t sb = bsrow[s] >> (8 * g);
+          const uint32_t sa = asrow[s] >> (8 * g);
+          acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, sa, sb);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hb[(4 * g + i) * DEC_HPITCH + wave * 16 + col] = acc[i];
+      lds_barrier();
+      // SwiGLU + requant: 16 lanes per row, two intermediate columns each (rows < R <= 8)
+      if (tid < DEC_ROWS * 16) {
+        const int r = tid >> 4, c = 2 * (tid & 15);
+        const float2 gg = *reinterpret_cast<const float2*>(&hb[r * DEC_HPITCH + c]);
+        const float2 uu = *reinterpret_cast<const float2*>(&hb[r * DEC_HPITCH + 32 + c]);
+        const float v0 = swiglu(gg.x, uu.x), v1 = swiglu(gg.y, uu.y);
+        float m = fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        m = fmaxf(m, __shfl_xor(m, 8));
+        if (r < nrows) {
+          const int64_t p = p0 + r0 + r;
+          const uint32_t sc = e8m0_code_for_amax(m, 8);
+          const uint32_t d = requant_e4m3(v0, sc) | (requant_e4m3(v1, sc) << 8);
+          *reinterpret_cast<uint16_t*>(qws + p * I + blk * 32 + c) = (uint16_t)d;
+          if ((tid & 15) == 0) qsc_ws[p * nb + blk] = (uint8_t)sc;
+          *reinterpret_cast<float2*>(h + p * 2 * I + blk * 32 + c) = gg;
+          *reinterpret_cast<float2*>(h + p * 2 * I + I + blk * 32 + c) = uu;
+        }
+      }
+    };
+    if (ONE) {
+      if (cnt > 0) run_pass(0, 1);                              // T = 1: at most one pair per expert
+      continue;
     }
     for (int r0 = 0; r0 < cnt; r0 += R) {
       const int nrows = min(R, cnt - r0);
-      // token of staged row `lane` (lanes < nrows), read once
-      int my_tok = -1;
-      if (lane < nrows) {
-        const int pr = a.perm[p0 + r0 + lane];
-        my_tok = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
+      if (r0 > 0) {                                             // later passes: gather their rows
+        lds_barrier();
+        if (tid < nrows) {
+          const int pr = a.perm[p0 + r0 + tid];
+          tok[tid] = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int r = 0; r < DEC_ROWS; ++r) {
+          const int t = r < nrows ? tok[r] : -1;
+          xv[r] = (t >= 0 && tid < chunks) ? ldg16(a.x + (int64_t)t * H + tid * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+        const int rs = tid / nsteps, ss = tid % nsteps;
+        const int ts = (tid < nrows * nsteps) ? tok[rs] : -1;
+        xsv = ts >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)ts * (H / 32))[ss] : 0x7F7F7F7Fu;
+#pragma unroll
+        for (int r = 0; r < DEC_ROWS; ++r)
+          if (r < nrows && tid < chunks) *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + tid * 16) = xv[r];
+        if (tid < nrows * nsteps) xslds[tid] = xsv;
+        lds_barrier();
       }
-      lds_barrier();                                            // previous rows' LDS reads are done
-      for (int r = 0; r < nrows; ++r) {
-        const int tok = __shfl(my_tok, r);
-        const uint8_t* src = a.x + (int64_t)(tok < 0 ? 0 : tok) * H;
-        uint8_t* dst = xlds + (size_t)r * pitch;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        u32x4 v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int off = (j * 64 + lane) * 16;
-          v[j] = (tok >= 0 && off < H) ? ldg16(src + off) : z;
-        }
-        const int sidx = lane;
-        const uint32_t sv = (tok >= 0 && sidx < nsteps)
-                                ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)tok * (H / 32))[sidx]
-                                : 0x7F7F7F7Fu;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int off = (j * 64 + lane) * 16;
-          if (off < H) *reinterpret_cast<u32x4*>(dst + off) = v[j];
-        }
-        if (sidx < nsteps) xslds[r * nsteps + sidx] = sv;
-      }
-      lds_barrier();
-      for (int rt = 0; rt < nrows; rt += 16) {
-        const int rr = rt + col;                                // staged row of this lane
-        const bool rv = rr < nrows;
-        const uint8_t* arow = xlds + (size_t)(rv ? rr : 0) * pitch;
-        const uint32_t* asrow = xslds + (rv ? rr : 0) * nsteps;
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < DEC_MAX_STEPS; ++s) {
-          if (s < nsteps) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 alo = rv ? *reinterpret_cast<const u32x4*>(arow + s * KSTEP + g * 16) : z;
-            const u32x4 ahi = rv ? *reinterpret_cast<const u32x4*>(arow + s * KSTEP + 64 + g * 16) : z;
-            const uint32_t sb = bsr[s] >> (8 * g);
-            const uint32_t sa = rv ? (asrow[s] >> (8 * g)) : sb;
-            acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, sa, sb);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = rt + 4 * g + i;
-          if (row < nrows) h[(int64_t)(p0 + r0 + row) * twoI + nt * 16 + col] = acc[i];
-        }
-      }
+      run_pass(r0, nrows);
     }
   }
 }
 
-// SwiGLU + requant of pair rows [p0, p0 + n) (n <= 16) from h into LDS, and
-// into the workspace when `publish`.  Block-wide; 8 consecutive lanes share
-// a block of 32 intermediate values (4 each), the block maximum is a
-// butterfly over those 8 lanes.
-__device__ void stage_intermediate(const float* __restrict__ h, int p0, int n, int I, uint8_t (*qlds)[MAX_I + 16],
-                                   uint8_t (*slds)[MAX_I / 32], uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws,
-                                   bool publish) {
-  const int q4 = I / 4, nb = I / 32;
-  const int total = 16 * q4;                                     // multiple of 128
-  for (int base = 0; base < total; base += blockDim.x) {
-    const int idx = base + (int)threadIdx.x;
-    const int r = idx / q4, c4 = idx % q4;
-    const bool in = idx < total && r < n;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (in) {
-      const float* hp = h + (int64_t)(p0 + r) * 2 * I + 4 * c4;
-      const float4 gg = *reinterpret_cast<const float4*>(hp);
-      const float4 uu = *reinterpret_cast<const float4*>(hp + I);
-      v[0] = swiglu(gg.x, uu.x);
-      v[1] = swiglu(gg.y, uu.y);
-      v[2] = swiglu(gg.z, uu.z);
-      v[3] = swiglu(gg.w, uu.w);
-    }
-    float m = fmaxf(fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])), fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    if (in) {
-      const uint32_t sc = e8m0_code_for_amax(m, 8);
-      const uint32_t d = requant_e4m3(v[0], sc) | (requant_e4m3(v[1], sc) << 8) | (requant_e4m3(v[2], sc) << 16) |
-                         (requant_e4m3(v[3], sc) << 24);
-      *reinterpret_cast<uint32_t*>(&qlds[r][4 * c4]) = d;
-      if ((c4 & 7) == 0) slds[r][c4 >> 3] = (uint8_t)sc;
-      if (publish) {
-        *reinterpret_cast<uint32_t*>(qws + (int64_t)(p0 + r) * I + 4 * c4) = d;
-        if ((c4 & 7) == 0) qsc_ws[(int64_t)(p0 + r) * nb + (c4 >> 3)] = (uint8_t)sc;
-      }
-    }
+// W2 operand of one 16-row tile for NS steps, branch-free: lane (col, g)
+// takes block 4 s + g of its row; blocks past I / 32 load the row's first
+// bytes (in bounds) and are zeroed where the MFMA consumes them.
+template <int NS>
+__device__ __forceinline__ void load_w2_tile(const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2_sc,
+                                             int64_t row, int I, int g, u32x4 (&bw)[NS], uint32_t (&bs)[NS]) {
+  const int nb = I / 32;
+  const uint8_t* wp = w2 + row * (I / 2);
+  const uint8_t* wsp = w2_sc + row * nb;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const bool bv = 4 * s + g < nb;
+    bw[s] = ldg16(wp + (bv ? s * 64 + g * 16 : 0));
+    bs[s] = wsp[bv ? 4 * s + g : 0];
   }
 }
 
-__global__ __launch_bounds__(256) void down_decode_kernel(FfnArgs a, const float* __restrict__ h,
-                                                          uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws,
-                                                          float* __restrict__ o, int Tk) {
-  __shared__ int tile_start[MAX_E + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t qlds[16][MAX_I + 16];   // padded rows: fewer bank conflicts
-  __shared__ uint8_t slds[16][MAX_I / 32];
-  build_tiles(a.offsets, a.E, 0, tile_start);
+__device__ __forceinline__ v8i fp4_operand_masked(const u32x4& b, bool valid) {
+  return valid ? v8i{(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0} : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+// Stage intermediate rows [p, p + nrows) (nrows <= DN_ROWS) of the workspace in LDS.
+__device__ void stage_q_rows(const uint8_t* __restrict__ qws, const uint8_t* __restrict__ qsc_ws, int64_t p, int nrows,
+                             int I, uint8_t (*qlds)[MAX_I + 16], uint8_t (*slds)[MAX_I / 32]) {
+  const int q16 = I / 16, nb = I / 32;
+  for (int idx = threadIdx.x; idx < DN_ROWS * q16; idx += blockDim.x) {
+    const int r = idx / q16, c16 = idx % q16;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&qlds[r][c16 * 16]) = r < nrows ? ldg16(qws + (p + r) * I + c16 * 16) : z;
+  }
+  for (int idx = threadIdx.x; idx < DN_ROWS * nb; idx += blockDim.x) {
+    const int r = idx / nb, b = idx % nb;
+    slds[r][b] = r < nrows ? qsc_ws[(p + r) * nb + b] : (uint8_t)127;
+  }
+}
+
+// Down: one workgroup per (expert, 128 W2 rows), 32 rows (two 16-row tiles)
+// per wavefront.  W2 first (NS >= I / 128 steps in registers), then the
+// expert's intermediate rows, 16 per pass, from the workspace into LDS;
+// writes o.
+template <int NS>
+__global__ __launch_bounds__(256, 2) void down_decode_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
+                                                             const uint8_t* __restrict__ qsc_ws,
+                                                             float* __restrict__ o, int Tk) {
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[DN_ROWS][MAX_I + 16];
+  __shared__ uint8_t slds[DN_ROWS][MAX_I / 32];
+  WaveExperts we;
+  wave_experts_load(a.offsets, a.E, we);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int H = a.H, I = a.I, nb = I / 32;
   const int nsteps = (I + KSTEP - 1) / KSTEP;
-  const int ntiles = H / 64;
-  const int nitems = tile_start[a.E] * ntiles;
+  const int ntiles = H / 128;
+  const int nitems = wave_experts_scan(a.E, we) * ntiles;
+  // K past I reads zeros: the row tails are cleared once, staging never writes them
+  for (int idx = threadIdx.x; idx < DN_ROWS * (NS * KSTEP - I); idx += blockDim.x)
+    qlds[idx / (NS * KSTEP - I)][I + idx % (NS * KSTEP - I)] = 0;
+  for (int idx = threadIdx.x; idx < DN_ROWS * (NS * 4 - nb); idx += blockDim.x)
+    slds[idx / (NS * 4 - nb)][nb + idx % (NS * 4 - nb)] = 127;
 
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int e = tile_expert(tile_start, a.E, item / ntiles), tile = item % ntiles;
-    const int p0 = a.offsets[e];
-    int cnt = a.offsets[e + 1] - p0;
+    const int tile = item % ntiles;
+    int e, p0, cnt;
+    wave_tile(we, a.E, item / ntiles, e, p0, cnt);
     if (p0 < 0 || p0 + cnt > Tk) cnt = 0;
-    const int n = tile * 64 + wave * 16 + col;                  // W2 row = output column of this lane
-    const uint8_t* wp = a.w2 + ((int64_t)e * H + n) * (I / 2);
-    const uint8_t* wsp = a.w2_sc + ((int64_t)e * H + n) * nb;
-    u32x4 bw[DOWN_MAX_STEPS];
-    uint32_t bs[DOWN_MAX_STEPS];
+    const int n0 = tile * 128 + wave * 32;                      // first W2 row of this wavefront
+    u32x4 bw[2][NS];
+    uint32_t bs[2][NS];
 #pragma unroll
-    for (int s = 0; s < DOWN_MAX_STEPS; ++s) {
-      if (s < nsteps) {
-        const bool bv = 4 * s + g < nb;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        bw[s] = bv ? ldg16(wp + s * 64 + g * 16) : z;
-        bs[s] = wsp[bv ? 4 * s + g : 0];
-      }
-    }
-    for (int rt = 0; rt * 16 < cnt; ++rt) {
-      const int nrows = min(16, cnt - rt * 16);
-      stage_intermediate(h, p0 + rt * 16, nrows, I, qlds, slds, qws, qsc_ws, tile == 0);
+    for (int n = 0; n < 2; ++n) load_w2_tile<NS>(a.w2, a.w2_sc, (int64_t)e * H + n0 + n * 16 + col, I, g, bw[n], bs[n]);
+    for (int r0 = 0; r0 < cnt; r0 += DN_ROWS) {
+      const int nrows = min(DN_ROWS, cnt - r0);
+      lds_barrier();                                            // the previous pass's LDS reads are done
+      stage_q_rows(qws, qsc_ws, p0 + r0, nrows, I, qlds, slds);
       lds_barrier();
-      const bool rv = col < nrows;
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int s = 0; s < DOWN_MAX_STEPS; ++s) {
+      for (int s = 0; s < NS; ++s) {
         if (s < nsteps) {
-          const int klo = s * KSTEP + g * 16, khi = klo + 64;
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 alo = (rv && klo < I) ? *reinterpret_cast<const u32x4*>(&qlds[col][klo]) : z;
-          const u32x4 ahi = (rv && khi < I) ? *reinterpret_cast<const u32x4*>(&qlds[col][khi]) : z;
-          const uint32_t sa = (rv && 4 * s + g < nb) ? (uint32_t)slds[col][4 * s + g] : bs[s];
-          acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, sa, bs[s]);
+          const int klo = s * KSTEP + g * 16;
+          const bool bv = 4 * s + g < nb;
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(&qlds[col][klo]);
+          const u32x4 ahi = *reinterpret_cast<const u32x4*>(&qlds[col][klo + 64]);
+          const uint32_t sa = slds[col][4 * s + g];
+          const v8i av = fp8_operand(alo, ahi);
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc[n] = mfma_fp8_fp4(av, fp4_operand_masked(bw[n][s], bv), acc[n], sa, bs[n][s]);
         }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * g + i;
-        if (row < nrows) o[(int64_t)(p0 + rt * 16 + row) * H + n] = acc[i];
+        if (row < nrows) {
+          float* orow = o + (int64_t)(p0 + r0 + row) * H + n0 + col;
+          orow[0] = acc[0][i];
+          orow[16] = acc[1][i];
+        }
       }
-      lds_barrier();
     }
+  }
+}
+
+// Single-row decode (T = 1: every touched expert holds exactly one pair, and
+// pair p belongs to the p-th touched expert): down and combine in one kernel.
+// One workgroup per 16 output columns.  The k intermediate rows are gathered
+// into LDS (requested first), wavefront w runs the down chains of slots w and
+// w + 4 (then w + 8 and w + 12 when k > 8) with their W2 rows in registers,
+// and the 16 columns are combined in slot order exactly as the combine
+// kernel does.
+template <int NS>
+__global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
+                                                               const uint8_t* __restrict__ qsc_ws, int Tk) {
+  constexpr int QP = NS * KSTEP + 16;                           // LDS pitch of an intermediate row
+  constexpr int QPT = (MAX_K * NS * 8 + 255) / 256;             // 16-byte chunks per thread
+  __shared__ int pslot[MAX_K];
+  __shared__ float wslot[MAX_K];
+  __shared__ float olds[MAX_K][16];
+  __shared__ __attribute__((aligned(16))) uint8_t q1[MAX_K][QP];
+  __shared__ uint8_t s1[MAX_K][NS * 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int H = a.H, I = a.I, nb = I / 32, k = a.k;
+  const int nsteps = (I + KSTEP - 1) / KSTEP;
+  const int n = blockIdx.x * 16 + col;                         // output column of this lane
+  int my_p = -1;
+  float my_w = 0.f;
+  if (tid < k) {                                                // in flight with the offsets
+    my_p = a.slot_pos[tid];
+    my_w = a.topk_w[tid];
+  }
+  WaveExperts we;
+  wave_experts_load(a.offsets, a.E, we);
+  if (tid < k) {
+    pslot[tid] = my_p;
+    wslot[tid] = my_w;
+  }
+  lds_barrier();
+  for (int idx = tid; idx < MAX_K * (NS * KSTEP - I); idx += 256)   // K past I reads zeros
+    q1[idx / (NS * KSTEP - I)][I + idx % (NS * KSTEP - I)] = 0;
+  for (int idx = tid; idx < MAX_K * (NS * 4 - nb); idx += 256)
+    s1[idx / (NS * 4 - nb)][nb + idx % (NS * 4 - nb)] = 127;
+  auto slot_ok = [&](int j) {
+    const int p = j < k ? pslot[j] : -1;
+    return p >= 0 && p < Tk;
+  };
+  // the k intermediate rows and their scales, requested before any weight
+  const int q16 = I / 16;
+  u32x4 qv[QPT];
+  uint32_t sv[4];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i, j = idx / q16, c = idx % q16;
+    const bool v = j < k && slot_ok(j);
+    qv[i] = v ? ldg16(qws + (int64_t)pslot[j] * I + c * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i, j = idx / nb, b = idx % nb;
+    sv[i] = (j < k && slot_ok(j)) ? (uint32_t)qsc_ws[(int64_t)pslot[j] * nb + b] : 127u;
+  }
+  auto load_pair = [&](int j0, bool (&ok)[2], u32x4 (&bw)[2][NS], uint32_t (&bs)[2][NS]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = j0 + 4 * u;
+      const int e = slot_ok(j) ? wave_owner(we, a.E, pslot[j]) : -1;
+      ok[u] = e >= 0;
+      load_w2_tile<NS>(a.w2, a.w2_sc, (int64_t)(ok[u] ? e : 0) * H + n, I, g, bw[u], bs[u]);
+    }
+  };
+  auto run_pair = [&](int j0, const bool (&ok)[2], const u32x4 (&bw)[2][NS], const uint32_t (&bs)[2][NS]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = j0 + 4 * u;
+      if (j >= k) continue;                                     // wavefront-uniform
+      if (!ok[u]) {
+        if (g == 0) olds[j][col] = 0.f;
+        continue;
+      }
+      // every row of the A tile is the slot's one activation row (rows are
+      // independent; row 0 is kept)
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s < nsteps) {
+          const int klo = s * KSTEP + g * 16;
+          const bool bv = 4 * s + g < nb;
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(&q1[j][klo]);
+          const u32x4 ahi = *reinterpret_cast<const u32x4*>(&q1[j][klo + 64]);
+          const uint32_t sa = s1[j][4 * s + g];
+          acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand_masked(bw[u][s], bv), acc, sa, bs[u][s]);
+        }
+      }
+      if (g == 0) olds[j][col] = acc[0];                        // row 0 of the tile
+    }
+  };
+  bool okA[2];
+  u32x4 bwA[2][NS];
+  uint32_t bsA[2][NS];
+  load_pair(wave, okA, bwA, bsA);
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i, j = idx / q16, c = idx % q16;
+    if (j < k) *reinterpret_cast<u32x4*>(&q1[j][c * 16]) = qv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i, j = idx / nb, b = idx % nb;
+    if (j < k) s1[j][b] = (uint8_t)sv[i];
+  }
+  lds_barrier();
+  run_pair(wave, okA, bwA, bsA);
+  if (k > 8) {
+    load_pair(wave + 8, okA, bwA, bsA);
+    run_pair(wave + 8, okA, bwA, bsA);
+  }
+  lds_barrier();
+  if (tid < 16) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int pj = pslot[j];
+      if (pj < 0 || pj >= Tk) continue;
+      acc = fmaf(wslot[j], olds[j][tid], acc);
+    }
+    a.y[blockIdx.x * 16 + tid] = acc;
   }
 }
 
@@ -670,14 +929,38 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     path = ((Tk <= DECODE_MAX_PAIRS && dec_ok) || !pre_ok) ? 1 : 2;
   }
   if (path == 1) {
-    const int R = a.T < 16 ? a.T : 16;                          // rows of one expert never exceed T
+    const int R = a.T < DEC_ROWS ? a.T : DEC_ROWS;               // rows of one expert never exceed T
     const size_t lds = (size_t)R * (a.H + 16) + (size_t)R * (a.H / KSTEP) * 4;
-    const int gu_items = max_active * (2 * a.I / 16);
-    const int dn_items = max_active * (a.H / 64);
-    const int gu_grid = gu_items < cus * 8 ? gu_items : cus * 8;
-    const int dn_grid = dn_items < cus * 4 ? dn_items : cus * 4;
-    hipLaunchKernelGGL(gu_decode_kernel, dim3(gu_grid), dim3(64), lds, stream, a, h, Tk, R);
-    hipLaunchKernelGGL(down_decode_kernel, dim3(dn_grid), dim3(256), 0, stream, a, h, qws, qsc, o, Tk);
+    const int gu_items = max_active * (a.I / 32);
+    const int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
+    const int hs = a.H / KSTEP, is = (a.I + KSTEP - 1) / KSTEP;
+    const dim3 g0(gu_grid), b0(256);
+    if (a.T == 1) {
+      if (hs <= 4) hipLaunchKernelGGL((gu_decode_kernel<4, true>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+      else if (hs <= 8) hipLaunchKernelGGL((gu_decode_kernel<8, true>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+      else if (hs <= 16) hipLaunchKernelGGL((gu_decode_kernel<16, true>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+      else hipLaunchKernelGGL((gu_decode_kernel<32, true>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+    } else {
+      if (hs <= 4) hipLaunchKernelGGL((gu_decode_kernel<4, false>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+      else if (hs <= 8) hipLaunchKernelGGL((gu_decode_kernel<8, false>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+      else if (hs <= 16) hipLaunchKernelGGL((gu_decode_kernel<16, false>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+      else hipLaunchKernelGGL((gu_decode_kernel<32, false>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+    }
+    if (a.T == 1) {
+      const dim3 g1(a.H / 16), b1(256);
+      if (is <= 2) hipLaunchKernelGGL(down_combine1_kernel<2>, g1, b1, 0, stream, a, qws, qsc, Tk);
+      else if (is <= 5) hipLaunchKernelGGL(down_combine1_kernel<5>, g1, b1, 0, stream, a, qws, qsc, Tk);
+      else if (is <= 8) hipLaunchKernelGGL(down_combine1_kernel<8>, g1, b1, 0, stream, a, qws, qsc, Tk);
+      else hipLaunchKernelGGL(down_combine1_kernel<16>, g1, b1, 0, stream, a, qws, qsc, Tk);
+      *variant = "ffn:gu_decode+down_combine1";
+      return hipGetLastError();
+    }
+    const int dn_items = max_active * (a.H / 128);
+    const dim3 g2(dn_items < cus * 2 ? dn_items : cus * 2), b2(256);
+    if (is <= 2) hipLaunchKernelGGL(down_decode_kernel<2>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
+    else if (is <= 5) hipLaunchKernelGGL(down_decode_kernel<5>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
+    else if (is <= 8) hipLaunchKernelGGL(down_decode_kernel<8>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
+    else hipLaunchKernelGGL(down_decode_kernel<16>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
     *variant = "ffn:gu_decode+down_decode+combine";
   } else {
     const int tiles_bound = Tk / PF_ROWS + max_active;
