@@ -72,6 +72,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to exceed 1.5 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay one HIP graph per step instead of eager launches")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode "
@@ -142,27 +143,56 @@ def main():
             g, gs = gcopies[i % R]
             mxmoe.fp8_block_gemm(aq, asc, g, gs, yg, mxmoe.MX_OUT_BF16)
 
+        route(logits, surv)
+        ffn(xq, xsc, route, *copies[0])
+        ffn_variant = mxmoe.last_variant()
+        step(0)
+        torch.cuda.synchronize()
+        if not args.graph:
+            run_step = step
+        else:
+            # one HIP graph per step (and weight copy), as a serving loop
+            # replays its decode step; the library allocates and syncs nothing
+            graphs = []
+            for i in range(R):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    step(i)
+                graphs.append(gr)
+            torch.cuda.synchronize()
+            run_step = lambda i: graphs[i % R].replay()
         for i in range(args.warmup):
-            step(i)
+            run_step(i)
         torch.cuda.synchronize()
-        # per-call events on the launch stream bracket the FFN call of every step
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         t_start.record()
         for i in range(args.steps):
-            w13q, w13s, w2q, w2s = copies[i % R]
-            route(logits, surv)
-            ev[i][0].record()
-            ffn(xq, xsc, route, w13q, w13s, w2q, w2s)
-            ev[i][1].record()
-            ffn_variant = mxmoe.last_variant()
-            g, gs = gcopies[i % R]
-            mxmoe.fp8_block_gemm(aq, asc, g, gs, yg, mxmoe.MX_OUT_BF16)
+            run_step(i)
         t_end.record()
         torch.cuda.synchronize()
         total_ms = t_start.elapsed_time(t_end)
-        ffn_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+        # the FFN call alone: R back-to-back calls over the weight copies (one
+        # graph, or eager), bracketed by events on the launch stream
+        def ffn_calls():
+            for i in range(R):
+                ffn(xq, xsc, route, *copies[i % R])
+        if not args.graph:
+            run_ffn = ffn_calls
+        else:
+            gffn = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gffn):
+                ffn_calls()
+            run_ffn = gffn.replay
+        run_ffn()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // R)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(reps):
+            run_ffn()
+        f1.record()
+        torch.cuda.synchronize()
+        ffn_ms = f0.elapsed_time(f1) / (reps * R)
         ms = total_ms / args.steps
         ffn_bytes = touched * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * H * 4
         achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
@@ -179,7 +209,8 @@ def main():
             "config": {"workload": f"{cfg.name} MoE layer step: T={T}, H={H}, E={E}, top-{k}, I={I}, MXFP4 experts, "
                                    f"FP8 block-32 activations, + dense FP8 block-32 projection M={T}, K=N=4096",
                        "rows": T, "hidden": H, "experts": E, "top_k": k, "intermediate": I,
-                       "touched_experts": touched, "bytes_per_step": step_bytes, "weight_copies": R},
+                       "touched_experts": touched, "bytes_per_step": step_bytes, "weight_copies": R,
+                       "launch": "hip_graph_per_step" if args.graph else "eager"},
         })
         return inp, touched
 

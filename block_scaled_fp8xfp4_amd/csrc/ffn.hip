@@ -199,8 +199,9 @@ constexpr int DEC_SPITCH = DEC_MAX_STEPS + 1;     // LDS pitch (dwords) of the s
 // results meet in LDS, where one pass turns each row's 32 gate/up pairs into
 // one requantized block.  Writes q, its scale, and the fp32 h = [gate | up]
 // of every pair.  ONE (T = 1): every pair is row 0, whose activations are
-// requested before the route is read.
-template <int NS, bool ONE>
+// requested before the route is read.  EXACT: H = 128 NS, so every address
+// offset is a constant.
+template <int NS, bool EXACT, bool ONE>
 __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* __restrict__ qws,
                                                            uint8_t* __restrict__ qsc_ws, float* __restrict__ h,
                                                            int Tk, int R) {
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
-  const int H = a.H, I = a.I, nb = I / 32;
+  const int H = EXACT ? NS * KSTEP : a.H, I = a.I, nb = I / 32;
   const int nsteps = H / KSTEP, chunks = H / 16;
   const int pitch = H + 16, spitch = nsteps | 1;              // odd dword pitch: the 16 rows hit 16 banks
   uint8_t* xlds = dyn_lds;                                      // [R][H + 16]
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
     const uint8_t* wp = a.w13 + (wrow0 + col) * (H / 2) + g * 16;
     u32x4 bw[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (s < nsteps ? s : nsteps - 1) * 64);
+    for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (EXACT || s < nsteps ? s : nsteps - 1) * 64);
     // stage what the first pass needs (its loads were issued before the weights)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -935,17 +936,25 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     const int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
     const int hs = a.H / KSTEP, is = (a.I + KSTEP - 1) / KSTEP;
     const dim3 g0(gu_grid), b0(256);
+#define MX_GU(NS_, EX_, ONE_) hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, ONE_>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R)
     if (a.T == 1) {
-      if (hs <= 4) hipLaunchKernelGGL((gu_decode_kernel<4, true>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
-      else if (hs <= 8) hipLaunchKernelGGL((gu_decode_kernel<8, true>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
-      else if (hs <= 16) hipLaunchKernelGGL((gu_decode_kernel<16, true>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
-      else hipLaunchKernelGGL((gu_decode_kernel<32, true>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+      if (hs == 32) MX_GU(32, true, true);
+      else if (hs == 16) MX_GU(16, true, true);
+      else if (hs == 8) MX_GU(8, true, true);
+      else if (hs <= 4) MX_GU(4, false, true);
+      else if (hs <= 8) MX_GU(8, false, true);
+      else if (hs <= 16) MX_GU(16, false, true);
+      else MX_GU(32, false, true);
     } else {
-      if (hs <= 4) hipLaunchKernelGGL((gu_decode_kernel<4, false>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
-      else if (hs <= 8) hipLaunchKernelGGL((gu_decode_kernel<8, false>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
-      else if (hs <= 16) hipLaunchKernelGGL((gu_decode_kernel<16, false>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
-      else hipLaunchKernelGGL((gu_decode_kernel<32, false>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R);
+      if (hs == 32) MX_GU(32, true, false);
+      else if (hs == 16) MX_GU(16, true, false);
+      else if (hs == 8) MX_GU(8, true, false);
+      else if (hs <= 4) MX_GU(4, false, false);
+      else if (hs <= 8) MX_GU(8, false, false);
+      else if (hs <= 16) MX_GU(16, false, false);
+      else MX_GU(32, false, false);
     }
+#undef MX_GU
     if (a.T == 1) {
       const dim3 g1(a.H / 16), b1(256);
       if (is <= 2) hipLaunchKernelGGL(down_combine1_kernel<2>, g1, b1, 0, stream, a, qws, qsc, Tk);
