@@ -310,11 +310,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
         const float2 gg = *reinterpret_cast<const float2*>(&hb[r * DEC_HPITCH + c]);
         const float2 uu = *reinterpret_cast<const float2*>(&hb[r * DEC_HPITCH + 32 + c]);
         const float v0 = swiglu(gg.x, uu.x), v1 = swiglu(gg.y, uu.y);
-        float m = fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
-        m = fmaxf(m, __shfl_xor(m, 4));
-        m = fmaxf(m, __shfl_xor(m, 8));
+        const float m = row16_max(fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
         if (r < nrows) {
           const int64_t p = p0 + r0 + r;
           const uint32_t sc = e8m0_code_for_amax(m, 8);
@@ -587,15 +583,6 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
 }
 
 // ========================================================== prefill path ==
-// Gate/up over an expert tile of up to 128 rows and 128 intermediate columns
-// (256 W13 rows: the 128 gate rows, then the 128 up rows).  Wavefront (wm,
-// wn) computes rows [64 wm, 64 wm + 64) x intermediate columns [64 wn, 64 wn
-// + 64): four 16-row A tiles against eight 16-row B tiles (4 gate + 4 up).
-// One MFMA step (K = 128) per stage: the gathered activation rows (16 KB),
-// the weight rows (16 KB) and their scale dwords go global -> registers ->
-// LDS, double-buffered, the next stage's loads in flight during the MFMAs.
-// LDS rows are XOR-swizzled by 16-byte chunk so that the 16 rows one MFMA
-// operand read touches fall in distinct banks.
 constexpr int GU_BM = 128;
 constexpr int GU_BN = 256;                        // W13 rows per tile (128 intermediate columns)
 constexpr int GU_ICOLS = GU_BN / 2;
@@ -610,11 +597,41 @@ struct GuStage {
   uint32_t bs[GU_BN];
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Global -> LDS without registers (gfx950 LDS DMA): lane l's 16 (4) bytes
+// land at dst + 16 l (4 l); dst is the same for the whole wavefront.  Issued
+// as inline assembly so that the compiler neither tracks nor waits for these
+// writes: the kernel orders them itself with explicit vmcnt waits and LDS
+// barriers.  Extra operations outside the compiler's count only make its own
+// vmcnt waits stricter (vector-memory loads complete in issue order).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)(lds_void*)p; }
+__device__ __forceinline__ void dma16_to_lds(const void* src, void* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr(dst))) : "m0");
+}
+__device__ __forceinline__ void dma4_to_lds(const void* src, void* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr(dst))) : "m0");
+}
+
+// Gate/up over an expert tile of up to 128 rows and 128 intermediate columns
+// (256 W13 rows: the 128 gate rows, then the 128 up rows).  Wavefront (wm,
+// wn) computes rows [64 wm, 64 wm + 64) x intermediate columns [64 wn, 64 wn
+// + 64): four 16-row A tiles against eight 16-row B tiles (4 gate + 4 up).
+// One MFMA step (K = 128) per stage; the gathered activation rows (16 KB),
+// the weight rows (16 KB) and their scale dwords go straight from global
+// memory into one of four LDS buffers (no registers), three stages ahead of
+// the matrix cores; within a stage each activation fragment is read from LDS
+// while the previous one is multiplied.  Each lane fetches the global chunk that belongs at its
+// LDS slot, so the buffers come out XOR-swizzled by 16-byte chunk and the 16
+// rows one MFMA operand read touches fall in distinct banks.
 __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
                                                             uint8_t* __restrict__ qsc_ws, int Tk) {
+  constexpr int DMA_PER_STAGE = 10;               // per thread: 4 A + 4 B chunks, 1 A + 1 B scale dword
   __shared__ int tile_start[MAX_E + 1];
   __shared__ int tok[GU_BM];
-  __shared__ GuStage st[2];
+  __shared__ GuStage st0, st1, st2, st3;
   build_tiles(a.offsets, a.E, GU_BM, tile_start);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -647,53 +664,35 @@ __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* 
     }
     lds_barrier();
 
-    // this thread's staging slots: 4 activation chunks, 4 weight chunks, one scale dword each
+    // sources of this thread's LDS slots (rows past the tile read a valid
+    // row whose results are discarded: rows and columns are independent)
     const uint8_t* asrc[4];
     const uint8_t* bsrc[4];
-    bool aok[4], bok[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int qa = tid + 256 * j, r = qa >> 3, c = qa & 7;
+      const int p = j * 256 + tid;
+      const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
       const int t = tok[r];
-      aok[j] = t >= 0;
       asrc[j] = a.x + (int64_t)(t < 0 ? 0 : t) * H + c * 16;
-      const int qb = tid + 256 * j, rb = qb >> 2, cb = qb & 3;
-      const int icol = (rb & 127);                              // intermediate column within the tile
-      bok[j] = icol < ncols;
-      const int r13 = (rb < 128 ? 0 : I) + c0 + (bok[j] ? icol : 0);
+      const int rb = p >> 2, cb = (p & 3) ^ ((rb >> 2) & 3);
+      const int icol = rb & 127;
+      const int r13 = (rb < 128 ? 0 : I) + c0 + (icol < ncols ? icol : 0);
       bsrc[j] = a.w13 + ((int64_t)e * 2 * I + r13) * (H / 2) + cb * 16;
     }
-    const int tas = tok[tid & (GU_BM - 1)];
-    const uint32_t* asc_src = reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)(tas < 0 ? 0 : tas) * (H / 32));
-    const bool asc_ok = tid < GU_BM && tas >= 0;
-    const int icol_s = tid & 127;
-    const bool bsc_ok = icol_s < ncols;
-    const uint32_t* bsc_src = reinterpret_cast<const uint32_t*>(
-        a.w13_sc + ((int64_t)e * 2 * I + (tid < 128 ? 0 : I) + c0 + (bsc_ok ? icol_s : 0)) * (H / 32));
+    const int ra = wave * 32 + (lane & 31);                     // A scale row of this lane (lanes < 32)
+    const int tas = tok[ra];
+    const uint8_t* asc_src = a.x_sc + (int64_t)(tas < 0 ? 0 : tas) * (H / 32);
+    const int rbs = wave * 64 + lane, icol_s = rbs & 127;
+    const uint8_t* bsc_src =
+        a.w13_sc + ((int64_t)e * 2 * I + (rbs < 128 ? 0 : I) + c0 + (icol_s < ncols ? icol_s : 0)) * (H / 32);
 
-    // two register sets of staged loads: stage s + 2 is requested while stage
-    // s is multiplied and stage s + 1 waits in registers for its LDS buffer
-    struct Regs { u32x4 a[4], b[4]; uint32_t as, bs; };
-    Regs R0, R1;                                                // named, never indexed: they stay in registers
-    auto load_stage = [&](int s, Regs& r) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
+    auto issue = [&](int s, GuStage& S) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        r.a[j] = aok[j] ? ldg16(asrc[j] + s * KSTEP) : z;
-        r.b[j] = bok[j] ? ldg16(bsrc[j] + s * 64) : z;
-      }
-      r.as = asc_ok ? asc_src[s] : 0x7F7F7F7Fu;
-      r.bs = bsc_ok ? bsc_src[s] : 0x7F7F7F7Fu;
-    };
-    auto store_stage = [&](GuStage& S, const Regs& r) {
+      for (int j = 0; j < 4; ++j) dma16_to_lds(asrc[j] + s * KSTEP, &S.a[j * 256 + wave * 64]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int qa = tid + 256 * j;
-        S.a[a_phys(qa >> 3, qa & 7)] = r.a[j];
-        S.b[b_phys(qa >> 2, qa & 3)] = r.b[j];
-      }
-      if (tid < GU_BM) S.as[tid] = r.as;
-      S.bs[tid] = r.bs;
+      for (int j = 0; j < 4; ++j) dma16_to_lds(bsrc[j] + s * 64, &S.b[j * 256 + wave * 64]);
+      if (lane < 32) dma4_to_lds(asc_src + s * 4, &S.as[wave * 32]);
+      dma4_to_lds(bsc_src + s * 4, &S.bs[wave * 64]);
     };
 
     v4f acc[4][8];
@@ -701,41 +700,69 @@ __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* 
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    // waves whose rows or columns fall outside the tile skip the matrix work
+    // waves whose rows or columns fall outside the tile skip the matrix work,
+    // and 16-row subtiles past the tile's rows are skipped
     const bool wact = wm * 64 < nrows && wn * 64 < ncols;
+    const int msub = min(4, (nrows - wm * 64 + 15) / 16);
 
-    // one MFMA step from LDS buffer s & 1; `nxt` holds stage s + 1, `fut` receives stage s + 2
-    auto step = [&](int s, Regs& nxt, Regs& fut) {
-      GuStage& S = st[s & 1];
-      lds_barrier();                                            // stage s is in LDS; stage s-1 reads are done
-      if (s + 2 < nsteps) load_stage(s + 2, fut);               // in flight during two steps of MFMAs
-      if (wact) {
-        v8i bf[8];
-        uint32_t bsv[8];
+    // one stage: the eight weight fragments and the first activation
+    // fragment are read, then each group of eight MFMAs runs while the next
+    // activation fragment is on its way from LDS
+    auto compute = [&](const GuStage& S) {
+      if (!wact) return;
+      v8i bf[8];
+      uint32_t bsv[8];
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const int r = (n < 4 ? 0 : 128) + wn * 64 + (n & 3) * 16 + col;
-          const u32x4 v = S.b[b_phys(r, g)];
-          bf[n] = fp4_operand(v);
-          bsv[n] = S.bs[r] >> (8 * g);
+      for (int n = 0; n < 8; ++n) {
+        const int r = (n < 4 ? 0 : 128) + wn * 64 + (n & 3) * 16 + col;
+        bf[n] = fp4_operand(S.b[b_phys(r, g)]);
+        bsv[n] = S.bs[r];
+      }
+      const int r0 = wm * 64 + col;
+      v8i af = fp8_operand(S.a[a_phys(r0, g)], S.a[a_phys(r0, 4 + g)]);
+      uint32_t sa = S.as[r0];
+      __builtin_amdgcn_sched_barrier(0);                        // all of the stage's first reads in flight at once
+#pragma unroll
+      for (int n = 0; n < 8; ++n) bsv[n] >>= 8 * g;
+      sa >>= 8 * g;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m >= msub) break;                                   // wavefront-uniform
+        v8i an;
+        uint32_t san = 0;
+        if (m < 3) {
+          const int r = wm * 64 + (m + 1) * 16 + col;
+          an = fp8_operand(S.a[a_phys(r, g)], S.a[a_phys(r, 4 + g)]);
+          san = S.as[r];
         }
+        __builtin_amdgcn_sched_barrier(0);                      // the next fragment's reads stay ahead of these MFMAs
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = wm * 64 + m * 16 + col;
-          const v8i af = fp8_operand(S.a[a_phys(r, g)], S.a[a_phys(r, 4 + g)]);
-          const uint32_t sa = S.as[r] >> (8 * g);
-#pragma unroll
-          for (int n = 0; n < 8; ++n) acc[m][n] = mfma_fp8_fp4(af, bf[n], acc[m][n], sa, bsv[n]);
+        for (int n = 0; n < 8; ++n) acc[m][n] = mfma_fp8_fp4(af, bf[n], acc[m][n], sa, bsv[n]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m < 3) {
+          af = an;
+          sa = san >> (8 * g);
         }
       }
-      if (s + 1 < nsteps) store_stage(st[(s + 1) & 1], nxt);
     };
-    load_stage(0, R0);
-    if (nsteps > 1) load_stage(1, R1);
-    store_stage(st[0], R0);
-    for (int s = 0; s < nsteps; s += 2) {
-      step(s, R1, R0);
-      if (s + 1 < nsteps) step(s + 1, R0, R1);
+    // stage s: wait for its own DMA (later stages stay in flight), make every
+    // wavefront's part visible, refill the buffer freed by stage s - 1, multiply
+    auto step = [&](int s, GuStage& S, GuStage& refill) {
+      if (s + 2 < nsteps) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * DMA_PER_STAGE) : "memory");
+      else if (s + 1 < nsteps) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(DMA_PER_STAGE) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      if (s + 3 < nsteps) issue(s + 3, refill);
+      compute(S);
+    };
+    issue(0, st0);
+    if (nsteps > 1) issue(1, st1);
+    if (nsteps > 2) issue(2, st2);
+    for (int s = 0; s < nsteps; s += 4) {
+      step(s, st0, st3);
+      if (s + 1 < nsteps) step(s + 1, st1, st0);
+      if (s + 2 < nsteps) step(s + 2, st2, st1);
+      if (s + 3 < nsteps) step(s + 3, st3, st2);
     }
 
     // epilogue: SwiGLU + requant; one block of 32 = two 16-column subtiles of one row
@@ -748,11 +775,7 @@ __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* 
           for (int i = 0; i < 4; ++i) {
             const float v0 = swiglu(acc[m][2 * blk][i], acc[m][4 + 2 * blk][i]);
             const float v1 = swiglu(acc[m][2 * blk + 1][i], acc[m][5 + 2 * blk][i]);
-            float mx = fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
-            mx = fmaxf(mx, __shfl_xor(mx, 1));
-            mx = fmaxf(mx, __shfl_xor(mx, 2));
-            mx = fmaxf(mx, __shfl_xor(mx, 4));
-            mx = fmaxf(mx, __shfl_xor(mx, 8));
+            const float mx = row16_max(fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
             const uint32_t sc = e8m0_code_for_amax(mx, 8);
             const int row = wm * 64 + m * 16 + 4 * g + i;
             const int cb = c0 + wn * 64 + blk * 32;           // first column of the block

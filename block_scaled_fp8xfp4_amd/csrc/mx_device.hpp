@@ -110,13 +110,25 @@ __device__ __forceinline__ uint32_t encode_e2m1(float v, uint32_t sc) {
   return code | sign;
 }
 
-// SwiGLU of one gate/up pair in fp32: silu(g) * u, silu(g) = g / (1 + e^-g).
-// Contraction is off so every kernel that inlines it rounds identically.
+// SwiGLU of one gate/up pair in fp32: silu(g) * u, silu(g) = g / (1 + e^-g),
+// with the hardware exponential and reciprocal (a few ulp; the FP8 requant
+// that follows keeps 3 mantissa bits).  Contraction is off so every kernel
+// that inlines it rounds identically.
 __device__ __forceinline__ float swiglu(float g, float u) {
 #pragma clang fp contract(off)
-  const float d = 1.0f + expf(-g);
-  const float s = g / d;
+  const float d = 1.0f + __expf(-g);
+  const float s = g * __builtin_amdgcn_rcpf(d);
   return s * u;
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), in
+// registers: quad butterflies, then rotations by 4 and 8 within the row.
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));   // quad [1,0,3,2]
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));   // quad [2,3,0,1]
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x124, 0xF, 0xF, false)));  // row_ror:4
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, false)));  // row_ror:8
+  return m;
 }
 
 // E4M3 code of one element of a block whose shared scale code is sc (the
