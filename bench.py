@@ -73,7 +73,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay one HIP graph per step instead of eager launches")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 256 MiB buffer 5 times (reference kernel for the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel(), "copies": 5}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode "
               "(the layer shards by rows or by the intermediate dimension; see the design notes).",
