@@ -5,12 +5,16 @@
 // rows on small row tiles).
 //
 // One workgroup per 16 output columns.  Its four wavefronts take the
-// canonical K parts (1024 each) and stream their slice of the 16 weight rows
-// straight from HBM into registers (two 16-byte loads per lane per MFMA
-// step, so every load instruction covers 64 contiguous bytes of 16 rows);
-// the row tile of activations is re-read from L2 by every column tile.  The
-// parts are added in part order through LDS, so an element's result does not
-// depend on M.
+// canonical K parts (1024 each, part q by wavefront q mod 4) and stream their
+// slice of the 16 weight rows straight from HBM into registers (two 16-byte
+// loads per lane per MFMA step, so every load instruction covers 64
+// contiguous bytes of 16 rows).  Every load is unconditional: lanes of rows
+// past M read row M - 1 again and their results are discarded (rows of the
+// product are independent), and a part past K reloads its last step without
+// using it, so a wavefront's loads issue back to back.  The row tile's
+// activations (re-read from L2 by every column tile) are requested before
+// the weights.  The parts are added in part order through LDS, so an
+// element's result does not depend on M.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
@@ -20,64 +24,45 @@ __device__ __forceinline__ v8i fp8_pair(const u32x4& lo, const u32x4& hi) {
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-template <bool BF16_OUT>
+template <bool BF16_OUT, bool WHOLE>                            // WHOLE: K is a multiple of the part (1024)
 __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
                                                           const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sc,
                                                           int M, int N, int K, void* __restrict__ y) {
-  __shared__ float red[MAX_PARTS][16][16];
+  __shared__ float red[MAX_PARTS][16][17];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int nsteps = K / KSTEP, nparts = (nsteps + KPART_STEPS - 1) / KPART_STEPS;
   const int n0 = blockIdx.x * 16;
   const int64_t n = n0 + col;
-  const uint8_t* wp = w + n * K;
+  const uint8_t* wp = w + n * K + g * 16;
   const uint32_t* wsp = reinterpret_cast<const uint32_t*>(w_sc + n * (K / 32));
   for (int rt = 0; rt * 16 < M; ++rt) {
-    const int m_row = rt * 16 + col;
-    const bool rv = m_row < M;
-    const uint8_t* ap = a + (int64_t)(rv ? m_row : 0) * K;
-    const uint32_t* asp = reinterpret_cast<const uint32_t*>(a_sc + (int64_t)(rv ? m_row : 0) * (K / 32));
+    const int m_row = min(rt * 16 + col, M - 1);               // rows past M repeat row M - 1
+    const uint8_t* ap = a + (int64_t)m_row * K + g * 16;
+    const uint32_t* asp = reinterpret_cast<const uint32_t*>(a_sc + (int64_t)m_row * (K / 32));
     for (int q = wave; q < nparts; q += 4) {
       const int s0 = q * KPART_STEPS;
       u32x4 blo[KPART_STEPS], bhi[KPART_STEPS], alo[KPART_STEPS], ahi[KPART_STEPS];
       uint32_t bs[KPART_STEPS], as[KPART_STEPS];
-      // weights then activations: every load of the part is in flight before
-      // any is used; scale dwords stay raw until the MFMA
-      if (s0 + KPART_STEPS <= nsteps) {
 #pragma unroll
-        for (int m = 0; m < KPART_STEPS; ++m) {
-          const int s = s0 + m;
-          blo[m] = ldg16(wp + s * KSTEP + g * 16);
-          bhi[m] = ldg16(wp + s * KSTEP + 64 + g * 16);
-          bs[m] = wsp[s];
-        }
-#pragma unroll
-        for (int m = 0; m < KPART_STEPS; ++m) {
-          const int s = s0 + m;
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          alo[m] = rv ? ldg16(ap + s * KSTEP + g * 16) : z;
-          ahi[m] = rv ? ldg16(ap + s * KSTEP + 64 + g * 16) : z;
-          as[m] = rv ? asp[s] : bs[m];
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < KPART_STEPS; ++m) {
-          const int s = s0 + m;
-          if (s < nsteps) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            blo[m] = ldg16(wp + s * KSTEP + g * 16);
-            bhi[m] = ldg16(wp + s * KSTEP + 64 + g * 16);
-            bs[m] = wsp[s];
-            alo[m] = rv ? ldg16(ap + s * KSTEP + g * 16) : z;
-            ahi[m] = rv ? ldg16(ap + s * KSTEP + 64 + g * 16) : z;
-            as[m] = rv ? asp[s] : bs[m];
-          }
-        }
+      for (int m = 0; m < KPART_STEPS; ++m) {
+        const int s = WHOLE ? s0 + m : min(s0 + m, nsteps - 1);
+        alo[m] = ldg16(ap + s * KSTEP);
+        ahi[m] = ldg16(ap + s * KSTEP + 64);
+        as[m] = asp[s];
       }
+#pragma unroll
+      for (int m = 0; m < KPART_STEPS; ++m) {
+        const int s = WHOLE ? s0 + m : min(s0 + m, nsteps - 1);
+        blo[m] = ldg16(wp + s * KSTEP);
+        bhi[m] = ldg16(wp + s * KSTEP + 64);
+        bs[m] = wsp[s];
+      }
+      __builtin_amdgcn_sched_barrier(0);                        // every load of the part issued before the first MFMA
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < KPART_STEPS; ++m)
-        if (s0 + m < nsteps)
+        if (WHOLE || s0 + m < nsteps)
           acc = mfma_fp8_fp8(fp8_pair(alo[m], ahi[m]), fp8_pair(blo[m], bhi[m]), acc, as[m] >> (8 * g), bs[m] >> (8 * g));
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[q][4 * g + i][col] = acc[i];
@@ -100,8 +85,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint8_t* __restr
 hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,
                              int M, int N, int K, void* y, bool bf16_out, hipStream_t stream, const char** variant) {
   const dim3 grid(N / 16), block(256);
-  if (bf16_out) hipLaunchKernelGGL(gemm_decode_kernel<true>, grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
-  else hipLaunchKernelGGL(gemm_decode_kernel<false>, grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
+  const bool whole = K % KPART == 0;
+  if (bf16_out && whole) hipLaunchKernelGGL((gemm_decode_kernel<true, true>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
+  else if (bf16_out) hipLaunchKernelGGL((gemm_decode_kernel<true, false>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
+  else if (whole) hipLaunchKernelGGL((gemm_decode_kernel<false, true>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
+  else hipLaunchKernelGGL((gemm_decode_kernel<false, false>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
   *variant = bf16_out ? "gemm:decode16_kpart4_bf16" : "gemm:decode16_kpart4_f32";
   return hipGetLastError();
 }
