@@ -42,12 +42,12 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 template <int PER>
 __device__ void wave_topk(const float* __restrict__ l, int E, int k, int& out_idx, float& out_val) {
   const int lane = threadIdx.x & 63;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = l[min(lane + 64 * i, E - 1)];   // branch-free: all loads in flight together
   uint32_t key[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? order_key(l[e]) : 0u;                      // 0: below every logit
-  }
+  for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? order_key(v[i]) : 0u;   // 0: below every logit
   out_idx = 0;
   out_val = 0.0f;
   for (int j = 0; j < k; ++j) {
