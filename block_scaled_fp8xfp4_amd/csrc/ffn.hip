@@ -792,117 +792,154 @@ __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* 
   }
 }
 
-// Down over a 64-row expert tile and 256 W2 rows (64 per wavefront, four
-// 16-row B tiles); the tile's intermediate rows are contiguous bucket rows.
-__global__ __launch_bounds__(256, 2) void down_prefill_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
+// Down, weight-stationary: one workgroup of eight wavefronts per (expert, 256
+// W2 rows); each wavefront keeps its 32 W2 rows (two 16-row B tiles, whole
+// K = I, NS steps) in registers and walks all of the expert's 64-row tiles.  A tile's
+// intermediate rows (contiguous bucket rows) go global -> LDS by LDS DMA, one
+// instruction per row (I / 16 lanes); their scale bytes through registers.
+// Each W2 byte is read once per workgroup instead of once per row tile.
+constexpr int DN_WAVES = 8;
+template <int NS>
+__global__ __launch_bounds__(64 * DN_WAVES, 2) void down_prefill_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
                                                               const uint8_t* __restrict__ qsc_ws,
                                                               float* __restrict__ o, int Tk) {
+  constexpr int NT = 64 * DN_WAVES;
+  constexpr int SPT = (PF_ROWS * NS * 4 + NT - 1) / NT;         // scale bytes per thread
   __shared__ int tile_start[MAX_E + 1];
+  __shared__ int offs[MAX_E + 1];
   __shared__ __attribute__((aligned(16))) uint8_t qlds[PF_ROWS][PF_MAX_I + 16];
   __shared__ uint8_t slds[PF_ROWS][PF_MAX_I / 32 + 4];
-  build_tiles(a.offsets, a.E, PF_ROWS, tile_start);
+  for (int i = threadIdx.x; i <= a.E; i += blockDim.x) offs[i] = a.offsets[i];   // published by build_tiles' barrier
+  build_tiles(a.offsets, a.E, 0, tile_start);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int H = a.H, I = a.I, nb = I / 32;
-  const int nsteps = (I + KSTEP - 1) / KSTEP;                   // <= 5
+  const int nsteps = (I + KSTEP - 1) / KSTEP;                   // <= NS
+  const int q16 = I / 16;                                       // <= 40 lanes per row
   const int nnt = H / PF_NCOLS;
   const int nitems = tile_start[a.E] * nnt;
+  // K past I reads zeros: the row tails are cleared once, staging never writes them
+  for (int idx = tid; idx < PF_ROWS * (NS * KSTEP - I); idx += NT)
+    qlds[idx / (NS * KSTEP - I)][I + idx % (NS * KSTEP - I)] = 0;
+  for (int idx = tid; idx < PF_ROWS * (NS * 4 - nb); idx += NT)
+    slds[idx / (NS * 4 - nb)][nb + idx % (NS * 4 - nb)] = 127;
 
   for (int round = 0;; ++round) {
     const int item = xcd_item(round, blockIdx.x, gridDim.x);
     if (item >= nitems) break;
-    const int tile = item / nnt, nt = item % nnt;
-    const int e = tile_expert(tile_start, a.E, tile);
-    const int p0 = a.offsets[e] + (tile - tile_start[e]) * PF_ROWS;
-    int nrows = a.offsets[e + 1] - p0;
-    nrows = nrows > PF_ROWS ? PF_ROWS : nrows;
-    if (p0 < 0 || p0 + nrows > Tk) nrows = 0;
-
-    // W2 of this lane's four columns first (whole K = I in registers)
-    const int n0 = nt * PF_NCOLS + wave * 64;
-    u32x4 bw[4][5];
-    uint32_t bs[4][5];
+    const int nt = item % nnt;
+    const int e = tile_expert(tile_start, a.E, item / nnt);
+    const int pbeg = offs[e];
+    int cnt = offs[e + 1] - pbeg;
+    if (pbeg < 0 || pbeg + cnt > Tk) cnt = 0;
+    const int n0 = nt * PF_NCOLS + wave * 32;
+    u32x4 bw[2][NS];
+    uint32_t bs[2][NS];
+    for (int r0 = 0; r0 < cnt; r0 += PF_ROWS) {
+      const int p0 = pbeg + r0;
+      const int nrows = min(PF_ROWS, cnt - r0);
+      lds_barrier();                                            // previous tile's LDS reads are done
+      // the tile's intermediate: wavefront w fills rows w, w + 8, ... (rows
+      // past nrows repeat the tile's last row; their results are discarded)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int64_t row = (int64_t)e * H + n0 + n * 16 + col;
-      const uint8_t* wp = a.w2 + row * (I / 2);
-      const uint8_t* wsp = a.w2_sc + row * nb;
-#pragma unroll
-      for (int s = 0; s < 5; ++s) {
-        const bool bv = s < nsteps && 4 * s + g < nb;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        bw[n][s] = bv ? ldg16(wp + s * 64 + g * 16) : z;
-        bs[n][s] = wsp[bv ? 4 * s + g : 0];
+      for (int i = 0; i < PF_ROWS / DN_WAVES; ++i) {
+        const int r = wave + DN_WAVES * i;
+        if (lane < q16) dma16_to_lds(qws + (int64_t)(p0 + min(r, nrows - 1)) * I + lane * 16, &qlds[r][0]);
       }
-    }
-    lds_barrier();                                              // previous item's LDS reads are done
-    const int q16 = I / 16;
-    for (int idx = tid; idx < PF_ROWS * q16; idx += 256) {
-      const int r = idx / q16, c16 = idx % q16;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&qlds[r][c16 * 16]) = r < nrows ? ldg16(qws + (int64_t)(p0 + r) * I + c16 * 16) : z;
-    }
-    for (int idx = tid; idx < PF_ROWS * nb; idx += 256) {
-      const int r = idx / nb, b = idx % nb;
-      slds[r][b] = r < nrows ? qsc_ws[(int64_t)(p0 + r) * nb + b] : (uint8_t)127;
-    }
-    lds_barrier();
+      uint32_t sv[SPT];
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        const int idx = min(tid + NT * i, PF_ROWS * nb - 1);
+        const int r = min(idx / nb, nrows - 1), b = idx % nb;
+        sv[i] = qsc_ws[(int64_t)(p0 + r) * nb + b];
+      }
+      if (r0 == 0) {
+        // first tile: this wavefront's W2 rows, requested after the tile's rows
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          load_w2_tile<NS>(a.w2, a.w2_sc, (int64_t)e * H + n0 + n * 16 + col, I, g, bw[n], bs[n]);
+      }
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        const int idx = tid + NT * i;
+        if (idx < PF_ROWS * nb) slds[idx / nb][idx % nb] = (uint8_t)sv[i];
+      }
+      if (r0 == 0) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(4 * NS) : "memory");   // DMA done, W2 may be in flight
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
 
-    v4f acc[4][4];
+      v4f acc[4][2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int n = 0; n < 4; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < 2; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 5; ++s) {
-      if (s < nsteps) {
-        const int klo = s * KSTEP + g * 16, khi = klo + 64;
+      for (int s = 0; s < NS; ++s) {
+        if (s < nsteps) {
+          const int klo = s * KSTEP + g * 16;
+          const bool bv = 4 * s + g < nb;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = m * 16 + col;
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 alo = klo < I ? *reinterpret_cast<const u32x4*>(&qlds[r][klo]) : z;
-          const u32x4 ahi = khi < I ? *reinterpret_cast<const u32x4*>(&qlds[r][khi]) : z;
-          const uint32_t sa = (4 * s + g < nb) ? (uint32_t)slds[r][4 * s + g] : bs[0][s];
-          const v8i av = fp8_operand(alo, ahi);
+          for (int m = 0; m < 4; ++m) {
+            const int r = m * 16 + col;
+            const v8i av = fp8_operand(*reinterpret_cast<const u32x4*>(&qlds[r][klo]),
+                                       *reinterpret_cast<const u32x4*>(&qlds[r][klo + 64]));
+            const uint32_t sa = slds[r][4 * s + g];
 #pragma unroll
-          for (int n = 0; n < 4; ++n) acc[m][n] = mfma_fp8_fp4(av, fp4_operand(bw[n][s]), acc[m][n], sa, bs[n][s]);
+            for (int n = 0; n < 2; ++n)
+              acc[m][n] = mfma_fp8_fp4(av, fp4_operand_masked(bw[n][s], bv), acc[m][n], sa, bs[n][s]);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m * 16 + 4 * g + i;
-        if (row < nrows) {
-          float* orow = o + (int64_t)(p0 + row) * H + n0 + col;
+        for (int i = 0; i < 4; ++i) {
+          const int row = m * 16 + 4 * g + i;
+          if (row < nrows) {
+            float* orow = o + (int64_t)(p0 + row) * H + n0 + col;
 #pragma unroll
-          for (int n = 0; n < 4; ++n) orow[n * 16] = acc[m][n][i];
+            for (int n = 0; n < 2; ++n) orow[n * 16] = acc[m][n][i];
+          }
         }
-      }
+    }
   }
 }
 
 // ============================================================== combine ===
-// y_t = sum_j w_tj * o[slot_pos[t][j]], j = 0..k-1 in order; 4 columns per thread.
+// y_t = sum_j w_tj * o[slot_pos[t][j]], j = 0..k-1 in order; 4 columns per
+// thread.  Every slot's position, weight and output are requested before the
+// first add (a dead slot reads row 0 and is skipped by a select).
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const float* __restrict__ w,
                                                       const int32_t* __restrict__ slot_pos, int T, int H, int k, int Tk,
                                                       float* __restrict__ y) {
   const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (n >= H) return;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    int p[KMAX];
+    float wj[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const int jj = j < k ? j : 0;
+      p[j] = slot_pos[(int64_t)t * k + jj];
+      wj[j] = w[(int64_t)t * k + jj];
+    }
+    float4 v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const bool ok = j < k && p[j] >= 0 && p[j] < Tk;
+      v[j] = *reinterpret_cast<const float4*>(o + (int64_t)(ok ? p[j] : 0) * H + n);
+    }
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int p = slot_pos[(int64_t)t * k + j];
-      if (p < 0 || p >= Tk) continue;
-      const float wj = w[(int64_t)t * k + j];
-      const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)p * H + n);
-      acc.x = fmaf(wj, v.x, acc.x);
-      acc.y = fmaf(wj, v.y, acc.y);
-      acc.z = fmaf(wj, v.z, acc.z);
-      acc.w = fmaf(wj, v.w, acc.w);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const bool ok = j < k && p[j] >= 0 && p[j] < Tk;
+      acc.x = ok ? fmaf(wj[j], v[j].x, acc.x) : acc.x;
+      acc.y = ok ? fmaf(wj[j], v[j].y, acc.y) : acc.y;
+      acc.z = ok ? fmaf(wj[j], v[j].z, acc.z) : acc.z;
+      acc.w = ok ? fmaf(wj[j], v[j].w, acc.w) : acc.w;
     }
     *reinterpret_cast<float4*>(y + (int64_t)t * H + n) = acc;
   }
@@ -995,19 +1032,20 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     else hipLaunchKernelGGL(down_decode_kernel<16>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
     *variant = "ffn:gu_decode+down_decode+combine";
   } else {
-    const int tiles_bound = Tk / PF_ROWS + max_active;
     const int gu_items = (Tk / GU_BM + max_active) * ((a.I + GU_ICOLS - 1) / GU_ICOLS);
-    const int dn_items = tiles_bound * (a.H / PF_NCOLS);
+    const int dn_items = max_active * (a.H / PF_NCOLS);
     int gu_grid = gu_items < cus ? gu_items : cus;             // one 4-wavefront workgroup per CU
     int dn_grid = dn_items < cus * 2 ? dn_items : cus * 2;
     gu_grid = (gu_grid + XCDS - 1) / XCDS * XCDS;
     dn_grid = (dn_grid + XCDS - 1) / XCDS * XCDS;
     hipLaunchKernelGGL(gu_prefill_kernel, dim3(gu_grid), dim3(256), 0, stream, a, qws, qsc, Tk);
-    hipLaunchKernelGGL(down_prefill_kernel, dim3(dn_grid), dim3(256), 0, stream, a, qws, qsc, o, Tk);
+    if (a.I <= 2 * KSTEP) hipLaunchKernelGGL(down_prefill_kernel<2>, dim3(dn_grid), dim3(64 * DN_WAVES), 0, stream, a, qws, qsc, o, Tk);
+    else hipLaunchKernelGGL(down_prefill_kernel<5>, dim3(dn_grid), dim3(64 * DN_WAVES), 0, stream, a, qws, qsc, o, Tk);
     *variant = "ffn:gu_prefill64+down_prefill64+combine";
   }
   const dim3 cgrid((a.H / 4 + 255) / 256, a.T < 65535 ? a.T : 65535);
-  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, o, a.topk_w, a.slot_pos, a.T, a.H, a.k, Tk, a.y);
+  if (a.k <= 8) hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(256), 0, stream, o, a.topk_w, a.slot_pos, a.T, a.H, a.k, Tk, a.y);
+  else hipLaunchKernelGGL(combine_kernel<MAX_K>, cgrid, dim3(256), 0, stream, o, a.topk_w, a.slot_pos, a.T, a.H, a.k, Tk, a.y);
   return hipGetLastError();
 }
 
