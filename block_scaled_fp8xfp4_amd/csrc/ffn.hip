@@ -170,6 +170,28 @@ __device__ __forceinline__ int xcd_item(int round, int b, int G) {
   return round * G + (b % XCDS) * per + b / XCDS;
 }
 
+// Work queue of a persistent kernel: items [0, n) are split into XCDS
+// contiguous ranges, one per XCD (the items that share activation rows and
+// weights then meet in one L2).  A workgroup takes the next item of its own
+// XCD's range from that range's counter and, once the range is drained, of
+// the following ones.  Called by one thread; returns -1 when every range is
+// drained.  Counters start at zero (cleared before the launch) and only grow.
+__device__ __forceinline__ int queue_next(int* ctr, int n, int& q) {
+  const int x0 = blockIdx.x % XCDS;
+  while (q < XCDS) {
+    const int x = (x0 + q) % XCDS;
+    const int lo = (int)((int64_t)n * x / XCDS), hi = (int)((int64_t)n * (x + 1) / XCDS);
+    const int c = atomicAdd(&ctr[x], 1);
+    if (c < hi - lo) return lo + c;
+    ++q;
+  }
+  return -1;
+}
+
+__global__ void clear_i32_kernel(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 __device__ __forceinline__ v8i fp8_operand(const u32x4& lo, const u32x4& hi) {
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
@@ -586,6 +608,8 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
 constexpr int GU_BM = 128;
 constexpr int GU_BN = 256;                        // W13 rows per tile (128 intermediate columns)
 constexpr int GU_ICOLS = GU_BN / 2;
+constexpr int GU_STAGES = 2;                      // LDS stages per workgroup
+constexpr int GU_WG_PER_CU = 4 / GU_STAGES;       // workgroups resident per CU (LDS-bound)
 
 __device__ __forceinline__ int a_phys(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }   // 16-byte chunk
 __device__ __forceinline__ int b_phys(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
@@ -598,6 +622,7 @@ struct GuStage {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+template <int N> struct IntC { static constexpr int value = N; };
 
 // Global -> LDS without registers (gfx950 LDS DMA): lane l's 16 (4) bytes
 // land at dst + 16 l (4 l); dst is the same for the whole wavefront.  Issued
@@ -614,6 +639,16 @@ __device__ __forceinline__ void dma4_to_lds(const void* src, void* dst) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr(dst))) : "m0");
 }
+// The same from a wavefront-uniform base plus a 32-bit per-lane byte offset,
+// to the wavefront-uniform LDS byte address dst.
+__device__ __forceinline__ void dma16_to_lds(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(dst) : "m0");
+}
+__device__ __forceinline__ void dma4_to_lds(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(dst) : "m0");
+}
 
 // Gate/up over an expert tile of up to 128 rows and 128 intermediate columns
 // (256 W13 rows: the 128 gate rows, then the 128 up rows).  Wavefront (wm,
@@ -626,25 +661,34 @@ __device__ __forceinline__ void dma4_to_lds(const void* src, void* dst) {
 // while the previous one is multiplied.  Each lane fetches the global chunk that belongs at its
 // LDS slot, so the buffers come out XOR-swizzled by 16-byte chunk and the 16
 // rows one MFMA operand read touches fall in distinct banks.
-__global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
-                                                            uint8_t* __restrict__ qsc_ws, int Tk) {
+template <int NSTG>
+__global__ __launch_bounds__(256, 4 / NSTG) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
+                                                                   uint8_t* __restrict__ qsc_ws, int Tk,
+                                                                   int* __restrict__ queue) {
   constexpr int DMA_PER_STAGE = 10;               // per thread: 4 A + 4 B chunks, 1 A + 1 B scale dword
   __shared__ int tile_start[MAX_E + 1];
   __shared__ int tok[GU_BM];
-  __shared__ GuStage st0, st1, st2, st3;
+  __shared__ GuStage st[NSTG];
   build_tiles(a.offsets, a.E, GU_BM, tile_start);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int H = a.H, I = a.I, nb = I / 32;
   const int nsteps = H / KSTEP;
+  const uint32_t st_lds = __builtin_amdgcn_readfirstlane(lds_addr(&st[0]));   // LDS byte address of stage 0
   const int nct = (I + GU_ICOLS - 1) / GU_ICOLS;
   const int nitems = tile_start[a.E] * nct;
+  __shared__ int s_item;
+  int qpos = 0;                                                 // queue position (thread 0)
 
-  for (int round = 0;; ++round) {
-    const int item = xcd_item(round, blockIdx.x, gridDim.x);
-    if (item >= nitems) break;
+  for (;;) {
+    lds_barrier();                                              // previous item's LDS reads are done
+    if (tid == 0) s_item = queue_next(queue, nitems, qpos);
+    lds_barrier();
+    const int item = s_item;
+    if (item < 0) break;
     const int tile = item / nct, ct = item % nct;
     const int e = tile_expert(tile_start, a.E, tile);
     const int p0 = a.offsets[e] + (tile - tile_start[e]) * GU_BM;
@@ -653,7 +697,6 @@ __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* 
     if (p0 < 0 || p0 + nrows > Tk) nrows = 0;
     const int c0 = ct * GU_ICOLS;                               // first intermediate column of the tile
     const int ncols = min(GU_ICOLS, I - c0);
-    lds_barrier();                                              // previous item's LDS reads are done
     if (tid < GU_BM) {
       int t = -1;
       if (tid < nrows) {
@@ -666,33 +709,38 @@ __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* 
 
     // sources of this thread's LDS slots (rows past the tile read a valid
     // row whose results are discarded: rows and columns are independent)
-    const uint8_t* asrc[4];
-    const uint8_t* bsrc[4];
+    // (byte offsets from wavefront-uniform bases: the activations, and this
+    // expert's weights and scales; T * H < 2^32 is checked at the boundary)
+    uint32_t aoff[4], boff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int p = j * 256 + tid;
       const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
       const int t = tok[r];
-      asrc[j] = a.x + (int64_t)(t < 0 ? 0 : t) * H + c * 16;
+      aoff[j] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)H + c * 16;
       const int rb = p >> 2, cb = (p & 3) ^ ((rb >> 2) & 3);
       const int icol = rb & 127;
       const int r13 = (rb < 128 ? 0 : I) + c0 + (icol < ncols ? icol : 0);
-      bsrc[j] = a.w13 + ((int64_t)e * 2 * I + r13) * (H / 2) + cb * 16;
+      boff[j] = (uint32_t)r13 * (uint32_t)(H / 2) + cb * 16;
     }
     const int ra = wave * 32 + (lane & 31);                     // A scale row of this lane (lanes < 32)
     const int tas = tok[ra];
-    const uint8_t* asc_src = a.x_sc + (int64_t)(tas < 0 ? 0 : tas) * (H / 32);
+    const uint32_t asoff = (uint32_t)(tas < 0 ? 0 : tas) * (uint32_t)(H / 32);
     const int rbs = wave * 64 + lane, icol_s = rbs & 127;
-    const uint8_t* bsc_src =
-        a.w13_sc + ((int64_t)e * 2 * I + (rbs < 128 ? 0 : I) + c0 + (icol_s < ncols ? icol_s : 0)) * (H / 32);
+    const uint32_t bsoff = (uint32_t)((rbs < 128 ? 0 : I) + c0 + (icol_s < ncols ? icol_s : 0)) * (uint32_t)(H / 32);
+    const uint8_t* w13e = a.w13 + (int64_t)e * 2 * I * (H / 2);
+    const uint8_t* w13se = a.w13_sc + (int64_t)e * 2 * I * (H / 32);
 
-    auto issue = [&](int s, GuStage& S) {
+    auto issue = [&](int s, int buf) {
+      const uint32_t d = st_lds + buf * (uint32_t)sizeof(GuStage);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16_to_lds(asrc[j] + s * KSTEP, &S.a[j * 256 + wave * 64]);
+      for (int j = 0; j < 4; ++j)
+        dma16_to_lds(a.x + s * KSTEP, aoff[j], d + (uint32_t)offsetof(GuStage, a) + (j * 256 + wave * 64) * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16_to_lds(bsrc[j] + s * 64, &S.b[j * 256 + wave * 64]);
-      if (lane < 32) dma4_to_lds(asc_src + s * 4, &S.as[wave * 32]);
-      dma4_to_lds(bsc_src + s * 4, &S.bs[wave * 64]);
+      for (int j = 0; j < 4; ++j)
+        dma16_to_lds(w13e + s * 64, boff[j], d + (uint32_t)offsetof(GuStage, b) + (j * 256 + wave * 64) * 16);
+      if (lane < 32) dma4_to_lds(a.x_sc + s * 4, asoff, d + (uint32_t)offsetof(GuStage, as) + wave * 32 * 4);
+      dma4_to_lds(w13se + s * 4, bsoff, d + (uint32_t)offsetof(GuStage, bs) + wave * 64 * 4);
     };
 
     v4f acc[4][8];
@@ -708,36 +756,44 @@ __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* 
     // one stage: the eight weight fragments and the first activation
     // fragment are read, then each group of eight MFMAs runs while the next
     // activation fragment is on its way from LDS
+    // one stage: the eight weight fragments and the first activation
+    // fragment are read, then each group of eight MFMAs runs while the next
+    // activation fragment is on its way from LDS; the groups of 16-row
+    // subtiles past the tile's rows are skipped (wavefront-uniform branches)
+    // lane parts of the swizzled LDS indices (row bases are multiples of 16,
+    // so the swizzle depends on the lane alone)
+    const int bl = b_phys(col, g), al0 = a_phys(col, g), al1 = a_phys(col, 4 + g);
     auto compute = [&](const GuStage& S) {
       if (!wact) return;
       v8i bf[8];
       uint32_t bsv[8];
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const int r = (n < 4 ? 0 : 128) + wn * 64 + (n & 3) * 16 + col;
-        bf[n] = fp4_operand(S.b[b_phys(r, g)]);
-        bsv[n] = S.bs[r];
+        const int rb = (n < 4 ? 0 : 128) + wn * 64 + (n & 3) * 16;
+        bf[n] = fp4_operand(S.b[rb * 4 + bl]);
+        bsv[n] = S.bs[rb + col];
       }
-      const int r0 = wm * 64 + col;
-      v8i af = fp8_operand(S.a[a_phys(r0, g)], S.a[a_phys(r0, 4 + g)]);
-      uint32_t sa = S.as[r0];
+      const int ra0 = wm * 64;
+      v8i af = fp8_operand(S.a[ra0 * 8 + al0], S.a[ra0 * 8 + al1]);
+      uint32_t sa = S.as[ra0 + col];
       __builtin_amdgcn_sched_barrier(0);                        // all of the stage's first reads in flight at once
 #pragma unroll
       for (int n = 0; n < 8; ++n) bsv[n] >>= 8 * g;
       sa >>= 8 * g;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        if (m >= msub) break;                                   // wavefront-uniform
         v8i an;
         uint32_t san = 0;
         if (m < 3) {
-          const int r = wm * 64 + (m + 1) * 16 + col;
-          an = fp8_operand(S.a[a_phys(r, g)], S.a[a_phys(r, 4 + g)]);
-          san = S.as[r];
+          const int ra = wm * 64 + (m + 1) * 16;
+          an = fp8_operand(S.a[ra * 8 + al0], S.a[ra * 8 + al1]);
+          san = S.as[ra + col];
         }
         __builtin_amdgcn_sched_barrier(0);                      // the next fragment's reads stay ahead of these MFMAs
+        if (m < msub) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n) acc[m][n] = mfma_fp8_fp4(af, bf[n], acc[m][n], sa, bsv[n]);
+          for (int n = 0; n < 8; ++n) acc[m][n] = mfma_fp8_fp4(af, bf[n], acc[m][n], sa, bsv[n]);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (m < 3) {
           af = an;
@@ -747,22 +803,22 @@ __global__ __launch_bounds__(256, 1) void gu_prefill_kernel(FfnArgs a, uint8_t* 
     };
     // stage s: wait for its own DMA (later stages stay in flight), make every
     // wavefront's part visible, refill the buffer freed by stage s - 1, multiply
-    auto step = [&](int s, GuStage& S, GuStage& refill) {
-      if (s + 2 < nsteps) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * DMA_PER_STAGE) : "memory");
-      else if (s + 1 < nsteps) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(DMA_PER_STAGE) : "memory");
+    auto step = [&](int s, const GuStage& S, int refill) {
+      const int later = min(NSTG - 2, nsteps - 1 - s);          // stages after s already in flight
+      if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * DMA_PER_STAGE) : "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(DMA_PER_STAGE) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       lds_barrier();
-      if (s + 3 < nsteps) issue(s + 3, refill);
+      if (s + NSTG - 1 < nsteps) issue(s + NSTG - 1, refill);
       compute(S);
     };
-    issue(0, st0);
-    if (nsteps > 1) issue(1, st1);
-    if (nsteps > 2) issue(2, st2);
-    for (int s = 0; s < nsteps; s += 4) {
-      step(s, st0, st3);
-      if (s + 1 < nsteps) step(s + 1, st1, st0);
-      if (s + 2 < nsteps) step(s + 2, st2, st1);
-      if (s + 3 < nsteps) step(s + 3, st3, st2);
+#pragma unroll
+    for (int j = 0; j < NSTG - 1; ++j)
+      if (j < nsteps) issue(j, j);
+    for (int s = 0; s < nsteps; s += NSTG) {
+#pragma unroll
+      for (int j = 0; j < NSTG; ++j)
+        if (s + j < nsteps) step(s + j, st[j], (j + NSTG - 1) % NSTG);
     }
 
     // epilogue: SwiGLU + requant; one block of 32 = two 16-column subtiles of one row
@@ -962,7 +1018,7 @@ size_t ffn_ws_bytes(int T, int H, int E, int I, int k) {
   (void)E;
   size_t q, qs, h, o;
   ffn_ws_layout(T, H, I, k, &q, &qs, &h, &o);
-  return o + align256((size_t)T * k * H * 4) + 256;
+  return o + align256((size_t)T * k * H * 4) + 256;            // + the work-queue counters
 }
 
 // Row pairs at or below which the decode kernels are chosen.
@@ -983,6 +1039,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
   uint8_t* qsc = base + oqs;
   float* h = reinterpret_cast<float*>(base + oh);
   float* o = reinterpret_cast<float*>(base + oo);
+  int* queue = reinterpret_cast<int*>(base + oo + align256((size_t)Tk * a.H * 4));   // XCDS counters
   const int cus = num_cus();
   const int max_active = a.E < Tk ? a.E : Tk;
   if (path == 0) {
@@ -1034,11 +1091,12 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
   } else {
     const int gu_items = (Tk / GU_BM + max_active) * ((a.I + GU_ICOLS - 1) / GU_ICOLS);
     const int dn_items = max_active * (a.H / PF_NCOLS);
-    int gu_grid = gu_items < cus ? gu_items : cus;             // one 4-wavefront workgroup per CU
+    int gu_grid = gu_items < cus * GU_WG_PER_CU ? gu_items : cus * GU_WG_PER_CU;
     int dn_grid = dn_items < cus * 2 ? dn_items : cus * 2;
     gu_grid = (gu_grid + XCDS - 1) / XCDS * XCDS;
     dn_grid = (dn_grid + XCDS - 1) / XCDS * XCDS;
-    hipLaunchKernelGGL(gu_prefill_kernel, dim3(gu_grid), dim3(256), 0, stream, a, qws, qsc, Tk);
+    hipLaunchKernelGGL(clear_i32_kernel, dim3(1), dim3(64), 0, stream, queue, 64);
+    hipLaunchKernelGGL(gu_prefill_kernel<GU_STAGES>, dim3(gu_grid), dim3(256), 0, stream, a, qws, qsc, Tk, queue);
     if (a.I <= 2 * KSTEP) hipLaunchKernelGGL(down_prefill_kernel<2>, dim3(dn_grid), dim3(64 * DN_WAVES), 0, stream, a, qws, qsc, o, Tk);
     else hipLaunchKernelGGL(down_prefill_kernel<5>, dim3(dn_grid), dim3(64 * DN_WAVES), 0, stream, a, qws, qsc, o, Tk);
     *variant = "ffn:gu_prefill64+down_prefill64+combine";
