@@ -112,6 +112,7 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H, co
   if (H % 32 != 0 || I % 32 != 0) return MX_EINVAL;
   if (H % 128 != 0 || H > 128 * 8 * mx::MAX_PARTS || I > mx::MAX_I) return MX_EUNSUPPORTED;
   if ((int64_t)T * k >= (int64_t(1) << 31)) return MX_EINVAL;
+  if ((int64_t)T * H >= (int64_t(1) << 32)) return MX_EUNSUPPORTED;
   if (!x || !x_sc || !topk_w || !expert_offsets || !perm || !slot_pos || !w13 || !w13_sc || !w2 || !w2_sc || !y)
     return MX_EINVAL;
   if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(x_sc, 4) ||

@@ -123,7 +123,8 @@ mx_status moe_route(const float* logits, int T, int E, int k,
  *        rows with no live pair are +0.
  * Every product is accumulated in fp32 on the matrix cores in one fixed
  * order per output element, the same for every batch size and path.
- * Supported: H % 128 == 0, I % 32 == 0, 1 <= k <= 16, T*k < 2^31.
+ * Supported: H % 128 == 0, I % 32 == 0, 1 <= k <= 16, T*k < 2^31,
+ *            T*H < 2^32 (the activations fit 32-bit byte offsets).
  * ws: device scratch of at least moe_expert_ffn_workspace_bytes(T,H,E,I,k)
  *     bytes (256-byte aligned).  Its layout is documented for diagnostics
  *     and filled in by moe_ws_layout(): the FP8 intermediate q [T*k][I] and

@@ -106,6 +106,7 @@ def test_ffn_rejects_bad_arguments(lib):
     assert ffn(lib, ws=None) == mxmoe.MX_EWORKSPACE
     assert ffn(lib, ws_bytes=1000) == mxmoe.MX_EWORKSPACE
     assert ffn(lib, E=0) == mxmoe.MX_EINVAL
+    assert ffn(lib, T=1 << 20, H=4096, k=1) == mxmoe.MX_EUNSUPPORTED             # T*H >= 2^32
 
 
 def gemm(lib, M=1, N=64, K=256, ydt=0, a=FAKE):
