@@ -146,4 +146,9 @@ mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w
   return from_hip(e);
 }
 
+mx_status mx_check_requant(uint32_t lo, uint32_t hi, unsigned long long* mismatches, void* stream) {
+  if (!mismatches || !aligned(mismatches, 8) || lo > hi || hi > 0x7F800000u) return MX_EINVAL;
+  return from_hip(mx::launch_check_requant(lo, hi, mismatches, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
         if (r < nrows) {
           const int64_t p = p0 + r0 + r;
           const uint32_t sc = e8m0_code_for_amax(m, 8);
-          const uint32_t d = requant_e4m3(v0, sc) | (requant_e4m3(v1, sc) << 8);
+          const uint32_t d = requant2_e4m3(v0, v1, sc);
           *reinterpret_cast<uint16_t*>(qws + p * I + blk * 32 + c) = (uint16_t)d;
           if ((tid & 15) == 0) qsc_ws[p * nb + blk] = (uint8_t)sc;
           *reinterpret_cast<float2*>(h + p * 2 * I + blk * 32 + c) = gg;
@@ -837,8 +837,9 @@ __global__ __launch_bounds__(256, 4 / NSTG) void gu_prefill_kernel(FfnArgs a, ui
             const int cb = c0 + wn * 64 + blk * 32;           // first column of the block
             if (row < nrows && cb < I) {
               uint8_t* qrow = qws + (int64_t)(p0 + row) * I;
-              qrow[cb + col] = (uint8_t)requant_e4m3(v0, sc);
-              qrow[cb + 16 + col] = (uint8_t)requant_e4m3(v1, sc);
+              const uint32_t d = requant2_e4m3(v0, v1, sc);
+              qrow[cb + col] = (uint8_t)d;
+              qrow[cb + 16 + col] = (uint8_t)(d >> 8);
               if (col == 0) qsc_ws[(int64_t)(p0 + row) * nb + cb / 32] = (uint8_t)sc;
             }
           }

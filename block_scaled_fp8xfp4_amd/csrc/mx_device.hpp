@@ -131,9 +131,19 @@ __device__ __forceinline__ float row16_max(float m) {
   return m;
 }
 
-// E4M3 code of one element of a block whose shared scale code is sc (the
-// requant of the intermediate): identical in every kernel that uses it.
-__device__ __forceinline__ uint32_t requant_e4m3(float a, uint32_t sc) { return encode_e4m3(a, sc); }
+// E4M3 codes of two elements of a block whose shared scale code is sc (the
+// requant of the intermediate), first element in bits 0..7, second in 8..15:
+// identical in every kernel that uses it.  The value is scaled by 2^(127 - sc)
+// (exact), clamped to +-448 and converted by the hardware (round to nearest
+// even, OCP E4M3, subnormals kept).  Inputs are finite and the scaled value
+// is below 512 in magnitude (the scale comes from the block's amax); on that
+// whole domain this equals encode_e4m3 bit for bit, every float compared.
+__device__ __forceinline__ uint32_t requant2_e4m3(float a, float b, uint32_t sc) {
+  const int k = 127 - (int)sc;
+  const float ta = __builtin_amdgcn_fmed3f(__builtin_ldexpf(a, k), -448.0f, 448.0f);
+  const float tb = __builtin_amdgcn_fmed3f(__builtin_ldexpf(b, k), -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ta, tb, 0, false) & 0xFFFFu;
+}
 
 // Quantize 32 fp32 values to E4M3: writes 32 code bytes as 8 dwords, returns the scale code.
 __device__ __forceinline__ uint32_t quantize32_e4m3(const float* v, uint32_t* out8) {

@@ -37,5 +37,6 @@ hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_
                              int M, int N, int K, void* y, bool bf16_out, hipStream_t stream, const char** variant);
 
 int num_cus();
+hipError_t launch_check_requant(uint32_t lo, uint32_t hi, unsigned long long* nbad, hipStream_t stream);
 
 }  // namespace mx

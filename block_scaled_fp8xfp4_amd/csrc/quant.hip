@@ -72,4 +72,26 @@ hipError_t launch_quantize(const void* src, bool bf16, int64_t rows, int64_t col
   return hipGetLastError();
 }
 
+// Diagnostic: the finite floats whose magnitude bits lie in [lo, hi), with
+// both signs, through both E4M3 encoders of the intermediate: the hardware
+// conversion of requant2_e4m3 and the integer rounding of encode_e4m3 (scale
+// code 127: the value itself is encoded).  Mismatches are added to *nbad.
+__global__ __launch_bounds__(256) void check_requant_kernel(uint32_t lo, uint32_t hi, unsigned long long* nbad) {
+  unsigned long long bad = 0;
+  for (uint64_t i = lo + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < hi; i += (uint64_t)gridDim.x * blockDim.x) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float v = __uint_as_float((uint32_t)i | (s ? 0x80000000u : 0u));
+      bad += (requant2_e4m3(v, 0.0f, 127) & 0xFFu) != encode_e4m3(v, 127);
+    }
+  }
+  if (bad) atomicAdd(nbad, bad);
+}
+
+hipError_t launch_check_requant(uint32_t lo, uint32_t hi, unsigned long long* nbad, hipStream_t stream) {
+  if (lo >= hi) return hipSuccess;
+  hipLaunchKernelGGL(check_requant_kernel, dim3(2048), dim3(256), 0, stream, lo, hi, nbad);
+  return hipGetLastError();
+}
+
 }  // namespace mx

@@ -18,7 +18,7 @@ MX_OUT_BF16, MX_OUT_F32 = 0, 1
 # every entry point declared in include/mxmoe.h
 EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "moe_expert_ffn_workspace_bytes",
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
-           "mx_last_variant", "mx_set_ffn_path")
+           "mx_last_variant", "mx_set_ffn_path", "mx_check_requant")
 
 _lib = None
 
@@ -58,6 +58,8 @@ def load():
     lib.mx_last_variant.argtypes = []
     lib.mx_set_ffn_path.restype = I32
     lib.mx_set_ffn_path.argtypes = [I32]
+    lib.mx_check_requant.restype = I32
+    lib.mx_check_requant.argtypes = [ctypes.c_uint32, ctypes.c_uint32, P, P]
     _lib = lib
     return lib
 
@@ -139,3 +141,10 @@ def fp8_block_gemm(a, a_sc, w, w_sc, y, y_dtype, stream=None):
     N = w.shape[0]
     _check(load().fp8_block_gemm(_ptr(a), _ptr(a_sc), _ptr(w), _ptr(w_sc), M, N, K, _ptr(y), y_dtype,
                                  _stream(stream)), "fp8_block_gemm")
+
+
+def check_requant(lo, hi, mismatches, stream=None):
+    """Add to mismatches (int64 device tensor of one element) the number of
+    finite floats with magnitude bits in [lo, hi), both signs, whose E4M3 code
+    from the FFN's hardware conversion differs from the quantize encoder's."""
+    _check(load().mx_check_requant(lo, hi, _ptr(mismatches), _stream(stream)), "mx_check_requant")

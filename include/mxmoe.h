@@ -171,6 +171,19 @@ const char* mx_last_variant(void);
  */
 int mx_set_ffn_path(int path);
 
+/*
+ * Diagnostic for the intermediate requant (FP8 E4M3 under the block's E8M0
+ * scale, OCP MX v1.0 "Conversion"; post #6 "Why TileLang": FP8
+ * quantization): every finite float whose magnitude bit pattern lies in
+ * [lo, hi) is encoded with both signs by the hardware conversion the FFN
+ * kernels use (clamp to +-448, round to nearest even) and by the integer
+ * rounding encoder the quantize kernels use; the number of differing codes is
+ * added to *mismatches (device memory, 8-byte aligned, initialised by the
+ * caller).  hi <= 0x7F800000 (the finite floats).  Asynchronous on stream.
+ * MX_EINVAL for a null or misaligned counter or lo > hi.
+ */
+mx_status mx_check_requant(uint32_t lo, uint32_t hi, unsigned long long* mismatches, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -127,3 +127,10 @@ def test_path_switch(lib):
     assert mxmoe.set_ffn_path(old) == 1
     with pytest.raises(mxmoe.MXError):
         mxmoe.set_ffn_path(3)
+
+
+def test_check_requant_rejects_bad_arguments(lib):
+    assert lib.mx_check_requant(0, 16, None, None) == mxmoe.MX_EINVAL
+    assert lib.mx_check_requant(0, 16, ctypes.c_void_p((1 << 20) + 4), None) == mxmoe.MX_EINVAL   # alignment
+    assert lib.mx_check_requant(32, 16, FAKE, None) == mxmoe.MX_EINVAL                          # lo > hi
+    assert lib.mx_check_requant(0, 0x7F800001, FAKE, None) == mxmoe.MX_EINVAL                   # past the finite floats
