@@ -957,7 +957,7 @@ __global__ __launch_bounds__(64 * DN_WAVES, 2) void down_prefill_kernel(FfnArgs 
           if (row < nrows) {
             float* orow = o + (int64_t)(p0 + row) * H + n0 + col;
 #pragma unroll
-            for (int n = 0; n < 2; ++n) orow[n * 16] = acc[m][n][i];
+            for (int n = 0; n < 2; ++n) __builtin_nontemporal_store(acc[m][n][i], orow + n * 16);   // read once, by the combine
           }
         }
     }
@@ -967,7 +967,8 @@ __global__ __launch_bounds__(64 * DN_WAVES, 2) void down_prefill_kernel(FfnArgs 
 // ============================================================== combine ===
 // y_t = sum_j w_tj * o[slot_pos[t][j]], j = 0..k-1 in order; 4 columns per
 // thread.  Every slot's position, weight and output are requested before the
-// first add (a dead slot reads row 0 and is skipped by a select).
+// first add (a dead slot reads row 0 and is skipped by a select).  o is read
+// once and y written once: both bypass the caches' retention (nontemporal).
 template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const float* __restrict__ w,
                                                       const int32_t* __restrict__ slot_pos, int T, int H, int k, int Tk,
@@ -983,22 +984,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       p[j] = slot_pos[(int64_t)t * k + jj];
       wj[j] = w[(int64_t)t * k + jj];
     }
-    float4 v[KMAX];
+    v4f v[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const bool ok = j < k && p[j] >= 0 && p[j] < Tk;
-      v[j] = *reinterpret_cast<const float4*>(o + (int64_t)(ok ? p[j] : 0) * H + n);
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(o + (int64_t)(ok ? p[j] : 0) * H + n));
     }
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const bool ok = j < k && p[j] >= 0 && p[j] < Tk;
-      acc.x = ok ? fmaf(wj[j], v[j].x, acc.x) : acc.x;
-      acc.y = ok ? fmaf(wj[j], v[j].y, acc.y) : acc.y;
-      acc.z = ok ? fmaf(wj[j], v[j].z, acc.z) : acc.z;
-      acc.w = ok ? fmaf(wj[j], v[j].w, acc.w) : acc.w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = ok ? fmaf(wj[j], v[j][c], acc[c]) : acc[c];
     }
-    *reinterpret_cast<float4*>(y + (int64_t)t * H + n) = acc;
+    __builtin_nontemporal_store(acc, reinterpret_cast<v4f*>(y + (int64_t)t * H + n));
   }
 }
 
