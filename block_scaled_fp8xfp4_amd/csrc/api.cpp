@@ -151,4 +151,15 @@ mx_status mx_check_requant(uint32_t lo, uint32_t hi, unsigned long long* mismatc
   return from_hip(mx::launch_check_requant(lo, hi, mismatches, static_cast<hipStream_t>(stream)));
 }
 
+mx_status mx_set_phase_events(void* const* events, int n) {
+  if (n != 0 && n != 4) return MX_EINVAL;
+  if (n == 4)
+    for (int i = 0; i < 4; ++i)
+      if (!events || !events[i]) return MX_EINVAL;
+  hipEvent_t ev[4] = {};
+  for (int i = 0; i < n; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+  mx::set_ffn_phase_events(ev, n);
+  return MX_OK;
+}
+
 }  // extern "C"

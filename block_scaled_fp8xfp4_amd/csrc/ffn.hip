@@ -1030,6 +1030,17 @@ bool ffn_path_supported(int path, int H, int I) {
   return true;
 }
 
+// Diagnostic phase events of this thread's FFN calls (set_ffn_phase_events).
+static thread_local hipEvent_t g_phase_ev[4];
+static thread_local bool g_phase_on = false;
+void set_ffn_phase_events(const hipEvent_t* ev, int n) {
+  g_phase_on = n == 4;
+  for (int i = 0; i < 4; ++i) g_phase_ev[i] = g_phase_on ? ev[i] : nullptr;
+}
+static inline void phase(int i, hipStream_t stream) {
+  if (g_phase_on) (void)hipEventRecord(g_phase_ev[i], stream);
+}
+
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant) {
   const int Tk = a.T * a.k;
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -1046,6 +1057,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     const bool dec_ok = ffn_path_supported(1, a.H, a.I), pre_ok = ffn_path_supported(2, a.H, a.I);
     path = ((Tk <= DECODE_MAX_PAIRS && dec_ok) || !pre_ok) ? 1 : 2;
   }
+  phase(0, stream);
   if (path == 1) {
     const int R = a.T < DEC_ROWS ? a.T : DEC_ROWS;               // rows of one expert never exceed T
     const size_t lds = (size_t)R * (a.H + 16) + (size_t)R * (a.H / KSTEP) * 4;
@@ -1072,6 +1084,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       else MX_GU(32, false, false);
     }
 #undef MX_GU
+    phase(1, stream);
     if (a.T == 1) {
       const dim3 g1(a.H / 16), b1(256);
       if (is <= 2) hipLaunchKernelGGL(down_combine1_kernel<2>, g1, b1, 0, stream, a, qws, qsc, Tk);
@@ -1079,6 +1092,8 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       else if (is <= 8) hipLaunchKernelGGL(down_combine1_kernel<8>, g1, b1, 0, stream, a, qws, qsc, Tk);
       else hipLaunchKernelGGL(down_combine1_kernel<16>, g1, b1, 0, stream, a, qws, qsc, Tk);
       *variant = "ffn:gu_decode+down_combine1";
+      phase(2, stream);                                         // the down kernel also combines
+      phase(3, stream);
       return hipGetLastError();
     }
     const int dn_items = max_active * (a.H / 128);
@@ -1088,6 +1103,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     else if (is <= 8) hipLaunchKernelGGL(down_decode_kernel<8>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
     else hipLaunchKernelGGL(down_decode_kernel<16>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
     *variant = "ffn:gu_decode+down_decode+combine";
+    phase(2, stream);
   } else {
     const int gu_items = (Tk / GU_BM + max_active) * ((a.I + GU_ICOLS - 1) / GU_ICOLS);
     const int dn_items = max_active * (a.H / PF_NCOLS);
@@ -1097,13 +1113,16 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     dn_grid = (dn_grid + XCDS - 1) / XCDS * XCDS;
     hipLaunchKernelGGL(clear_i32_kernel, dim3(1), dim3(64), 0, stream, queue, 64);
     hipLaunchKernelGGL(gu_prefill_kernel<GU_STAGES>, dim3(gu_grid), dim3(256), 0, stream, a, qws, qsc, Tk, queue);
+    phase(1, stream);
     if (a.I <= 2 * KSTEP) hipLaunchKernelGGL(down_prefill_kernel<2>, dim3(dn_grid), dim3(64 * DN_WAVES), 0, stream, a, qws, qsc, o, Tk);
     else hipLaunchKernelGGL(down_prefill_kernel<5>, dim3(dn_grid), dim3(64 * DN_WAVES), 0, stream, a, qws, qsc, o, Tk);
     *variant = "ffn:gu_prefill64+down_prefill64+combine";
+    phase(2, stream);
   }
   const dim3 cgrid((a.H / 4 + 255) / 256, a.T < 65535 ? a.T : 65535);
   if (a.k <= 8) hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(256), 0, stream, o, a.topk_w, a.slot_pos, a.T, a.H, a.k, Tk, a.y);
   else hipLaunchKernelGGL(combine_kernel<MAX_K>, cgrid, dim3(256), 0, stream, o, a.topk_w, a.slot_pos, a.T, a.H, a.k, Tk, a.y);
+  phase(3, stream);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, 
 // path: 0 automatic, 1 decode kernels, 2 prefill kernels
 bool ffn_path_supported(int path, int H, int I);
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant);
+void set_ffn_phase_events(const hipEvent_t* ev, int n);
 
 hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,
                              int M, int N, int K, void* y, bool bf16_out, hipStream_t stream, const char** variant);

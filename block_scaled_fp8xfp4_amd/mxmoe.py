@@ -18,7 +18,7 @@ MX_OUT_BF16, MX_OUT_F32 = 0, 1
 # every entry point declared in include/mxmoe.h
 EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "moe_expert_ffn_workspace_bytes",
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
-           "mx_last_variant", "mx_set_ffn_path", "mx_check_requant")
+           "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events")
 
 _lib = None
 
@@ -60,6 +60,8 @@ def load():
     lib.mx_set_ffn_path.argtypes = [I32]
     lib.mx_check_requant.restype = I32
     lib.mx_check_requant.argtypes = [ctypes.c_uint32, ctypes.c_uint32, P, P]
+    lib.mx_set_phase_events.restype = I32
+    lib.mx_set_phase_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
     _lib = lib
     return lib
 
@@ -148,3 +150,17 @@ def check_requant(lo, hi, mismatches, stream=None):
     finite floats with magnitude bits in [lo, hi), both signs, whose E4M3 code
     from the FFN's hardware conversion differs from the quantize encoder's."""
     _check(load().mx_check_requant(lo, hi, _ptr(mismatches), _stream(stream)), "mx_check_requant")
+
+
+def set_phase_events(events):
+    """Record torch.cuda.Event objects (4, created with enable_timing=True) at
+    the phase boundaries of this thread's later moe_expert_ffn calls: before
+    the first kernel, after gate/up, after the down projection, after the last
+    kernel.  None stops the recording."""
+    if events is None:
+        _check(load().mx_set_phase_events(None, 0), "mx_set_phase_events")
+        return
+    for e in events:
+        e.record()                                   # materialise the HIP event handle
+    arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    _check(load().mx_set_phase_events(arr, 4), "mx_set_phase_events")

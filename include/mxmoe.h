@@ -184,6 +184,18 @@ int mx_set_ffn_path(int path);
  */
 mx_status mx_check_requant(uint32_t lo, uint32_t hi, unsigned long long* mismatches, void* stream);
 
+/*
+ * Diagnostic timing of moe_expert_ffn's phases (for benchmarks: a call's
+ * kernels cannot be bracketed from outside it).  With n = 4 caller-owned
+ * hipEvent_t handles set, every later moe_expert_ffn call of this thread
+ * records, on the call's stream, events[0] before its first kernel,
+ * events[1] after the gate/up kernel, events[2] after the down projection
+ * and events[3] after its last kernel (on the single-row path the down kernel
+ * also combines, so events[2] and events[3] are recorded together).  n = 0
+ * stops the recording.  MX_EINVAL for another n or a null handle.
+ */
+mx_status mx_set_phase_events(void* const* events, int n);
+
 #ifdef __cplusplus
 }
 #endif

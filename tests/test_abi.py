@@ -134,3 +134,9 @@ def test_check_requant_rejects_bad_arguments(lib):
     assert lib.mx_check_requant(0, 16, ctypes.c_void_p((1 << 20) + 4), None) == mxmoe.MX_EINVAL   # alignment
     assert lib.mx_check_requant(32, 16, FAKE, None) == mxmoe.MX_EINVAL                          # lo > hi
     assert lib.mx_check_requant(0, 0x7F800001, FAKE, None) == mxmoe.MX_EINVAL                   # past the finite floats
+
+
+def test_phase_events_reject_bad_arguments(lib):
+    assert lib.mx_set_phase_events(None, 3) == mxmoe.MX_EINVAL
+    assert lib.mx_set_phase_events(None, 4) == mxmoe.MX_EINVAL
+    assert lib.mx_set_phase_events(None, 0) == mxmoe.MX_OK
