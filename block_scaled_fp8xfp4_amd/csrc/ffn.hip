@@ -45,7 +45,7 @@ constexpr int DEC_MAX_STEPS = 32;                 // decode gate/up: H <= 4096 h
 constexpr int DOWN_MAX_STEPS = MAX_I / KSTEP;     // 16
 constexpr int PF_ROWS = 64;                       // prefill expert tile rows
 constexpr int PF_NCOLS = 256;                     // prefill down: W2 rows per workgroup
-constexpr int PF_MAX_I = 640;                     // prefill down: intermediate held in LDS (5 steps)
+constexpr int PF_MAX_I = 608;                     // prefill down: W2 slice of 256 rows x (I/32 + 1) chunks in LDS
 constexpr int XCDS = 8;
 
 // ---------------------------------------------------------------- work lists
@@ -186,6 +186,22 @@ __device__ __forceinline__ int queue_next(int* ctr, int n, int& q) {
     ++q;
   }
   return -1;
+}
+
+// The same in two halves, so that the counter's round trip overlaps other
+// work: queue_take() starts the increment of the current range's counter,
+// queue_finish() turns its result into an item (walking on synchronously when
+// that range is drained).
+__device__ __forceinline__ int queue_take(int* ctr, int q) {
+  return q < XCDS ? atomicAdd(&ctr[(blockIdx.x % XCDS + q) % XCDS], 1) : 0;
+}
+__device__ __forceinline__ int queue_finish(int* ctr, int n, int& q, int c) {
+  if (q >= XCDS) return -1;
+  const int x = (blockIdx.x % XCDS + q) % XCDS;
+  const int lo = (int)((int64_t)n * x / XCDS), hi = (int)((int64_t)n * (x + 1) / XCDS);
+  if (c < hi - lo) return lo + c;
+  ++q;
+  return queue_next(ctr, n, q);
 }
 
 __global__ void clear_i32_kernel(int* p, int n) {
@@ -849,119 +865,227 @@ __global__ __launch_bounds__(256, 4 / NSTG) void gu_prefill_kernel(FfnArgs a, ui
   }
 }
 
-// Down, weight-stationary: one workgroup of eight wavefronts per (expert, 256
-// W2 rows); each wavefront keeps its 32 W2 rows (two 16-row B tiles, whole
-// K = I, NS steps) in registers and walks all of the expert's 64-row tiles.  A tile's
-// intermediate rows (contiguous bucket rows) go global -> LDS by LDS DMA, one
-// instruction per row (I / 16 lanes); their scale bytes through registers.
-// Each W2 byte is read once per workgroup instead of once per row tile.
+// Down, weight-stationary, one workgroup of eight wavefronts per CU taking
+// (expert, 256 W2 rows) items from the work queue: each wavefront keeps its
+// 32 W2 rows (two 16-row B tiles, whole K = I) in registers and walks all of
+// the expert's 32-row tiles.  Every global -> LDS transfer is an LDS DMA
+// issued well ahead of its use, and the kernel counts them itself (vmcnt):
+//  - the next tile's intermediate rows and scale bytes (this tile's MFMAs
+//    read the other of two buffers);
+//  - the next item's W2 slice (rows and scales, into one LDS buffer, read
+//    into registers at the item's first tile), requested at this item's first
+//    tile: the queue runs two items ahead, so the next item is known.
+// Results leave through a per-wavefront LDS transpose, 8 rows x 128 bytes per
+// store; every wavefront issues the same number of memory instructions per
+// tile (rows past the tile go to a scratch row of the workspace), so the
+// counts are exact.
 constexpr int DN_WAVES = 8;
+constexpr int DN_NT = 64 * DN_WAVES;
+constexpr int DN_ROWS_T = 32;                     // intermediate rows per tile
+constexpr int DN_NCOLS = 256;                     // W2 rows per item
+constexpr int DN_QPITCH = 5 * KSTEP + 16;         // LDS pitch of an intermediate row (K past I zero)
+constexpr int DN_TPITCH = 36;                     // transpose rows: 32 floats + 4 (bank spread)
+constexpr int DN_W2_DMA = 10;                     // W2 row DMAs per wavefront per item (256 rows x <= 20 chunks)
+constexpr int DN_W2S_DMA = 3;                     // W2 scale dword DMAs per wavefront per item
+constexpr int DN_TILE_DMA = DN_ROWS_T / DN_WAVES + 1;   // per tile: 4 rows + 1 scale dword DMA
+constexpr int DN_TILE_ST = 4;                     // per tile: stores (2 subtiles x 2 halves)
+struct DnLds {
+  uint8_t q[2][DN_ROWS_T][DN_QPITCH];             // intermediate rows, two buffers
+  uint8_t qs[2][DN_WAVES * 256];                  // their scale bytes (DMA'd as dwords; waves 3.. fill slack)
+  u32x4 w2[DN_WAVES * DN_W2_DMA * 64];            // W2 slice: row r, 16-byte chunk c at r * (nb + 1) + c
+  uint32_t w2s[DN_WAVES * DN_W2S_DMA * 64];       // its scale bytes, row-major [256][nb]
+  float tr[DN_WAVES][16][DN_TPITCH];
+};
+
 template <int NS>
-__global__ __launch_bounds__(64 * DN_WAVES, 2) void down_prefill_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
-                                                              const uint8_t* __restrict__ qsc_ws,
-                                                              float* __restrict__ o, int Tk) {
-  constexpr int NT = 64 * DN_WAVES;
-  constexpr int SPT = (PF_ROWS * NS * 4 + NT - 1) / NT;         // scale bytes per thread
+__global__ __launch_bounds__(DN_NT, 1) void down_prefill_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
+                                                                const uint8_t* __restrict__ qsc_ws,
+                                                                float* __restrict__ o, float* __restrict__ junk, int Tk,
+                                                                int* __restrict__ queue) {
   __shared__ int tile_start[MAX_E + 1];
-  __shared__ int offs[MAX_E + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t qlds[PF_ROWS][PF_MAX_I + 16];
-  __shared__ uint8_t slds[PF_ROWS][PF_MAX_I / 32 + 4];
-  for (int i = threadIdx.x; i <= a.E; i += blockDim.x) offs[i] = a.offsets[i];   // published by build_tiles' barrier
+  __shared__ int s_slot[2];
+  __shared__ __attribute__((aligned(16))) DnLds L;
   build_tiles(a.offsets, a.E, 0, tile_start);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
-  const int H = a.H, I = a.I, nb = I / 32;
+  const int H = a.H, I = a.I, nb = I / 32, nch = nb + 1;        // W2 row: nb 16-byte chunks + 1 pad
   const int nsteps = (I + KSTEP - 1) / KSTEP;                   // <= NS
-  const int q16 = I / 16;                                       // <= 40 lanes per row
-  const int nnt = H / PF_NCOLS;
+  const int q16 = I / 16;
+  const int nnt = H / DN_NCOLS;
   const int nitems = tile_start[a.E] * nnt;
-  // K past I reads zeros: the row tails are cleared once, staging never writes them
-  for (int idx = tid; idx < PF_ROWS * (NS * KSTEP - I); idx += NT)
-    qlds[idx / (NS * KSTEP - I)][I + idx % (NS * KSTEP - I)] = 0;
-  for (int idx = tid; idx < PF_ROWS * (NS * 4 - nb); idx += NT)
-    slds[idx / (NS * 4 - nb)][nb + idx % (NS * 4 - nb)] = 127;
-
-  for (int round = 0;; ++round) {
-    const int item = xcd_item(round, blockIdx.x, gridDim.x);
-    if (item >= nitems) break;
-    const int nt = item % nnt;
-    const int e = tile_expert(tile_start, a.E, item / nnt);
-    const int pbeg = offs[e];
-    int cnt = offs[e + 1] - pbeg;
-    if (pbeg < 0 || pbeg + cnt > Tk) cnt = 0;
-    const int n0 = nt * PF_NCOLS + wave * 32;
-    u32x4 bw[2][NS];
-    uint32_t bs[2][NS];
-    for (int r0 = 0; r0 < cnt; r0 += PF_ROWS) {
-      const int p0 = pbeg + r0;
-      const int nrows = min(PF_ROWS, cnt - r0);
-      lds_barrier();                                            // previous tile's LDS reads are done
-      // the tile's intermediate: wavefront w fills rows w, w + 8, ... (rows
-      // past nrows repeat the tile's last row; their results are discarded)
-#pragma unroll
-      for (int i = 0; i < PF_ROWS / DN_WAVES; ++i) {
-        const int r = wave + DN_WAVES * i;
-        if (lane < q16) dma16_to_lds(qws + (int64_t)(p0 + min(r, nrows - 1)) * I + lane * 16, &qlds[r][0]);
-      }
-      uint32_t sv[SPT];
-#pragma unroll
-      for (int i = 0; i < SPT; ++i) {
-        const int idx = min(tid + NT * i, PF_ROWS * nb - 1);
-        const int r = min(idx / nb, nrows - 1), b = idx % nb;
-        sv[i] = qsc_ws[(int64_t)(p0 + r) * nb + b];
-      }
-      if (r0 == 0) {
-        // first tile: this wavefront's W2 rows, requested after the tile's rows
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          load_w2_tile<NS>(a.w2, a.w2_sc, (int64_t)e * H + n0 + n * 16 + col, I, g, bw[n], bs[n]);
-      }
-#pragma unroll
-      for (int i = 0; i < SPT; ++i) {
-        const int idx = tid + NT * i;
-        if (idx < PF_ROWS * nb) slds[idx / nb][idx % nb] = (uint8_t)sv[i];
-      }
-      if (r0 == 0) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(4 * NS) : "memory");   // DMA done, W2 may be in flight
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      lds_barrier();
-
-      v4f acc[4][2];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (s < nsteps) {
-          const int klo = s * KSTEP + g * 16;
-          const bool bv = 4 * s + g < nb;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int r = m * 16 + col;
-            const v8i av = fp8_operand(*reinterpret_cast<const u32x4*>(&qlds[r][klo]),
-                                       *reinterpret_cast<const u32x4*>(&qlds[r][klo + 64]));
-            const uint32_t sa = slds[r][4 * s + g];
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-              acc[m][n] = mfma_fp8_fp4(av, fp4_operand_masked(bw[n][s], bv), acc[m][n], sa, bs[n][s]);
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + 4 * g + i;
-          if (row < nrows) {
-            float* orow = o + (int64_t)(p0 + row) * H + n0 + col;
-#pragma unroll
-            for (int n = 0; n < 2; ++n) __builtin_nontemporal_store(acc[m][n][i], orow + n * 16);   // read once, by the combine
-          }
-        }
-    }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(&L));
+  // K past I of the intermediate rows reads zeros: staging never writes there
+  for (int idx = tid; idx < 2 * DN_ROWS_T * (NS * KSTEP - I); idx += DN_NT) {
+    const int bf = idx / (DN_ROWS_T * (NS * KSTEP - I)), rem = idx % (DN_ROWS_T * (NS * KSTEP - I));
+    L.q[bf][rem / (NS * KSTEP - I)][I + rem % (NS * KSTEP - I)] = 0;
   }
+
+  struct Item { int e, pbeg, cnt, ntiles, nt; };
+  auto describe = [&](int item) {
+    Item it;
+    it.e = __builtin_amdgcn_readfirstlane(tile_expert(tile_start, a.E, item / nnt));
+    it.pbeg = a.offsets[it.e];
+    it.cnt = a.offsets[it.e + 1] - it.pbeg;
+    if (it.pbeg < 0 || it.pbeg + it.cnt > Tk) it.cnt = 0;
+    it.ntiles = (it.cnt + DN_ROWS_T - 1) / DN_ROWS_T;
+    it.nt = item % nnt;
+    return it;
+  };
+  // one tile's rows and scale bytes into buffer bf: 4 row DMAs and one scale
+  // DMA per wavefront (rows past the tile repeat its last row; waves past the
+  // tile's scale dwords load a valid dword into slack)
+  auto stage = [&](const Item& it, int t, int bf) {
+    const int p0 = min(it.pbeg + t * DN_ROWS_T, Tk - 1);
+    const int nrows = max(1, min(DN_ROWS_T, it.cnt - t * DN_ROWS_T));   // (an item without rows stages row p0)
+#pragma unroll
+    for (int i = 0; i < DN_ROWS_T / DN_WAVES; ++i) {
+      const int r = wave + DN_WAVES * i;
+      if (lane < q16)
+        dma16_to_lds(qws, (uint32_t)(min(p0 + min(r, nrows - 1), Tk - 1) * I + lane * 16),
+                     lds0 + (uint32_t)offsetof(DnLds, q) + (bf * DN_ROWS_T + r) * DN_QPITCH);
+    }
+    const uint32_t sb = (uint32_t)p0 * nb & ~3u;               // first scale dword of the tile
+    const uint32_t ndw = ((uint32_t)(p0 * nb & 3) + DN_ROWS_T * nb + 3) / 4;
+    const uint32_t d = wave * 64 + lane;
+    dma4_to_lds(qsc_ws, sb + 4 * (d < ndw ? d : 0), lds0 + (uint32_t)offsetof(DnLds, qs) + bf * DN_WAVES * 256 + wave * 256);
+  };
+  // the item's W2 slice: rows [nt * 256, nt * 256 + 256) of expert e
+  auto stage_w2 = [&](const Item& it) {
+    const uint8_t* w2e = a.w2 + (int64_t)it.e * H * (I / 2) + (int64_t)it.nt * DN_NCOLS * (I / 2);
+#pragma unroll
+    for (int i = 0; i < DN_W2_DMA; ++i) {
+      const int slot = (wave * DN_W2_DMA + i) * 64 + lane;       // 16-byte slot of the LDS slice
+      const int r = slot / nch, c = slot % nch;
+      const bool ok = r < DN_NCOLS && c < nb;
+      dma16_to_lds(w2e, ok ? (uint32_t)(r * (I / 2) + c * 16) : 0u,
+                   lds0 + (uint32_t)offsetof(DnLds, w2) + (wave * DN_W2_DMA + i) * 1024);
+    }
+    const uint8_t* w2se = a.w2_sc + ((int64_t)it.e * H + (int64_t)it.nt * DN_NCOLS) * nb;
+#pragma unroll
+    for (int i = 0; i < DN_W2S_DMA; ++i) {
+      const int dw = (wave * DN_W2S_DMA + i) * 64 + lane;
+      dma4_to_lds(w2se, dw < DN_NCOLS * nb / 4 ? 4u * dw : 0u,
+                  lds0 + (uint32_t)offsetof(DnLds, w2s) + (wave * DN_W2S_DMA + i) * 256);
+    }
+  };
+
+  // the workgroup's items, two ahead: its k-th item sits in s_slot[k & 1]
+  int qpos = 0;                                                 // queue position (thread 0)
+  if (tid == 0) {
+    const int i0 = queue_next(queue, nitems, qpos);
+    s_slot[0] = i0;
+    s_slot[1] = i0 < 0 ? -1 : queue_next(queue, nitems, qpos);
+  }
+  lds_barrier();
+  int cur = __builtin_amdgcn_readfirstlane(s_slot[0]);
+  if (cur < 0) return;
+  Item C = describe(cur);
+  stage_w2(C);
+  if (C.ntiles > 0) stage(C, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  u32x4 bw[2][NS];
+  uint32_t bs[2][NS];
+  int buf = 0;
+  for (int k = 0;; ++k) {
+    const int n0 = C.nt * DN_NCOLS + wave * 32;                 // this wavefront's first W2 row (= output column)
+    int raw = 0;
+    int nxt = -1;
+    Item N = C;
+    const int ntl = C.ntiles > 0 ? C.ntiles : 1;                // an item without rows only passes the queue on
+    for (int t = 0; t < ntl; ++t) {
+      const bool last = t + 1 == ntl;
+      lds_barrier();                                            // tile t (and at t = 0 the W2 slice) in LDS
+      if (t == 0) {
+        // the next item (published at the previous item's last tile, before this barrier)
+        nxt = __builtin_amdgcn_readfirstlane(s_slot[(k + 1) & 1]);
+        N = describe(nxt < 0 ? cur : nxt);
+        if (tid == 0) raw = queue_take(queue, qpos);           // item k + 2; consumed after the last tile
+        // this wavefront's W2 rows into registers, then the slice is free
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int r = wave * 32 + n * 16 + col;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const int c = 4 * s + g;
+            const u32x4 v = L.w2[r * nch + (c < nb ? c : 0)];
+            bw[n][s] = c < nb ? v : u32x4{0u, 0u, 0u, 0u};      // K past I multiplies zeros
+            bs[n][s] = reinterpret_cast<const uint8_t*>(L.w2s)[r * nb + (c < nb ? c : 0)];
+          }
+        }
+        lds_barrier();
+        // next: the following tile (or the next item's first), then the next item's W2
+        if (!last) stage(C, t + 1, buf ^ 1);
+        else stage(N, 0, buf ^ 1);
+        stage_w2(N);
+      } else {
+        if (!last) stage(C, t + 1, buf ^ 1);
+        else stage(N, 0, buf ^ 1);
+      }
+
+      if (C.ntiles > 0) {
+        const int p0 = C.pbeg + t * DN_ROWS_T, nrows = min(DN_ROWS_T, C.cnt - t * DN_ROWS_T);
+        const uint8_t* qsb = L.qs[buf] + ((uint32_t)p0 * nb & 3u);
+        v4f acc[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          if (s < nsteps) {
+            const int klo = s * KSTEP + g * 16, c = 4 * s + g;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const int r = m * 16 + col;
+              const v8i av = fp8_operand(*reinterpret_cast<const u32x4*>(&L.q[buf][r][klo]),
+                                         *reinterpret_cast<const u32x4*>(&L.q[buf][r][klo + 64]));
+              const uint32_t sa = c < nb ? (uint32_t)qsb[r * nb + c] : 127u;
+#pragma unroll
+              for (int n = 0; n < 2; ++n)
+                acc[m][n] = mfma_fp8_fp4(av, fp4_operand(bw[n][s]), acc[m][n], sa, bs[n][s]);
+            }
+          }
+        }
+        // results: 16 rows x 32 columns per subtile through the transpose,
+        // 8 rows x 128 bytes per store (rows past the tile: the scratch row)
+        float(*Tt)[DN_TPITCH] = L.tr[wave];
+        const int rr = lane >> 3, c4 = (lane & 7) * 4;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) Tt[4 * g + i][n * 16 + col] = acc[m][n][i];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int row = m * 16 + h * 8 + rr;
+            const v4f v = *reinterpret_cast<const v4f*>(&Tt[h * 8 + rr][c4]);
+            float* dst = row < nrows ? o + (int64_t)(p0 + row) * H + n0 + c4 : junk + c4;
+            __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(dst));   // read once, by the combine
+          }
+        }
+      } else {
+        // keep the per-tile store count: four stores to the scratch row
+#pragma unroll
+        for (int i = 0; i < DN_TILE_ST; ++i)
+          __builtin_nontemporal_store(v4f{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<v4f*>(junk + (lane & 7) * 4));
+      }
+      if (last && tid == 0) s_slot[k & 1] = queue_finish(queue, nitems, qpos, raw);
+      // the next tile's DMAs have landed once at most the newer operations
+      // (the W2 slice at t = 0, then this tile's stores) are outstanding
+      // (at an item's only tile the next W2 slice must have landed as well)
+      if (t == 0 && !last) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(DN_W2_DMA + DN_W2S_DMA + DN_TILE_ST) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(DN_TILE_ST) : "memory");
+      buf ^= 1;
+    }
+    if (nxt < 0) break;
+    cur = nxt;
+    C = N;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ============================================================== combine ===
@@ -1018,7 +1142,7 @@ size_t ffn_ws_bytes(int T, int H, int E, int I, int k) {
   (void)E;
   size_t q, qs, h, o;
   ffn_ws_layout(T, H, I, k, &q, &qs, &h, &o);
-  return o + align256((size_t)T * k * H * 4) + 256;            // + the work-queue counters
+  return o + align256((size_t)T * k * H * 4) + 256 + 256;      // + the work-queue counters + a scratch row (64 floats)
 }
 
 // Row pairs at or below which the decode kernels are chosen.
@@ -1050,7 +1174,8 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
   uint8_t* qsc = base + oqs;
   float* h = reinterpret_cast<float*>(base + oh);
   float* o = reinterpret_cast<float*>(base + oo);
-  int* queue = reinterpret_cast<int*>(base + oo + align256((size_t)Tk * a.H * 4));   // XCDS counters
+  int* queue = reinterpret_cast<int*>(base + oo + align256((size_t)Tk * a.H * 4));   // work-queue counters
+  float* junk = reinterpret_cast<float*>(base + oo + align256((size_t)Tk * a.H * 4) + 256);   // scratch row
   const int cus = num_cus();
   const int max_active = a.E < Tk ? a.E : Tk;
   if (path == 0) {
@@ -1106,16 +1231,18 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     phase(2, stream);
   } else {
     const int gu_items = (Tk / GU_BM + max_active) * ((a.I + GU_ICOLS - 1) / GU_ICOLS);
-    const int dn_items = max_active * (a.H / PF_NCOLS);
+    const int dn_items = max_active * (a.H / DN_NCOLS);
     int gu_grid = gu_items < cus * GU_WG_PER_CU ? gu_items : cus * GU_WG_PER_CU;
-    int dn_grid = dn_items < cus * 2 ? dn_items : cus * 2;
+    int dn_grid = dn_items < cus ? dn_items : cus;             // one 8-wavefront workgroup per CU
     gu_grid = (gu_grid + XCDS - 1) / XCDS * XCDS;
     dn_grid = (dn_grid + XCDS - 1) / XCDS * XCDS;
     hipLaunchKernelGGL(clear_i32_kernel, dim3(1), dim3(64), 0, stream, queue, 64);
     hipLaunchKernelGGL(gu_prefill_kernel<GU_STAGES>, dim3(gu_grid), dim3(256), 0, stream, a, qws, qsc, Tk, queue);
     phase(1, stream);
-    if (a.I <= 2 * KSTEP) hipLaunchKernelGGL(down_prefill_kernel<2>, dim3(dn_grid), dim3(64 * DN_WAVES), 0, stream, a, qws, qsc, o, Tk);
-    else hipLaunchKernelGGL(down_prefill_kernel<5>, dim3(dn_grid), dim3(64 * DN_WAVES), 0, stream, a, qws, qsc, o, Tk);
+    if (a.I <= 2 * KSTEP)
+      hipLaunchKernelGGL(down_prefill_kernel<2>, dim3(dn_grid), dim3(DN_NT), 0, stream, a, qws, qsc, o, junk, Tk, queue + 32);
+    else
+      hipLaunchKernelGGL(down_prefill_kernel<5>, dim3(dn_grid), dim3(DN_NT), 0, stream, a, qws, qsc, o, junk, Tk, queue + 32);
     *variant = "ffn:gu_prefill64+down_prefill64+combine";
     phase(2, stream);
   }
