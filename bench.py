@@ -225,6 +225,34 @@ def main():
         })
         return inp, touched
 
+    # ------------------------------------------------------------ dense FP8 GEMM at prefill size
+    def run_dense_prefill(M, steps, warmup):
+        """fp8_block_gemm with the chunk's rows (M = T) through the dense 4096 x 4096
+        projection: synthetic N(0,1) activations, the dense config's weights, bf16 out."""
+        d = synth.dense_inputs()
+        _, wq, wsc = dense_layer(synth.DENSE)
+        K, N = d.cfg.K, d.cfg.N
+        g = torch.Generator(device="cpu").manual_seed(5)
+        a = torch.randn((M, K), generator=g).to(dev).to(torch.bfloat16)
+        aq, asc = quantize(a, mxmoe.MX_FMT_E4M3)
+        del a
+        yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        copies = [(wq, wsc), (wq.clone(), wsc.clone())]
+        for i in range(warmup):
+            mxmoe.fp8_block_gemm(aq, asc, *copies[i % 2], yd, mxmoe.MX_OUT_BF16)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            mxmoe.fp8_block_gemm(aq, asc, *copies[i % 2], yd, mxmoe.MX_OUT_BF16)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flop = 2 * M * N * K
+        return dict(M=M, N=N, K=K, ms=round(ms, 4), tflops=round(flop / (ms * 1e-3) / 1e12, 2),
+                    pct_fp8_peak=round(100 * flop / (ms * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 2),
+                    variant=mxmoe.last_variant())
+
     # ------------------------------------------------------------ prefill
     def run_prefill(steps, warmup):
         cfg = synth.PREFILL
@@ -259,7 +287,9 @@ def main():
         flop = flop_gu + flop_dn
         tf = lambda f, ms: f / (ms * 1e-3) / 1e12
         combine_bytes = P * H * 4 + T * H * 4 + T * k * 8
+        dense = run_dense_prefill(T, steps, warmup)
         return dict(tflops=round(tf(flop, ffn_ms), 2), pct_fp8_peak=round(100 * tf(flop, ffn_ms) / MFMA_FP8_PEAK_TFLOPS, 2),
+                    dense_gemm=dense,
                     expert_gemms_tflops=round(tf(flop, gu_ms + dn_ms), 2),
                     expert_gemms_pct_fp8_peak=round(100 * tf(flop, gu_ms + dn_ms) / MFMA_FP8_PEAK_TFLOPS, 2),
                     expert_gemms_pct_fp4_peak=round(100 * tf(flop, gu_ms + dn_ms) / MFMA_FP4_PEAK_TFLOPS, 2),
@@ -282,6 +312,7 @@ def main():
             "phases": {k: pre[k] for k in ("gate_up_ms", "gate_up_tflops", "down_ms", "down_tflops", "combine_ms",
                                            "combine_gbs", "expert_gemms_tflops", "expert_gemms_pct_fp8_peak",
                                            "expert_gemms_pct_fp4_peak", "ffn_ms")},
+            "dense_gemm": pre["dense_gemm"],
             "config": {"workload": "prefill MoE chunk: T=8192, H=4096, E=256, top-8, I=576, MXFP4 experts, "
                                    "FP8 block-32 activations", "pairs": pre["pairs"]},
         })

@@ -20,6 +20,9 @@
 
 namespace mx {
 
+constexpr int XCDS_GEMM = 8;                      // XCDs of an MI355X (block scheduling)
+constexpr int GEMM_PREFILL_MIN_M = 256;            // rows from which the tiled prefill kernel runs
+
 __device__ __forceinline__ v8i fp8_pair(const u32x4& lo, const u32x4& hi) {
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
@@ -113,8 +116,169 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint8_t* __restr
   }
 }
 
+// Dense block-32 FP8 GEMM, prefill shapes (many rows): 128 x 128 output
+// tiles, two 4-wavefront workgroups per CU, each wavefront 64 x 64.  Per
+// MFMA step (K = 128) the tile's activation rows (16 KB), weight rows (16 KB)
+// and their scale dwords go global -> LDS by LDS DMA into one of two
+// XOR-swizzled buffers, one step ahead of the matrix cores, ordered by
+// explicit vmcnt waits and LDS-only barriers.  The canonical order is kept:
+// each part of 8 steps is a chain from zero, added to the running total in
+// part order, so every element equals the decode kernel's bit for bit.
+// Tiles are handed out in 8 x 8 blocks, one block per XCD per round, so that a
+// block's 8 activation panels and 8 weight panels are shared in that XCD's
+// L2 while its 64 workgroups move through K together.
+constexpr int GP_BM = 128, GP_BN = 128;
+constexpr int GP_DMA = 9;                         // per wavefront per step: 4 A + 4 B chunk DMAs + 1 scale DMA
+__device__ __forceinline__ int gp_phys(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }   // 16-byte chunk
+struct GpStage {
+  u32x4 a[GP_BM * 8];                             // [row][8 chunks] swizzled
+  u32x4 b[GP_BN * 8];
+  uint32_t as[GP_BM];                             // the step's 4 scale bytes per row
+  uint32_t bs[GP_BN];
+};
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
+                                                              const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sc,
+                                                              int M, int N, int K, void* __restrict__ y) {
+  __shared__ GpStage st[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nsteps = K / KSTEP;
+  const int nrt = (M + GP_BM - 1) / GP_BM, nct = (N + GP_BN - 1) / GP_BN;
+  const int nsbr = (nrt + 7) / 8, nsbc = (nct + 7) / 8;
+  const uint32_t st_lds = __builtin_amdgcn_readfirstlane(lds_addr(&st[0]));
+  const int per_xcd = gridDim.x / XCDS_GEMM;                    // workgroups per XCD (<= 64)
+  const int x = blockIdx.x % XCDS_GEMM, j = blockIdx.x / XCDS_GEMM;
+  const int al0 = gp_phys(col, g), al1 = gp_phys(col, 4 + g);
+
+  for (int sb = x; sb < nsbr * nsbc; sb += XCDS_GEMM) {
+    for (int tj = j; tj < 64; tj += per_xcd) {
+      const int rt = (sb / nsbc) * 8 + tj / 8, ct = (sb % nsbc) * 8 + tj % 8;
+      if (rt >= nrt || ct >= nct) continue;                     // workgroup-uniform
+      const int m0 = rt * GP_BM, n0 = ct * GP_BN;
+      lds_barrier();                                            // the previous tile's LDS reads are done
+      // this thread's slots: rows past M / N repeat the last row (results discarded)
+      uint32_t aoff[4], boff[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p = q * 256 + tid;
+        const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+        aoff[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c * 16;
+        boff[q] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + c * 16;
+      }
+      const int sr = (wave & 1) * 64 + lane;                    // scale row of this lane: waves 0-1 A, 2-3 B
+      const uint32_t soff = (uint32_t)min((wave < 2 ? m0 : n0) + sr, (wave < 2 ? M : N) - 1) * (uint32_t)(K / 32);
+      auto issue = [&](int s, int bf) {
+        const uint32_t d = st_lds + bf * (uint32_t)sizeof(GpStage);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dma16_to_lds(a + s * KSTEP, aoff[q], d + (uint32_t)offsetof(GpStage, a) + (q * 256 + wave * 64) * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dma16_to_lds(w + s * KSTEP, boff[q], d + (uint32_t)offsetof(GpStage, b) + (q * 256 + wave * 64) * 16);
+        if (wave < 2) dma4_to_lds(a_sc + s * 4, soff, d + (uint32_t)offsetof(GpStage, as) + (wave & 1) * 256);
+        else dma4_to_lds(w_sc + s * 4, soff, d + (uint32_t)offsetof(GpStage, bs) + (wave & 1) * 256);
+      };
+
+      v4f tot[4][4], cur[4][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) tot[m][n] = cur[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+      auto compute = [&](const GpStage& S) {
+        v8i bf[4];
+        uint32_t bsv[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int rb = wn * 64 + n * 16;
+          bf[n] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          const u32x4 lo = S.b[rb * 8 + al0], hi = S.b[rb * 8 + al1];
+          bf[n] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          bsv[n] = S.bs[rb + col];
+        }
+        const int ra0 = wm * 64;
+        u32x4 alo = S.a[ra0 * 8 + al0], ahi = S.a[ra0 * 8 + al1];
+        uint32_t sa = S.as[ra0 + col];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) bsv[n] >>= 8 * g;
+        sa >>= 8 * g;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          u32x4 nlo, nhi;
+          uint32_t san = 0;
+          if (m < 3) {
+            const int ra = wm * 64 + (m + 1) * 16;
+            nlo = S.a[ra * 8 + al0];
+            nhi = S.a[ra * 8 + al1];
+            san = S.as[ra + col];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const v8i af = v8i{(int)alo[0], (int)alo[1], (int)alo[2], (int)alo[3], (int)ahi[0], (int)ahi[1], (int)ahi[2], (int)ahi[3]};
+#pragma unroll
+          for (int n = 0; n < 4; ++n) cur[m][n] = mfma_fp8_fp8(af, bf[n], cur[m][n], sa, bsv[n]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (m < 3) {
+            alo = nlo;
+            ahi = nhi;
+            sa = san >> (8 * g);
+          }
+        }
+      };
+      // step s: wait for its DMA (the next step's stays in flight), make every
+      // wavefront's part visible, refill the other buffer, multiply; at the
+      // end of each part of 8 steps its chain joins the total
+      issue(0, 0);
+      for (int s = 0; s < nsteps; ++s) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
+        compute(st[s & 1]);
+        if ((s + 1) % KPART_STEPS == 0 || s + 1 == nsteps) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+              tot[m][n] = s < KPART_STEPS ? cur[m][n] : tot[m][n] + cur[m][n];
+              cur[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+      }
+      // results: lane holds column n0 + 64 wn + 16 n + col, rows m0 + 64 wm + 16 m + 4 g + i
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m0 + wm * 64 + m * 16 + 4 * g + i;
+          if (row < M) {
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+              const int c = n0 + wn * 64 + n * 16 + col;
+              if (c < N) {
+                if (BF16_OUT) static_cast<uint16_t*>(y)[(int64_t)row * N + c] = f32_to_bf16_rne(tot[m][n][i]);
+                else static_cast<float*>(y)[(int64_t)row * N + c] = tot[m][n][i];
+              }
+            }
+          }
+        }
+    }
+  }
+}
+
 hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,
                              int M, int N, int K, void* y, bool bf16_out, hipStream_t stream, const char** variant) {
+  if (M >= GEMM_PREFILL_MIN_M) {
+    const int tiles = ((M + GP_BM - 1) / GP_BM) * ((N + GP_BN - 1) / GP_BN);
+    const int per_xcd = tiles / XCDS_GEMM < 64 ? (tiles + XCDS_GEMM - 1) / XCDS_GEMM : 64;   // 2 per CU at most
+    const dim3 gp(per_xcd * XCDS_GEMM);
+    if (bf16_out) hipLaunchKernelGGL((gemm_prefill_kernel<true>), gp, dim3(256), 0, stream, a, a_sc, w, w_sc, M, N, K, y);
+    else hipLaunchKernelGGL((gemm_prefill_kernel<false>), gp, dim3(256), 0, stream, a, a_sc, w, w_sc, M, N, K, y);
+    *variant = bf16_out ? "gemm:prefill128x128_bf16" : "gemm:prefill128x128_f32";
+    return hipGetLastError();
+  }
   const dim3 grid(N / 16), block(256);
   const bool whole = K == 4 * KPART;
   if (bf16_out && whole) hipLaunchKernelGGL((gemm_decode_kernel<true, true>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);

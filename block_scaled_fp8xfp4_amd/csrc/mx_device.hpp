@@ -61,6 +61,34 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Global -> LDS without registers (gfx950 LDS DMA): lane l's 16 (4) bytes
+// land at dst + 16 l (4 l); dst is the same for the whole wavefront.  Issued
+// as inline assembly so that the compiler neither tracks nor waits for these
+// writes: the kernel orders them itself with explicit vmcnt waits and LDS
+// barriers.  Extra operations outside the compiler's count only make its own
+// vmcnt waits stricter (vector-memory loads complete in issue order).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)(lds_void*)p; }
+__device__ __forceinline__ void dma16_to_lds(const void* src, void* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr(dst))) : "m0");
+}
+__device__ __forceinline__ void dma4_to_lds(const void* src, void* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr(dst))) : "m0");
+}
+// The same from a wavefront-uniform base plus a 32-bit per-lane byte offset,
+// to the wavefront-uniform LDS byte address dst.
+__device__ __forceinline__ void dma16_to_lds(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(dst) : "m0");
+}
+__device__ __forceinline__ void dma4_to_lds(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(dst) : "m0");
+}
+
 // ---------------------------------------------------------------------------
 // Block-32 quantization (OCP MX v1.0 conversion): shared scale
 // X = 2^(floor(log2 amax) - emax) as an E8M0 code clamped to [0, 254]
