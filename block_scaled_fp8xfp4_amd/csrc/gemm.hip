@@ -21,7 +21,7 @@
 namespace mx {
 
 constexpr int XCDS_GEMM = 8;                      // XCDs of an MI355X (block scheduling)
-constexpr int GEMM_PREFILL_MIN_M = 256;            // rows from which the tiled prefill kernel runs
+constexpr int GEMM_PREFILL_MIN_M = 320;            // rows from which the tiled kernel beats the decode kernel (measured)
 
 __device__ __forceinline__ v8i fp8_pair(const u32x4& lo, const u32x4& hi) {
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
