@@ -21,6 +21,10 @@ Workloads (sizes, distributions and structure), one per seed 0..4:
          replacement, popularity Zipf(1.1))
   prefill T=8192, same layer; logits N(0,1)
 Activations are N(0,1) rounded to bf16; weights are N(0, 0.02^2) in fp32.
+Router gate (the linear map whose scores the top-k gate ranks): bf16-valued
+N(0, 1/H) rows [E][H] from the stream SeedSequence([seed, 7]), so that the
+workload's bf16 hidden rows give logits of unit variance, like the drawn
+N(0,1) logits above.
 """
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
@@ -184,3 +188,18 @@ def small_moe(seed, T, H, E, k, I, logits="normal", skip_frac=0.0):
         inp.survival = _gen(np.random.SeedSequence([seed, 99])).random(T, dtype=np.float32)
         inp.survival = np.where(inp.survival < skip_frac, np.float32(0.1), np.float32(0.9))
     return inp
+
+
+def router_gate(cfg, E=None, H=None):
+    """bf16-valued fp32 router gate rows [E][H], N(0, 1/H) (shape defaults to the workload's)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    E = cfg.E if E is None else E
+    H = cfg.H if H is None else H
+    w = _normal(np.random.SeedSequence([cfg.seed, 7]), (E, H), float(H) ** -0.5)
+    return _to_bf16_values(w)
+
+
+def hidden_rows(seed, T, H):
+    """bf16-valued N(0,1) hidden rows [T][H] of an arbitrary (small) shape."""
+    return _to_bf16_values(_normal(np.random.SeedSequence([seed, 8]), (T, H)))

@@ -59,6 +59,8 @@ def _load():
     lib.or_swiglu_requant.argtypes = [P, i64, i32, P, P, P]
     lib.or_block_gemm.restype = i32
     lib.or_block_gemm.argtypes = [P, P, P, P, i32, i32, P, i32, P, i32]
+    lib.or_router_logits.restype = i32
+    lib.or_router_logits.argtypes = [P, P, i32, i32, P, i32, P, i32]
     lib.or_f32_to_bf16.restype = None
     lib.or_f32_to_bf16.argtypes = [P, i64, P]
     lib.or_hardware_threads.restype = i32
@@ -222,6 +224,21 @@ def block_gemm(a, a_sc, w, w_sc, rows=None, threads=0):
     if _load().or_block_gemm(_p(a), _p(a_sc), _p(w), _p(w_sc), N, K, _p(rows), len(rows), _p(y), threads):
         raise ValueError("K must be a multiple of 32")
     return y
+
+
+# ---------------------------------------------------------- router logits
+def router_logits(h, wg, rows=None, threads=0):
+    """fp32 logits [len(rows), E] = decoded h[rows] @ decoded wg^T (bf16 bit patterns h [T, H], wg [E, H])."""
+    h, wg = _c(h, np.uint16), _c(wg, np.uint16)
+    T, H = h.shape
+    E = wg.shape[0]
+    if wg.shape[1] != H:
+        raise ValueError("hidden width mismatch")
+    rows = np.arange(T, dtype=np.int32) if rows is None else _c(rows, np.int32)
+    out = np.empty((len(rows), E), np.float32)
+    if _load().or_router_logits(_p(h), _p(wg), E, H, _p(rows), len(rows), _p(out), threads):
+        raise ValueError("bad router_logits arguments")
+    return out
 
 
 def f32_to_bf16(v):

@@ -414,6 +414,34 @@ int or_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* wq, cons
   return 0;
 }
 
+// ---- router logits ----
+// The routed experts are picked from one score per (row, expert): the
+// hidden row against that expert's gate row, a linear map without bias
+// (post #6 "How it works": the MoE top-k gate; "Kernel by kernel against
+// B12X": the router's own time per step).  The pages give no precisions;
+// read here as bf16 hidden states and bf16 gate rows, accumulated exactly
+// and stored as fp32 logits.
+//   logits[r][e] = fp32( sum_{j=0..H-1} h[rows[r]][j] * wg[e][j] )
+// bf16 is the upper half of an IEEE binary32, so decoding is exact.
+static double bf16_value(uint16_t b) {
+  const uint32_t u = uint32_t(b) << 16;
+  float f; std::memcpy(&f, &u, 4);
+  return double(f);
+}
+
+int or_router_logits(const uint16_t* h, const uint16_t* wg, int E, int H, const int32_t* rows, int nrows,
+                     float* logits, int threads) {
+  if (E < 1 || H < 1) return -1;
+  parallel_for(int64_t(nrows) * E, threads, [&](int64_t idx) {
+    const int64_t r = idx / E, e = idx % E;
+    const int64_t m = rows[r];
+    double acc = 0.0;
+    for (int64_t j = 0; j < H; ++j) acc += bf16_value(h[m * H + j]) * bf16_value(wg[e * H + j]);
+    logits[idx] = float(acc);
+  });
+  return 0;
+}
+
 // ---- fp32 -> bf16, round to nearest, ties to even (finite inputs) ----
 // The two bf16 neighbours of v are its truncation and the next bf16 value
 // away from zero; the nearer one wins, an exact tie takes the even one.
