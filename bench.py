@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense FP8 matrix rate (the FP8 x FP4 MFMA issues at this rate)
 MFMA_FP4_PEAK_TFLOPS = 10100.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix rate (router logits)
 
 EXPERT_BYTES = lambda H, I: 2 * I * (H // 2 + H // 32) + H * (I // 2 + I // 32)
 
@@ -253,6 +254,36 @@ def main():
                     pct_fp8_peak=round(100 * flop / (ms * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 2),
                     variant=mxmoe.last_variant())
 
+    # ------------------------------------------------------------ router logits (the gate's input side)
+    def run_router_logits(cfg, inp, steps, warmup):
+        """moe_router_logits on the workload's bf16 hidden rows and a synthetic
+        bf16 gate [E][H]; the gate is rotated over enough copies to leave the
+        caches for the row counts of a decode step."""
+        from block_scaled_fp8xfp4_amd.layer import RouterLogits
+        T, H, E = cfg.T, cfg.H, cfg.E
+        hid = torch.from_numpy(inp.x).to(dev).to(torch.bfloat16)
+        gate = torch.from_numpy(synth.router_gate(cfg)).to(dev).to(torch.bfloat16)
+        R = 2 if T >= 1024 else 256                              # 256 x 2 MB gates > the 256 MB MALL
+        gates = [gate] + [gate.clone() for _ in range(R - 1)]
+        out = torch.empty((T, E), dtype=torch.float32, device=dev)
+        rl = RouterLogits(T, H, E)
+        for i in range(warmup):
+            rl(hid, gates[i % R], out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            rl(hid, gates[i % R], out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbytes, flop = E * H * 2 + T * H * 2 + T * E * 4, 2 * T * H * E
+        return dict(T=T, H=H, E=E, ms=round(ms, 5), gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    pct_hbm_peak=round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                    tflops=round(flop / (ms * 1e-3) / 1e12, 2),
+                    pct_bf16_peak=round(100 * flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
+                    bytes=nbytes, flop=flop, variant=mxmoe.last_variant(), gate_copies=R)
+
     # ------------------------------------------------------------ prefill
     def run_prefill(steps, warmup):
         cfg = synth.PREFILL
@@ -279,6 +310,7 @@ def main():
         t1.record()
         mxmoe.set_phase_events(None)
         torch.cuda.synchronize()
+        ffn_variant = mxmoe.last_variant()
         ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])   # ms per phase
         gu_ms, dn_ms, cb_ms = (float(np.mean(ph[:, j])) for j in range(3))
         ffn_ms = float(np.mean(ph.sum(axis=1)))
@@ -288,7 +320,8 @@ def main():
         tf = lambda f, ms: f / (ms * 1e-3) / 1e12
         combine_bytes = P * H * 4 + T * H * 4 + T * k * 8
         dense = run_dense_prefill(T, steps, warmup)
-        return dict(tflops=round(tf(flop, ffn_ms), 2), pct_fp8_peak=round(100 * tf(flop, ffn_ms) / MFMA_FP8_PEAK_TFLOPS, 2),
+        router = run_router_logits(cfg, inp, steps, warmup)
+        return dict(router_logits=router, tflops=round(tf(flop, ffn_ms), 2), pct_fp8_peak=round(100 * tf(flop, ffn_ms) / MFMA_FP8_PEAK_TFLOPS, 2),
                     dense_gemm=dense,
                     expert_gemms_tflops=round(tf(flop, gu_ms + dn_ms), 2),
                     expert_gemms_pct_fp8_peak=round(100 * tf(flop, gu_ms + dn_ms) / MFMA_FP8_PEAK_TFLOPS, 2),
@@ -297,7 +330,7 @@ def main():
                     down_ms=round(dn_ms, 4), down_tflops=round(tf(flop_dn, dn_ms), 2),
                     combine_ms=round(cb_ms, 4), combine_gbs=round(combine_bytes / (cb_ms * 1e-3) / 1e9, 1),
                     ffn_ms=round(ffn_ms, 4), step_ms=round(t0.elapsed_time(t1) / steps, 4), flop_per_call=flop,
-                    flop_gate_up=flop_gu, variant=mxmoe.last_variant(), pairs=P), inp
+                    flop_gate_up=flop_gu, variant=ffn_variant, pairs=P), inp
 
     if args.workload == "prefill":
         pre, inp = run_prefill(args.steps, args.warmup)
@@ -313,6 +346,7 @@ def main():
                                            "combine_gbs", "expert_gemms_tflops", "expert_gemms_pct_fp8_peak",
                                            "expert_gemms_pct_fp4_peak", "ffn_ms")},
             "dense_gemm": pre["dense_gemm"],
+            "router_logits": pre["router_logits"],
             "config": {"workload": "prefill MoE chunk: T=8192, H=4096, E=256, top-8, I=576, MXFP4 experts, "
                                    "FP8 block-32 activations", "pairs": pre["pairs"]},
         })
@@ -320,6 +354,7 @@ def main():
     else:
         cfg = synth.DECODE if args.workload == "decode" else synth.VERIFY
         inp, touched = run_decode(cfg)
+        result["router_logits"] = run_router_logits(cfg, inp, args.steps, args.warmup)
         cpu_cfg = cfg
         if not args.no_prefill:
             pre, _ = run_prefill(5, 2)

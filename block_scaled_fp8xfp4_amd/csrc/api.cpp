@@ -69,6 +69,30 @@ mx_status mx_quantize(const void* src, int src_dtype, int64_t rows, int64_t cols
   return from_hip(e);
 }
 
+size_t moe_router_logits_workspace_bytes(int T, int H, int E) {
+  if (T < 0 || E < 1 || H < 32 || H % 32 != 0 || H > mx::LG_MAX_H) return 0;
+  return mx::router_logits_ws_bytes(T, H, E);
+}
+
+mx_status moe_router_logits(const uint16_t* hidden, int T, int H, const uint16_t* w_gate, int E, float* logits,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || H < 32 || H % 32 != 0) return MX_EINVAL;
+  if (H > mx::LG_MAX_H) return MX_EUNSUPPORTED;
+  if ((int64_t)T * H >= (int64_t(1) << 31) || (int64_t)E * H >= (int64_t(1) << 31) ||
+      (int64_t)T * E >= (int64_t(1) << 31))
+    return MX_EUNSUPPORTED;
+  if (!w_gate || (T > 0 && (!hidden || !logits))) return MX_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(w_gate, 16) || !aligned(logits, 4) || !aligned(ws, 256)) return MX_EINVAL;
+  const size_t need = mx::router_logits_ws_bytes(T, H, E);
+  if (need > 0 && (!ws || ws_bytes < need)) return MX_EWORKSPACE;
+  if (T == 0) { g_variant = "logits:empty"; return MX_OK; }
+  const char* v = "";
+  const hipError_t e = mx::launch_router_logits(hidden, T, H, w_gate, E, logits, ws,
+                                                static_cast<hipStream_t>(stream), &v);
+  if (e == hipSuccess) g_variant = v;
+  return from_hip(e);
+}
+
 size_t moe_route_workspace_bytes(int T, int E, int k) {
   (void)k;
   if (T < 0 || E < 1) return 0;

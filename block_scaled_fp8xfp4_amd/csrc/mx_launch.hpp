@@ -12,6 +12,8 @@ constexpr int MAX_K = 16;        // top-k
 constexpr int MAX_I = 2048;      // expert intermediate (decode LDS staging)
 constexpr int MAX_PARTS = 16;    // K parts of 1024 -> H, K <= 16384
 constexpr int ROUTE_CHUNK = 256; // rows per bucketing chunk
+constexpr int LG_MAX_H = 16384;     // router logits: hidden width
+constexpr int LG_PREFILL_MIN_T = 1024; // router logits: rows from which the tiled kernel runs (measured crossover)
 
 hipError_t launch_quantize(const void* src, bool bf16, int64_t rows, int64_t cols, bool fp4,
                            uint8_t* q, uint8_t* sc, hipStream_t stream);
@@ -36,6 +38,10 @@ void set_ffn_phase_events(const hipEvent_t* ev, int n);
 
 hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,
                              int M, int N, int K, void* y, bool bf16_out, hipStream_t stream, const char** variant);
+
+size_t router_logits_ws_bytes(int T, int H, int E);
+hipError_t launch_router_logits(const uint16_t* h, int T, int H, const uint16_t* wg, int E, float* logits, void* ws,
+                                hipStream_t stream, const char** variant);
 
 int num_cus();
 hipError_t launch_check_requant(uint32_t lo, uint32_t hi, unsigned long long* nbad, hipStream_t stream);

@@ -37,6 +37,21 @@ def quantize_experts(w_host, chunk=16):
     return q, sc
 
 
+class RouterLogits:
+    """Owns the workspace of moe_router_logits for up to T rows."""
+
+    def __init__(self, T, H, E):
+        self.T, self.H, self.E = T, H, E
+        n = max(mxmoe.moe_router_logits_workspace_bytes(t, H, E) for t in range(1, min(T, 1024) + 1))
+        self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+
+    def __call__(self, hidden, w_gate, logits, stream=None):
+        if hidden.shape[0] > self.T:
+            raise ValueError("RouterLogits: more rows than sized for")
+        mxmoe.moe_router_logits(hidden, w_gate, logits, self.ws, stream)
+        return logits
+
+
 class Route:
     def __init__(self, T, E, k):
         dev = "cuda"

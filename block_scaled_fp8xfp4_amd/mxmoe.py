@@ -16,7 +16,7 @@ MX_IN_F32, MX_IN_BF16 = 0, 1
 MX_OUT_BF16, MX_OUT_F32 = 0, 1
 
 # every entry point declared in include/mxmoe.h
-EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "moe_expert_ffn_workspace_bytes",
+EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logits", "moe_route_workspace_bytes", "moe_route", "moe_expert_ffn_workspace_bytes",
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
            "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events")
 
@@ -40,6 +40,10 @@ def load():
     P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     lib.mx_quantize.restype = I32
     lib.mx_quantize.argtypes = [P, I32, I64, I64, I32, P, P, P]
+    lib.moe_router_logits.restype = I32
+    lib.moe_router_logits.argtypes = [P, I32, I32, P, I32, P, P, SZ, P]
+    lib.moe_router_logits_workspace_bytes.restype = SZ
+    lib.moe_router_logits_workspace_bytes.argtypes = [I32, I32, I32]
     lib.moe_route_workspace_bytes.restype = SZ
     lib.moe_route_workspace_bytes.argtypes = [I32, I32, I32]
     lib.moe_route.restype = I32
@@ -106,6 +110,25 @@ def mx_quantize(src, q, sc, fmt, stream=None):
     cols = src.shape[-1]
     rows = src.numel() // cols if cols else 0
     _check(load().mx_quantize(_ptr(src), dt, rows, cols, fmt, _ptr(q), _ptr(sc), _stream(stream)), "mx_quantize")
+
+
+def moe_router_logits_workspace_bytes(T, H, E):
+    return load().moe_router_logits_workspace_bytes(T, H, E)
+
+
+def moe_router_logits(hidden, w_gate, logits, ws=None, stream=None):
+    """logits [T, E] fp32 = hidden [T, H] bf16 . w_gate [E, H] bf16 (ws: uint8 device tensor of
+    moe_router_logits_workspace_bytes(T, H, E) bytes, or None when that size is 0)."""
+    T, H = hidden.shape
+    E = w_gate.shape[0]
+    if w_gate.shape[1] != H or tuple(logits.shape) != (T, E):
+        raise ValueError("moe_router_logits: shape mismatch")
+    for t in (hidden, w_gate):
+        if t.element_size() != 2 or not t.is_contiguous():
+            raise ValueError("moe_router_logits: hidden and w_gate must be contiguous 16-bit (bf16) tensors")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().moe_router_logits(_ptr(hidden), T, H, _ptr(w_gate), E, _ptr(logits), _ptr(ws), ws_bytes,
+                                    _stream(stream)), "moe_router_logits")
 
 
 def moe_route_workspace_bytes(T, E, k):

@@ -83,6 +83,31 @@ mx_status mx_quantize(const void* src, int src_dtype, int64_t rows, int64_t cols
                       uint8_t* q, uint8_t* sc, void* stream);
 
 /*
+ * Router logits, the scores the top-k gate ranks (post #6 "How it works"
+ * item 3: the MoE top-k gate; "Kernel by kernel against B12X": the router's
+ * time per step).  A linear map without bias:
+ *   logits[t][e] = sum_j hidden[t][j] * w_gate[e][j]
+ * hidden: bf16 [T][H] (uint16 bit patterns), w_gate: bf16 [E][H], both
+ * 16-byte aligned, row-major, read only.  logits: fp32 [T][E] (4-byte
+ * aligned), written for every (t, e); caller-owned device memory.
+ * Products are accumulated in fp32 on the matrix cores in one fixed order
+ * per element (K steps of 32, parts of 256 each chained from zero, parts
+ * added left to right), the same for every T, so a row's logits never
+ * depend on the rows beside it.
+ * Supported: T >= 0, E >= 1, H % 32 == 0, 32 <= H <= 16384, and T*H, E*H,
+ * T*E < 2^31.  ws: device scratch of at least
+ * moe_router_logits_workspace_bytes(T, H, E) bytes (256-byte aligned;
+ * contents on entry ignored; may be NULL when that size is 0): few rows
+ * (T < 1024) split K over workgroups and keep the per-part sums there.
+ * MX_EINVAL for null pointers, misalignment or a bad shape, MX_EWORKSPACE
+ * for a missing or short workspace, MX_EUNSUPPORTED beyond the limits.
+ * Asynchronous on stream.
+ */
+size_t    moe_router_logits_workspace_bytes(int T, int H, int E);
+mx_status moe_router_logits(const uint16_t* hidden, int T, int H, const uint16_t* w_gate, int E,
+                            float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Top-k gate + bucketing (post #6 "How it works" item 3: the MoE top-k gate;
  * post #2 "What changed": dead verification rows; TP4 README "Experts": the
  * route planner and per-slot buffer).

@@ -122,6 +122,31 @@ def test_gemm_rejects_bad_arguments(lib):
     assert gemm(lib, a=None) == mxmoe.MX_EINVAL
 
 
+def logits(lib, T=4, H=256, E=8, h=FAKE, w=FAKE, out=FAKE, ws=FAKE_WS, ws_bytes=1 << 30):
+    return lib.moe_router_logits(h, T, H, w, E, out, ws, ws_bytes, None)
+
+
+def test_router_logits_rejects_bad_arguments(lib):
+    assert logits(lib, T=-1) == mxmoe.MX_EINVAL
+    assert logits(lib, E=0) == mxmoe.MX_EINVAL
+    assert logits(lib, H=100) == mxmoe.MX_EINVAL                       # H % 32
+    assert logits(lib, H=0) == mxmoe.MX_EINVAL
+    assert logits(lib, H=16384 + 32) == mxmoe.MX_EUNSUPPORTED
+    assert logits(lib, T=1 << 20, H=4096) == mxmoe.MX_EUNSUPPORTED      # T*H >= 2^31
+    assert logits(lib, w=None) == mxmoe.MX_EINVAL
+    assert logits(lib, h=None) == mxmoe.MX_EINVAL
+    assert logits(lib, out=None) == mxmoe.MX_EINVAL
+    assert logits(lib, h=ctypes.c_void_p((1 << 20) + 8)) == mxmoe.MX_EINVAL   # 16-byte alignment
+    assert logits(lib, out=ctypes.c_void_p((1 << 20) + 2)) == mxmoe.MX_EINVAL
+    assert logits(lib, ws=ctypes.c_void_p((1 << 24) + 64)) == mxmoe.MX_EINVAL
+    need = mxmoe.moe_router_logits_workspace_bytes(4, 256, 8)
+    assert need >= 4 * 8 * 4                                            # at least one part sum per element
+    assert logits(lib, ws=None) == mxmoe.MX_EWORKSPACE
+    assert logits(lib, ws_bytes=need - 1) == mxmoe.MX_EWORKSPACE
+    assert logits(lib, T=0, h=None, out=None, ws=None) == mxmoe.MX_OK   # nothing to do, nothing launched
+    assert mxmoe.moe_router_logits_workspace_bytes(1, 100, 8) == 0      # invalid shape
+
+
 def test_path_switch(lib):
     old = mxmoe.set_ffn_path(1)
     assert mxmoe.set_ffn_path(old) == 1
