@@ -49,6 +49,8 @@ def _load():
     lib.or_dequantize.argtypes = [P, P, i64, i64, i32, P]
     lib.or_route.restype = i32
     lib.or_route.argtypes = [P, i32, i32, i32, P, f32, P, P, P, P, P]
+    lib.or_route_live.restype = i32
+    lib.or_route_live.argtypes = [P, i32, i32, i32, P, f32, P, P, P, P, P, P]
     lib.or_moe_rows.restype = i32
     lib.or_moe_rows.argtypes = [P, P, i32, P, P, P, i32, P, P, P, P, i32, i32, P, i32, P, i32]
     lib.or_pair_ffn.restype = i32
@@ -143,6 +145,25 @@ def route(logits, k, survival=None, skip_below=0.2):
         raise ValueError("bad route arguments")
     live = np.ones(T, np.uint8) if surv is None else (~(surv < np.float32(skip_below))).astype(np.uint8)
     return dict(ids=ids, w=w, offsets=offsets, perm=perm, slot_pos=slot_pos, live=live)
+
+
+def route_live(logits, k, survival, anchor, reuse_below=0.1):
+    """Top-k gate where rows with survival < reuse_below take their anchor row's
+    experts (weighted by their own logits); every pair is bucketed."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    surv = _c(survival, np.float32) if survival is not None else None
+    anc = _c(anchor, np.int32)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(T * k, np.int32)
+    slot_pos = np.empty((T, k), np.int32)
+    rc = _load().or_route_live(_p(logits), T, E, k, _p(surv), reuse_below, _p(anc),
+                               _p(ids), _p(w), _p(offsets), _p(perm), _p(slot_pos))
+    if rc:
+        raise ValueError("bad route_live arguments")
+    return dict(ids=ids, w=w, offsets=offsets, perm=perm, slot_pos=slot_pos, live=np.ones(T, np.uint8))
 
 
 # ------------------------------------------------------------- expert FFN

@@ -325,6 +325,56 @@ int or_route(const float* logits, int T, int E, int k, const float* survival, fl
   return 0;
 }
 
+// ---- top-k gate with router-live verification rows ----
+// Verification rows that the confidence estimate does not expect to survive
+// (survival[t] < reuse_below) reuse their anchor row's experts instead of
+// skipping the experts: no weight is read that the anchor does not read, and
+// the row still gets an output (DeepSeek-V4.1-Flash-4x-DGX-Spark-TP4 README,
+// settings table, row "Verify length").  Read here as: such a row t with an
+// anchor a = anchor[t] in [0, T), a != t, takes row a's own top-k experts in
+// row a's slot order (whatever row a's survival), weighted by the softmax of
+// row t's own logits over those experts, w_j = exp(l_j - m) / sum_i
+// exp(l_i - m) with m the largest of them, in double, rounded to fp32.  Every
+// other row keeps its own top-k.  Every pair of every row enters the buckets
+// (same order as or_route).
+int or_route_live(const float* logits, int T, int E, int k, const float* survival, float reuse_below,
+                  const int32_t* anchor, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
+                  int32_t* slot_pos) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return -1;
+  std::vector<int32_t> own(int64_t(T) * k);
+  std::vector<float> own_w(int64_t(T) * k);
+  std::vector<int32_t> off(E + 1), pm(int64_t(T) * k), sp(int64_t(T) * k);
+  if (or_route(logits, T, E, k, nullptr, 0.0f, own.data(), own_w.data(), off.data(), pm.data(), sp.data()))
+    return -1;
+  for (int t = 0; t < T; ++t) {
+    const int a = anchor ? anchor[t] : t;
+    const bool reuse = survival && survival[t] < reuse_below && a >= 0 && a < T && a != t;
+    const int src = reuse ? a : t;
+    const float* l = logits + int64_t(t) * E;
+    double m = -INFINITY;
+    for (int j = 0; j < k; ++j) m = std::max(m, double(l[own[int64_t(src) * k + j]]));
+    std::vector<double> ex(k);
+    double den = 0.0;
+    for (int j = 0; j < k; ++j) {
+      ex[j] = std::exp(double(l[own[int64_t(src) * k + j]]) - m);
+      den += ex[j];
+    }
+    for (int j = 0; j < k; ++j) {
+      ids[int64_t(t) * k + j] = own[int64_t(src) * k + j];
+      w[int64_t(t) * k + j] = float(ex[j] / den);
+    }
+  }
+  int32_t p = 0;
+  for (int e = 0; e < E; ++e) {
+    offsets[e] = p;
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j)
+        if (ids[int64_t(t) * k + j] == e) { perm[p] = t * k + j; slot_pos[int64_t(t) * k + j] = p; ++p; }
+  }
+  offsets[E] = p;
+  return 0;
+}
+
 // ---- routed-expert layer on a set of token rows ----
 // For each row t listed in rows[0..nrows): if live[t], y_t = sum over slots j
 // in order 0..k-1 of w_tj * o_tj (double, rounded to fp32), where o_tj is the
