@@ -208,6 +208,40 @@ def main():
         ms = total_ms / args.steps
         ffn_bytes = touched * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * H * 4
         achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+        if cfg.streams:
+            # the same step with router-live verification rows: rows below the
+            # confidence threshold take their anchor's experts instead of skipping
+            thr = 0.1
+            anchor = torch.from_numpy((np.arange(T) // (cfg.drafts + 1) * (cfg.drafts + 1)).astype(np.int32)).to(dev)
+            route(logits, surv, thr, anchor=anchor)
+            live_variant = mxmoe.last_variant()
+            torch.cuda.synchronize()
+            touched_l = int(np.count_nonzero(np.diff(route.offsets.cpu().numpy())))
+            reusing = int(np.sum((inp.survival < np.float32(thr)) & (np.arange(T) % (cfg.drafts + 1) != 0)))
+
+            def step_live(i):
+                w13q, w13s, w2q, w2s = copies[i % R]
+                route(logits, surv, thr, anchor=anchor)
+                ffn(xq, xsc, route, w13q, w13s, w2q, w2s)
+                g, gs = gcopies[i % R]
+                mxmoe.fp8_block_gemm(aq, asc, g, gs, yg, mxmoe.MX_OUT_BF16)
+
+            for i in range(args.warmup):
+                step_live(i)
+            torch.cuda.synchronize()
+            l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            l0.record()
+            for i in range(args.steps):
+                step_live(i)
+            l1.record()
+            torch.cuda.synchronize()
+            live_ms = l0.elapsed_time(l1) / args.steps
+            live_bytes = touched_l * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * E * 4 + T * H * 4 + dense_bytes
+            result["router_live"] = {"reuse_below": thr, "rows_reusing": reusing, "pairs": T * k,
+                                     "touched_experts": touched_l, "ms_per_step": round(live_ms, 5),
+                                     "gbs": round(live_bytes / (live_ms * 1e-3) / 1e9, 2),
+                                     "variant": live_variant}
+            route(logits, surv)                                  # back to the skip-mode routing
         result.update({
             "metric": "decode weight-stream GB/s (% HBM peak) + prefill expert TFLOP/s (% MFMA peak)",
             "value": round(step_bytes / (ms * 1e-3) / 1e9, 2),

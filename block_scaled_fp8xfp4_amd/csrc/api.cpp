@@ -99,22 +99,41 @@ size_t moe_route_workspace_bytes(int T, int E, int k) {
   return mx::route_ws_bytes(T, E);
 }
 
-mx_status moe_route(const float* logits, int T, int E, int k, const float* survival, float skip_below,
-                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* perm, int32_t* slot_pos,
-                    void* ws, size_t ws_bytes, void* stream) {
+namespace {
+mx_status route_common(const float* logits, int T, int E, int k, const float* survival, float threshold,
+                       const int32_t* anchor, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                       int32_t* perm, int32_t* slot_pos, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || E < 1 || E > mx::MAX_E || k < 1 || k > E || k > mx::MAX_K) return MX_EINVAL;
   if ((int64_t)T * k >= (int64_t(1) << 31)) return MX_EINVAL;
   if (!expert_offsets) return MX_EINVAL;
   if (T > 0 && (!logits || !topk_ids || !topk_w || !perm || !slot_pos)) return MX_EINVAL;
   if (!ws || ws_bytes < mx::route_ws_bytes(T, E)) return MX_EWORKSPACE;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
-      !aligned(perm, 4) || !aligned(slot_pos, 4) || !aligned(survival, 4) || !aligned(ws, 256))
+      !aligned(perm, 4) || !aligned(slot_pos, 4) || !aligned(survival, 4) || !aligned(anchor, 4) ||
+      !aligned(ws, 256))
     return MX_EINVAL;
   const char* v = "";
-  const hipError_t e = mx::launch_route(logits, T, E, k, survival, skip_below, topk_ids, topk_w, expert_offsets, perm,
-                                        slot_pos, ws, static_cast<hipStream_t>(stream), &v);
+  const hipError_t e = mx::launch_route(logits, T, E, k, survival, threshold, anchor, topk_ids, topk_w,
+                                        expert_offsets, perm, slot_pos, ws, static_cast<hipStream_t>(stream), &v);
   if (e == hipSuccess) g_variant = v;
   return from_hip(e);
+}
+}  // namespace
+
+mx_status moe_route(const float* logits, int T, int E, int k, const float* survival, float skip_below,
+                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* perm, int32_t* slot_pos,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return route_common(logits, T, E, k, survival, skip_below, nullptr, topk_ids, topk_w, expert_offsets, perm,
+                      slot_pos, ws, ws_bytes, stream);
+}
+
+mx_status moe_route_live(const float* logits, int T, int E, int k, const float* survival, float reuse_below,
+                         const int32_t* anchor, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                         int32_t* perm, int32_t* slot_pos, void* ws, size_t ws_bytes, void* stream) {
+  if (T > 0 && !anchor) return MX_EINVAL;
+  if (T == 0) anchor = reinterpret_cast<const int32_t*>(ws);   // any non-null pointer: nothing is read
+  return route_common(logits, T, E, k, survival, reuse_below, anchor, topk_ids, topk_w, expert_offsets, perm,
+                      slot_pos, ws, ws_bytes, stream);
 }
 
 mx_status moe_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h, size_t* off_o) {

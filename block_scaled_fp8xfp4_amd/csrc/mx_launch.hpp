@@ -19,9 +19,10 @@ hipError_t launch_quantize(const void* src, bool bf16, int64_t rows, int64_t col
                            uint8_t* q, uint8_t* sc, hipStream_t stream);
 
 size_t route_ws_bytes(int T, int E);
+// anchor == NULL: skip mode; otherwise router-live mode
 hipError_t launch_route(const float* logits, int T, int E, int k, const float* survival, float skip_below,
-                        int32_t* ids, float* w, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
-                        void* ws, hipStream_t stream, const char** variant);
+                        const int32_t* anchor, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
+                        int32_t* slot_pos, void* ws, hipStream_t stream, const char** variant);
 
 struct FfnArgs {
   const uint8_t* x; const uint8_t* x_sc; int T; int H;

@@ -2,7 +2,8 @@
 // flash recipe" thread, post #6, "How it works"; exact ties by lowest
 // position, post #4, "Exact indexer selections"; dead verification rows of
 // post #2, "What changed"; the route planner and per-slot buffer of the
-// DeepSeek-V4.1-Flash-4x-DGX-Spark-TP4 README, settings table, row "Experts").
+// DeepSeek-V4.1-Flash-4x-DGX-Spark-TP4 README, settings table, row "Experts";
+// router-live verification rows, same table, row "Verify length").
 //
 // Top-k of one row, one wavefront: each lane holds E/64 logits as order-
 // preserving 32-bit keys (-0 folded into +0, so it ties with +0).  k rounds
@@ -19,6 +20,12 @@
 // decides a position.  One row: the wavefront that ranked it also buckets it
 // in registers.  Up to 256 rows: one workgroup, one wavefront per row at a
 // time.  More rows: chunks of 256 rows over several launches.
+//
+// Router-live mode (an anchor per row): a verification row below the
+// survival threshold does not skip the experts but takes its anchor row's
+// top-k, found by its own wavefront from the anchor's logits (no dependence
+// between rows), weighted by the softmax of its own logits over those
+// experts; every row joins the buckets.
 #include <climits>
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
@@ -88,20 +95,62 @@ __device__ __forceinline__ float slot_weight(float val, int k) {
   return (float)(ex / den);
 }
 
+// softmax over k logits of another row's picks, w_j = exp(l_j - m) / sum_i
+// exp(l_i - m) with m the largest of them, in double
+__device__ __forceinline__ float slot_weight_max(float val, int k) {
+  const int lane = threadIdx.x & 63;
+  float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), 0));
+  for (int j = 1; j < k; ++j) m = fmaxf(m, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), j)));
+  const double ex = lane < k ? exp((double)val - (double)m) : 0.0;
+  double den = 0.0;
+  for (int j = 0; j < k; ++j) {
+    const long long bits = __double_as_longlong(ex);
+    const int lo = __builtin_amdgcn_readlane((int)(bits & 0xFFFFFFFFll), j);
+    const int hi = __builtin_amdgcn_readlane((int)(bits >> 32), j);
+    den += __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+  }
+  return (float)(ex / den);
+}
+
 __device__ __forceinline__ bool row_live(const float* survival, float skip_below, int t) {
   return survival == nullptr || !(survival[t] < skip_below);
 }
 
+// How row t is routed.  Skip mode (anchor == NULL): its own experts, in the
+// buckets only when live.  Router-live mode: every row is bucketed; a row
+// below the threshold with a valid anchor a != t takes row a's experts.
+__device__ __forceinline__ void row_mode(const float* survival, float thr, const int32_t* anchor, int T, int t,
+                                         bool& live, int& src) {
+  src = t;
+  if (!anchor) {
+    live = row_live(survival, thr, t);
+    return;
+  }
+  live = true;
+  if (survival && survival[t] < thr) {
+    const int a = anchor[t];
+    if (a >= 0 && a < T) src = a;
+  }
+}
+
 // Top-k + weights of row t by one wavefront; writes ids and weights (and -1
 // slot positions for a dead row); returns the row's expert in lanes < k.
+// The experts are row src's top-k (src = t, or a router-live row's anchor);
+// the weights always come from row t's own logits.
 template <int PER>
-__device__ int topk_row(const float* __restrict__ logits, int t, int E, int k, bool live, int32_t* __restrict__ ids,
-                        float* __restrict__ w, int32_t* __restrict__ slot_pos) {
+__device__ int topk_row(const float* __restrict__ logits, int t, int src, int E, int k, bool live,
+                        int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ slot_pos) {
   const int lane = threadIdx.x & 63;
   int idx;
   float val;
-  wave_topk<PER>(logits + (int64_t)t * E, E, k, idx, val);
-  const float wt = slot_weight(val, k);
+  wave_topk<PER>(logits + (int64_t)src * E, E, k, idx, val);
+  float wt;
+  if (src == t) {
+    wt = slot_weight(val, k);
+  } else {
+    val = lane < k ? logits[(int64_t)t * E + idx] : 0.0f;
+    wt = slot_weight_max(val, k);
+  }
   if (lane < k) {
     ids[(int64_t)t * k + lane] = idx;
     w[(int64_t)t * k + lane] = wt;
@@ -117,12 +166,15 @@ __device__ int topk_row(const float* __restrict__ logits, int t, int E, int k, b
 template <int PER>
 __global__ __launch_bounds__(64) void route1_kernel(const float* __restrict__ logits, int E, int k,
                                                     const float* __restrict__ survival, float skip_below,
+                                                    const int32_t* __restrict__ anchor,
                                                     int32_t* __restrict__ ids, float* __restrict__ w,
                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                     int32_t* __restrict__ slot_pos) {
   const int lane = threadIdx.x;
-  const bool live = row_live(survival, skip_below, 0);
-  const int idx = topk_row<PER>(logits, 0, E, k, live, ids, w, slot_pos);
+  bool live;
+  int src;
+  row_mode(survival, skip_below, anchor, 1, 0, live, src);
+  const int idx = topk_row<PER>(logits, 0, src, E, k, live, ids, w, slot_pos);
   int rank = 0;
   for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(idx, i) < idx ? 1 : 0;
   if (lane < k) {
@@ -207,6 +259,7 @@ __device__ void scatter_chunk(const RowMasks& cm, const int32_t* ids_lds, int c0
 template <int PER>
 __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                            const float* __restrict__ survival, float skip_below,
+                                                           const int32_t* __restrict__ anchor,
                                                            int32_t* __restrict__ ids, float* __restrict__ w,
                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ slot_pos) {
@@ -216,8 +269,10 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int i = threadIdx.x; i < E * 4; i += blockDim.x) (&cm.m[0][0])[i] = 0ull;
   for (int t = wave; t < T; t += nw) {
-    const bool live = row_live(survival, skip_below, t);
-    const int idx = topk_row<PER>(logits, t, E, k, live, ids, w, slot_pos);
+    bool live;
+    int src;
+    row_mode(survival, skip_below, anchor, T, t, live, src);
+    const int idx = topk_row<PER>(logits, t, src, E, k, live, ids, w, slot_pos);
     if (lane < k) ids_lds[t * k + lane] = live ? idx : -1;
   }
   lds_barrier();
@@ -249,10 +304,15 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
 template <int PER>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    const float* __restrict__ survival, float skip_below,
+                                                   const int32_t* __restrict__ anchor,
                                                    int32_t* __restrict__ ids, float* __restrict__ w,
                                                    int32_t* __restrict__ slot_pos) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t < T) topk_row<PER>(logits, t, E, k, row_live(survival, skip_below, t), ids, w, slot_pos);
+  if (t >= T) return;
+  bool live;
+  int src;
+  row_mode(survival, skip_below, anchor, T, t, live, src);
+  topk_row<PER>(logits, t, src, E, k, live, ids, w, slot_pos);
 }
 
 // Gather chunk c's experts (-1 for dead rows) into LDS.
@@ -318,6 +378,11 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(const int32_t* __re
   scatter_chunk(cm, ids_lds, c * ROUTE_CHUNK, nrows, E, k, bases + (int64_t)c * E, perm, slot_pos);
 }
 
+// T = 0: no pairs, every bucket offset is 0
+__global__ __launch_bounds__(256) void zero_offsets_kernel(int32_t* __restrict__ offsets, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) offsets[i] = 0;
+}
+
 size_t route_ws_bytes(int T, int E) {
   const size_t nchunks = ((size_t)T + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
   const size_t b = nchunks * (size_t)E * 4;
@@ -326,39 +391,46 @@ size_t route_ws_bytes(int T, int E) {
 
 template <int PER>
 static void launch_route_per(const float* logits, int T, int E, int k, const float* survival, float skip_below,
-                             int32_t* ids, float* w, int32_t* offsets, int32_t* perm, int32_t* slot_pos, void* ws,
-                             hipStream_t stream, const char** variant) {
+                             const int32_t* anchor, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
+                             int32_t* slot_pos, void* ws, hipStream_t stream, const char** variant) {
   const int nchunks = (T + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
-  if (T == 1) {
-    hipLaunchKernelGGL((route1_kernel<PER>), dim3(1), dim3(64), 0, stream, logits, E, k, survival, skip_below, ids, w,
-                       offsets, perm, slot_pos);
-    *variant = "route:one_row_wavefront";
+  const float* bucket_survival = anchor ? nullptr : survival;   // router-live: every row is bucketed
+  if (T == 0) {
+    hipLaunchKernelGGL(zero_offsets_kernel, dim3(1), dim3(256), 0, stream, offsets, E + 1);
+    *variant = "route:empty";
+  } else if (T == 1) {
+    hipLaunchKernelGGL((route1_kernel<PER>), dim3(1), dim3(64), 0, stream, logits, E, k, survival, skip_below, anchor,
+                       ids, w, offsets, perm, slot_pos);
+    *variant = anchor ? "route_live:one_row_wavefront" : "route:one_row_wavefront";
   } else if (nchunks <= 1) {
     const int threads = 64 * (T < 16 ? T : 16);
     hipLaunchKernelGGL((route_small_kernel<PER>), dim3(1), dim3(threads), 0, stream, logits, T, E, k, survival,
-                       skip_below, ids, w, offsets, perm, slot_pos);
-    *variant = "route:fused_single_workgroup";
+                       skip_below, anchor, ids, w, offsets, perm, slot_pos);
+    *variant = anchor ? "route_live:fused_single_workgroup" : "route:fused_single_workgroup";
   } else {
     int32_t* counts = static_cast<int32_t*>(ws);
     hipLaunchKernelGGL((topk_kernel<PER>), dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, survival,
-                       skip_below, ids, w, slot_pos);
-    hipLaunchKernelGGL(bucket_count_kernel, dim3(nchunks), dim3(256), 0, stream, ids, T, E, k, survival, skip_below,
-                       counts);
+                       skip_below, anchor, ids, w, slot_pos);
+    hipLaunchKernelGGL(bucket_count_kernel, dim3(nchunks), dim3(256), 0, stream, ids, T, E, k, bucket_survival,
+                       skip_below, counts);
     hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), 0, stream, counts, nchunks, T, E, k, offsets, perm);
-    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nchunks), dim3(256), 0, stream, ids, T, E, k, survival,
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nchunks), dim3(256), 0, stream, ids, T, E, k, bucket_survival,
                        skip_below, counts, perm, slot_pos);
-    *variant = "route:topk_wave+bucket_count/scan/scatter";
+    *variant = anchor ? "route_live:topk_wave+bucket_count/scan/scatter" : "route:topk_wave+bucket_count/scan/scatter";
   }
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, const float* survival, float skip_below,
-                        int32_t* ids, float* w, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
-                        void* ws, hipStream_t stream, const char** variant) {
-  if (E <= 64) launch_route_per<1>(logits, T, E, k, survival, skip_below, ids, w, offsets, perm, slot_pos, ws, stream, variant);
-  else if (E <= 128) launch_route_per<2>(logits, T, E, k, survival, skip_below, ids, w, offsets, perm, slot_pos, ws, stream, variant);
-  else if (E <= 256) launch_route_per<4>(logits, T, E, k, survival, skip_below, ids, w, offsets, perm, slot_pos, ws, stream, variant);
-  else if (E <= 512) launch_route_per<8>(logits, T, E, k, survival, skip_below, ids, w, offsets, perm, slot_pos, ws, stream, variant);
-  else launch_route_per<16>(logits, T, E, k, survival, skip_below, ids, w, offsets, perm, slot_pos, ws, stream, variant);
+                        const int32_t* anchor, int32_t* ids, float* w, int32_t* offsets, int32_t* perm,
+                        int32_t* slot_pos, void* ws, hipStream_t stream, const char** variant) {
+#define MX_ROUTE(P) launch_route_per<P>(logits, T, E, k, survival, skip_below, anchor, ids, w, offsets, perm, \
+                                        slot_pos, ws, stream, variant)
+  if (E <= 64) MX_ROUTE(1);
+  else if (E <= 128) MX_ROUTE(2);
+  else if (E <= 256) MX_ROUTE(4);
+  else if (E <= 512) MX_ROUTE(8);
+  else MX_ROUTE(16);
+#undef MX_ROUTE
   return hipGetLastError();
 }
 

@@ -63,9 +63,15 @@ class Route:
         self.slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.ws = torch.empty(mxmoe.moe_route_workspace_bytes(T, E, k), dtype=torch.uint8, device=dev)
 
-    def __call__(self, logits, survival=None, skip_below=0.2, stream=None):
-        mxmoe.moe_route(logits, self.k, survival, skip_below, self.ids, self.w, self.offsets, self.perm,
-                        self.slot_pos, self.ws, stream)
+    def __call__(self, logits, survival=None, skip_below=0.2, stream=None, anchor=None):
+        """Skip mode, or router-live mode when anchor (int32 [T]) is given
+        (then skip_below is the reuse threshold)."""
+        if anchor is None:
+            mxmoe.moe_route(logits, self.k, survival, skip_below, self.ids, self.w, self.offsets, self.perm,
+                            self.slot_pos, self.ws, stream)
+        else:
+            mxmoe.moe_route_live(logits, self.k, survival, skip_below, anchor, self.ids, self.w, self.offsets,
+                                 self.perm, self.slot_pos, self.ws, stream)
         return self
 
 

@@ -16,7 +16,7 @@ MX_IN_F32, MX_IN_BF16 = 0, 1
 MX_OUT_BF16, MX_OUT_F32 = 0, 1
 
 # every entry point declared in include/mxmoe.h
-EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logits", "moe_route_workspace_bytes", "moe_route", "moe_expert_ffn_workspace_bytes",
+EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logits", "moe_route_workspace_bytes", "moe_route", "moe_route_live", "moe_expert_ffn_workspace_bytes",
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
            "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events")
 
@@ -48,6 +48,8 @@ def load():
     lib.moe_route_workspace_bytes.argtypes = [I32, I32, I32]
     lib.moe_route.restype = I32
     lib.moe_route.argtypes = [P, I32, I32, I32, P, F32, P, P, P, P, P, P, SZ, P]
+    lib.moe_route_live.restype = I32
+    lib.moe_route_live.argtypes = [P, I32, I32, I32, P, F32, P, P, P, P, P, P, P, SZ, P]
     lib.moe_expert_ffn_workspace_bytes.restype = SZ
     lib.moe_expert_ffn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.moe_ws_layout.restype = I32
@@ -140,6 +142,14 @@ def moe_route(logits, k, survival, skip_below, topk_ids, topk_w, expert_offsets,
     _check(load().moe_route(_ptr(logits), T, E, k, _ptr(survival), float(skip_below), _ptr(topk_ids), _ptr(topk_w),
                             _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(ws), ws.numel() * ws.element_size(),
                             _stream(stream)), "moe_route")
+
+
+def moe_route_live(logits, k, survival, reuse_below, anchor, topk_ids, topk_w, expert_offsets, perm, slot_pos, ws,
+                   stream=None):
+    T, E = logits.shape
+    _check(load().moe_route_live(_ptr(logits), T, E, k, _ptr(survival), float(reuse_below), _ptr(anchor),
+                                 _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_route_live")
 
 
 def moe_expert_ffn_workspace_bytes(T, H, E, I, k):

@@ -129,6 +129,29 @@ mx_status moe_router_logits(const uint16_t* hidden, int T, int H, const uint16_t
  *     (256-byte aligned); contents on entry are ignored.
  */
 size_t    moe_route_workspace_bytes(int T, int E, int k);
+
+/*
+ * Top-k gate with router-live verification rows (TP4 README, settings
+ * table, row "Verify length": rows the confidence estimate does not expect
+ * to survive reuse the anchor row's experts inside the router, so they read
+ * no weights the anchor does not, and still get an output).
+ * As moe_route, except:
+ *   anchor  int32 [T] (device): the anchor row of each row (itself for an
+ *           anchor).  Row t with survival[t] < reuse_below (strict) and
+ *           0 <= anchor[t] < T takes row anchor[t]'s own top-k experts, in
+ *           that row's slot order (whatever its survival), and weights
+ *           w_j = exp(l_j - m) / sum_i exp(l_i - m) over its OWN logits l at
+ *           those experts (m = their maximum).  Other rows (anchor out of
+ *           range or t itself, or survival NULL) keep their own top-k.
+ *   Every row is live: all T*k pairs join the buckets, no slot_pos is -1,
+ *   expert_offsets[E] = T*k.
+ * anchor must be non-null when T > 0.  ws: moe_route_workspace_bytes(T, E, k).
+ */
+mx_status moe_route_live(const float* logits, int T, int E, int k,
+                         const float* survival, float reuse_below, const int32_t* anchor,
+                         int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                         int32_t* perm, int32_t* slot_pos,
+                         void* ws, size_t ws_bytes, void* stream);
 mx_status moe_route(const float* logits, int T, int E, int k,
                     const float* survival, float skip_below,
                     int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,

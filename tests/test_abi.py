@@ -88,6 +88,19 @@ def test_route_rejects_bad_arguments(lib):
     assert route(lib, T=8192, E=256, k=8, ws_bytes=100) == mxmoe.MX_EWORKSPACE
 
 
+def route_live(lib, T=4, E=8, k=2, anchor=FAKE, ws=FAKE_WS, ws_bytes=1 << 20, logits=FAKE):
+    return lib.moe_route_live(logits, T, E, k, FAKE, 0.1, anchor, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_route_live_rejects_bad_arguments(lib):
+    assert route_live(lib, anchor=None) == mxmoe.MX_EINVAL
+    assert route_live(lib, anchor=ctypes.c_void_p((1 << 20) + 2)) == mxmoe.MX_EINVAL   # alignment
+    assert route_live(lib, k=9, E=8) == mxmoe.MX_EINVAL
+    assert route_live(lib, logits=None) == mxmoe.MX_EINVAL
+    assert route_live(lib, ws=None) == mxmoe.MX_EWORKSPACE
+    assert route_live(lib, T=8192, E=256, k=8, ws_bytes=100) == mxmoe.MX_EWORKSPACE
+
+
 def ffn(lib, T=4, H=256, E=8, I=64, k=2, ws=FAKE_WS, ws_bytes=1 << 34, x=FAKE, w13=FAKE):
     return lib.moe_expert_ffn(x, FAKE, T, H, FAKE, FAKE, FAKE, FAKE, k, w13, FAKE, FAKE, FAKE, E, I, FAKE,
                               ws, ws_bytes, None)

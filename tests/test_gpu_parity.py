@@ -140,7 +140,7 @@ def check_requant(q_gpu, sc_gpu, q_ref, sc_ref, a_ref):
 E2E_TOL = 5e-3
 
 
-def ffn_parity(inp, r, layer, rows=None, what="", e2e_tol=E2E_TOL, max_pairs=96):
+def ffn_parity(inp, r, layer, rows=None, what="", e2e_tol=E2E_TOL, max_pairs=96, route=None):
     """Staged parity on identical inputs: (i) gate/up h vs the oracle, (ii) the
     requant of the GPU's h vs the oracle's requant of the same h, (iii) y vs the
     oracle's down projection + combine of the GPU's intermediate; then the
@@ -148,7 +148,7 @@ def ffn_parity(inp, r, layer, rows=None, what="", e2e_tol=E2E_TOL, max_pairs=96)
     c = inp.cfg
     old = mxmoe.set_ffn_path(1)             # the decode path publishes h for stage (i)
     try:
-        y, route, ffn = layer.gpu_y()
+        y, route, ffn = layer.gpu_y(route=route)
     finally:
         mxmoe.set_ffn_path(old)
     assert np.array_equal(host(route.perm), r["perm"]) and np.array_equal(host(route.offsets), r["offsets"])
