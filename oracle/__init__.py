@@ -247,6 +247,22 @@ def block_gemm(a, a_sc, w, w_sc, rows=None, threads=0):
     return y
 
 
+# ---------------------------------------------------------- shared expert
+def shared_expert(x, x_sc, w13, w13_sc, w2, w2_sc, rows=None, threads=0):
+    """The shared expert, a dense SwiGLU MLP on every row with block-32 FP8
+    operands (forum thread post #6, "Kernel by kernel against B12X": the shared
+    expert's two kernels per call; TP4 README, settings table, row "Kernels",
+    and its boot-log lines: the shared expert's down weight (5120, 576), K = 576
+    padded to 640 there): h = x . W13^T (fp32, W13 [2I][H], rows [0, I) gate,
+    [I, 2I) up), a = silu(gate) * up requantized to E4M3 block-32 (the same
+    routine as the routed experts), y = a . W2^T (fp32, W2 [H][I]).  Returns
+    y [len(rows), H] and the intermediate (h, q, q_sc)."""
+    h = block_gemm(x, x_sc, w13, w13_sc, rows=rows, threads=threads)
+    q, q_sc, _ = swiglu_requant(h)
+    y = block_gemm(q, q_sc, w2, w2_sc, threads=threads)
+    return y, h, q, q_sc
+
+
 # ---------------------------------------------------------- router logits
 def router_logits(h, wg, rows=None, threads=0):
     """fp32 logits [len(rows), E] = decoded h[rows] @ decoded wg^T (bf16 bit patterns h [T, H], wg [E, H])."""
