@@ -318,6 +318,40 @@ def main():
                     pct_bf16_peak=round(100 * flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
                     bytes=nbytes, flop=flop, variant=mxmoe.last_variant(), gate_copies=R)
 
+    # ------------------------------------------------------------ shared expert
+    def run_shared_expert(cfg, inp, steps, warmup):
+        """moe_shared_expert (FP8 gate/up [2I][H], SwiGLU + requant, FP8 down [H][I],
+        K = I = 576 unpadded) on the layer's own rows, with enough weight copies
+        to leave the caches at decode sizes."""
+        T, H, I = cfg.T, cfg.H, cfg.I
+        x = torch.from_numpy(inp.x).to(dev).to(torch.bfloat16)
+        xq, xsc = quantize(x, mxmoe.MX_FMT_E4M3)
+        w13, w2 = synth.shared_expert_weights(cfg)
+        W = quantize(torch.from_numpy(w13).to(dev), mxmoe.MX_FMT_E4M3) + \
+            quantize(torch.from_numpy(w2).to(dev), mxmoe.MX_FMT_E4M3)
+        wbytes = sum(t.numel() for t in W)
+        R = 2 if T >= 1024 else max(2, int(np.ceil(1.0e9 / wbytes)))
+        copies = [W] + [tuple(t.clone() for t in W) for _ in range(R - 1)]
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(mxmoe.moe_shared_expert_workspace_bytes(T, H, I), dtype=torch.uint8, device=dev)
+        for i in range(warmup):
+            mxmoe.moe_shared_expert(xq, xsc, *copies[i % R], y, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            mxmoe.moe_shared_expert(xq, xsc, *copies[i % R], y, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbytes = wbytes + T * (H + H // 32) + T * H * 4
+        flop = 2 * T * (2 * I) * H + 2 * T * H * I
+        return dict(T=T, H=H, I=I, ms=round(ms, 5), gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    pct_hbm_peak=round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                    tflops=round(flop / (ms * 1e-3) / 1e12, 2),
+                    pct_fp8_peak=round(100 * flop / (ms * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 2),
+                    bytes=nbytes, flop=flop, weight_copies=R, variant=mxmoe.last_variant())
+
     # ------------------------------------------------------------ prefill
     def run_prefill(steps, warmup):
         cfg = synth.PREFILL
@@ -355,7 +389,8 @@ def main():
         combine_bytes = P * H * 4 + T * H * 4 + T * k * 8
         dense = run_dense_prefill(T, steps, warmup)
         router = run_router_logits(cfg, inp, steps, warmup)
-        return dict(router_logits=router, tflops=round(tf(flop, ffn_ms), 2), pct_fp8_peak=round(100 * tf(flop, ffn_ms) / MFMA_FP8_PEAK_TFLOPS, 2),
+        shared = run_shared_expert(cfg, inp, steps, warmup)
+        return dict(router_logits=router, shared_expert=shared, tflops=round(tf(flop, ffn_ms), 2), pct_fp8_peak=round(100 * tf(flop, ffn_ms) / MFMA_FP8_PEAK_TFLOPS, 2),
                     dense_gemm=dense,
                     expert_gemms_tflops=round(tf(flop, gu_ms + dn_ms), 2),
                     expert_gemms_pct_fp8_peak=round(100 * tf(flop, gu_ms + dn_ms) / MFMA_FP8_PEAK_TFLOPS, 2),
@@ -381,6 +416,7 @@ def main():
                                            "expert_gemms_pct_fp4_peak", "ffn_ms")},
             "dense_gemm": pre["dense_gemm"],
             "router_logits": pre["router_logits"],
+            "shared_expert": pre["shared_expert"],
             "config": {"workload": "prefill MoE chunk: T=8192, H=4096, E=256, top-8, I=576, MXFP4 experts, "
                                    "FP8 block-32 activations", "pairs": pre["pairs"]},
         })
@@ -389,6 +425,7 @@ def main():
         cfg = synth.DECODE if args.workload == "decode" else synth.VERIFY
         inp, touched = run_decode(cfg)
         result["router_logits"] = run_router_logits(cfg, inp, args.steps, args.warmup)
+        result["shared_expert"] = run_shared_expert(cfg, inp, args.steps, args.warmup)
         cpu_cfg = cfg
         if not args.no_prefill:
             pre, _ = run_prefill(5, 2)

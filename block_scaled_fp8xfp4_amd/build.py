@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmxmoe.so")
-SOURCES = ["quant.hip", "logits.hip", "route.hip", "ffn.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "logits.hip", "route.hip", "ffn.hip", "gemm.hip", "shared.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -179,12 +179,37 @@ mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w
   if (!a || !a_sc || !w || !w_sc || !y) return MX_EINVAL;
   if (M < 1 || N < 1 || K < 32 || K % 32 != 0) return MX_EINVAL;
   if (y_dtype != MX_OUT_BF16 && y_dtype != MX_OUT_F32) return MX_EINVAL;
-  if (N % 16 != 0 || K % 128 != 0 || K > 128 * 8 * mx::MAX_PARTS) return MX_EUNSUPPORTED;
+  if (N % 16 != 0 || K > 128 * 8 * mx::MAX_PARTS) return MX_EUNSUPPORTED;
   if ((int64_t)M * N >= (int64_t(1) << 31) || (int64_t)M * K >= (int64_t(1) << 40)) return MX_EUNSUPPORTED;
   if (!aligned(a, 16) || !aligned(w, 16) || !aligned(a_sc, 4) || !aligned(w_sc, 4) || !aligned(y, 4)) return MX_EINVAL;
   const char* v = "";
   const hipError_t e =
       mx::launch_block_gemm(a, a_sc, w, w_sc, M, N, K, y, y_dtype == MX_OUT_BF16, static_cast<hipStream_t>(stream), &v);
+  if (e == hipSuccess) g_variant = v;
+  return from_hip(e);
+}
+
+size_t moe_shared_expert_workspace_bytes(int T, int H, int I) {
+  if (T < 0 || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0) return 0;
+  return mx::shared_ws_bytes(T, H, I);
+}
+
+mx_status moe_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H, const uint8_t* w13,
+                            const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (T < 0 || H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0) return MX_EINVAL;
+  const int kmax = 128 * 8 * mx::MAX_PARTS;
+  if (H > kmax || I > kmax) return MX_EUNSUPPORTED;
+  if ((int64_t)T * H >= (int64_t(1) << 31) || (int64_t)T * 2 * I >= (int64_t(1) << 31)) return MX_EUNSUPPORTED;
+  if (!w13 || !w13_sc || !w2 || !w2_sc || (T > 0 && (!x || !x_sc || !y))) return MX_EINVAL;
+  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(y, 4) || !aligned(x_sc, 4) ||
+      !aligned(w13_sc, 4) || !aligned(w2_sc, 4) || !aligned(ws, 256))
+    return MX_EINVAL;
+  if (T == 0) { g_variant = "shared:empty"; return MX_OK; }
+  if (!ws || ws_bytes < mx::shared_ws_bytes(T, H, I)) return MX_EWORKSPACE;
+  const char* v = "";
+  const hipError_t e = mx::launch_shared_expert(x, x_sc, T, H, w13, w13_sc, w2, w2_sc, I, y, ws,
+                                                static_cast<hipStream_t>(stream), &v);
   if (e == hipSuccess) g_variant = v;
   return from_hip(e);
 }

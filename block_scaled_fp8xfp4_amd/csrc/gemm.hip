@@ -21,35 +21,52 @@
 namespace mx {
 
 constexpr int XCDS_GEMM = 8;                      // XCDs of an MI355X (block scheduling)
-constexpr int GEMM_PREFILL_MIN_M = 320;            // rows from which the tiled kernel beats the decode kernel (measured)
 
 __device__ __forceinline__ v8i fp8_pair(const u32x4& lo, const u32x4& hi) {
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-template <bool BF16_OUT, bool WHOLE>                            // WHOLE: K = 4 parts of 1024 exactly
+// K tail (TAIL: K % 128 != 0, e.g. the shared expert's K = 576): the last
+// step's 16-byte chunks past K are zero in registers and its scale blocks
+// past K are 127 (1.0), on both operands, in every kernel; scale rows are
+// then not dword-aligned and are read a byte at a time.
+template <bool TAIL>
+__device__ __forceinline__ u32x4 ld_chunk(const uint8_t* p, int kpos, int K) {   // p: 16 bytes at K position kpos
+  if (TAIL && kpos >= K) return u32x4{0u, 0u, 0u, 0u};
+  return ldg16(p);
+}
+// lane group g's scale of step s, in byte g (the MFMA is passed dword >> 8 g)
+template <bool TAIL>
+__device__ __forceinline__ uint32_t ld_scale(const uint8_t* row_sc, int s, int g, int nblk) {
+  if (!TAIL) return reinterpret_cast<const uint32_t*>(row_sc)[s];
+  const int b = 4 * s + g;
+  return (uint32_t)(b < nblk ? row_sc[b] : 127) << (8 * g);
+}
+
+template <bool BF16_OUT, bool WHOLE, bool TAIL>                 // WHOLE: K = 4 parts of 1024 exactly
 __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
                                                           const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sc,
                                                           int M, int N, int K, void* __restrict__ y) {
   __shared__ float red[MAX_PARTS][16][17];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
-  const int nsteps = WHOLE ? 4 * KPART_STEPS : K / KSTEP;
+  const int nsteps = WHOLE ? 4 * KPART_STEPS : (K + KSTEP - 1) / KSTEP;
+  const int nblk = K / 32;
   const int nparts = (nsteps + KPART_STEPS - 1) / KPART_STEPS;
   const int Kb = WHOLE ? 4 * KPART : K;
   const int n0 = blockIdx.x * 16;
   const int64_t n = n0 + col;
   const uint8_t* wp = w + n * Kb + g * 16;
-  const uint32_t* wsp = reinterpret_cast<const uint32_t*>(w_sc + n * (Kb / 32));
+  const uint8_t* wsp = w_sc + n * (Kb / 32);
   u32x4 blo[KPART_STEPS], bhi[KPART_STEPS];
   uint32_t bs[KPART_STEPS];
   auto load_w = [&](int s0) {
 #pragma unroll
     for (int m = 0; m < KPART_STEPS; ++m) {
       const int s = WHOLE ? s0 + m : min(s0 + m, nsteps - 1);
-      blo[m] = ldg16(wp + s * KSTEP);
-      bhi[m] = ldg16(wp + s * KSTEP + 64);
-      bs[m] = wsp[s];
+      blo[m] = ld_chunk<TAIL>(wp + s * KSTEP, s * KSTEP + 16 * g, K);
+      bhi[m] = ld_chunk<TAIL>(wp + s * KSTEP + 64, s * KSTEP + 64 + 16 * g, K);
+      bs[m] = ld_scale<TAIL>(wsp, s, g, nblk);
     }
   };
   // the activations of row tile rt for part q
@@ -58,13 +75,13 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint8_t* __restr
     const int s0 = q * KPART_STEPS;
     const int m_row = min(rt * 16 + col, M - 1);               // rows past M repeat row M - 1
     const uint8_t* ap = a + (int64_t)m_row * Kb + g * 16;
-    const uint32_t* asp = reinterpret_cast<const uint32_t*>(a_sc + (int64_t)m_row * (Kb / 32));
+    const uint8_t* asp = a_sc + (int64_t)m_row * (Kb / 32);
 #pragma unroll
     for (int m = 0; m < KPART_STEPS; ++m) {
       const int s = WHOLE ? s0 + m : min(s0 + m, nsteps - 1);
-      A.lo[m] = ldg16(ap + s * KSTEP);
-      A.hi[m] = ldg16(ap + s * KSTEP + 64);
-      A.s[m] = asp[s];
+      A.lo[m] = ld_chunk<TAIL>(ap + s * KSTEP, s * KSTEP + 16 * g, K);
+      A.hi[m] = ld_chunk<TAIL>(ap + s * KSTEP + 64, s * KSTEP + 64 + 16 * g, K);
+      A.s[m] = ld_scale<TAIL>(asp, s, g, nblk);
     }
   };
   // row tile against part q, whose weights are in registers
@@ -137,7 +154,7 @@ struct GpStage {
   uint32_t bs[GP_BN];
 };
 
-template <bool BF16_OUT>
+template <bool BF16_OUT, bool TAIL>
 __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
                                                               const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sc,
                                                               int M, int N, int K, void* __restrict__ y) {
@@ -146,7 +163,8 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t* __r
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nsteps = K / KSTEP;
+  const int nsteps = (K + KSTEP - 1) / KSTEP;
+  const int nblk = K / 32;
   const int nrt = (M + GP_BM - 1) / GP_BM, nct = (N + GP_BN - 1) / GP_BN;
   const int nsbr = (nrt + 7) / 8, nsbc = (nct + 7) / 8;
   const uint32_t st_lds = __builtin_amdgcn_readfirstlane(lds_addr(&st[0]));
@@ -162,25 +180,52 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t* __r
       lds_barrier();                                            // the previous tile's LDS reads are done
       // this thread's slots: rows past M / N repeat the last row (results discarded)
       uint32_t aoff[4], boff[4];
+      int cpos[4];                                              // K position of each slot's chunk within a step
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int p = q * 256 + tid;
         const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
         aoff[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c * 16;
         boff[q] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + c * 16;
+        cpos[q] = c * 16;
       }
       const int sr = (wave & 1) * 64 + lane;                    // scale row of this lane: waves 0-1 A, 2-3 B
       const uint32_t soff = (uint32_t)min((wave < 2 ? m0 : n0) + sr, (wave < 2 ? M : N) - 1) * (uint32_t)(K / 32);
+      const uint8_t* srow = (wave < 2 ? a_sc : w_sc) + soff;    // TAIL: scale rows are read a byte at a time
+      uint32_t sreg = 0;                                        // TAIL: the issued step's scale dword
       auto issue = [&](int s, int bf) {
         const uint32_t d = st_lds + bf * (uint32_t)sizeof(GpStage);
+        if (!TAIL) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dma16_to_lds(a + s * KSTEP, aoff[q], d + (uint32_t)offsetof(GpStage, a) + (q * 256 + wave * 64) * 16);
+          for (int q = 0; q < 4; ++q)
+            dma16_to_lds(a + s * KSTEP, aoff[q], d + (uint32_t)offsetof(GpStage, a) + (q * 256 + wave * 64) * 16);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dma16_to_lds(w + s * KSTEP, boff[q], d + (uint32_t)offsetof(GpStage, b) + (q * 256 + wave * 64) * 16);
-        if (wave < 2) dma4_to_lds(a_sc + s * 4, soff, d + (uint32_t)offsetof(GpStage, as) + (wave & 1) * 256);
-        else dma4_to_lds(w_sc + s * 4, soff, d + (uint32_t)offsetof(GpStage, bs) + (wave & 1) * 256);
+          for (int q = 0; q < 4; ++q)
+            dma16_to_lds(w + s * KSTEP, boff[q], d + (uint32_t)offsetof(GpStage, b) + (q * 256 + wave * 64) * 16);
+          if (wave < 2) dma4_to_lds(a_sc + s * 4, soff, d + (uint32_t)offsetof(GpStage, as) + (wave & 1) * 256);
+          else dma4_to_lds(w_sc + s * 4, soff, d + (uint32_t)offsetof(GpStage, bs) + (wave & 1) * 256);
+        } else {
+          // chunks past K read their row's first chunk (in bounds) and are
+          // zeroed in LDS once they have landed
+          const uint32_t k0 = (uint32_t)s * KSTEP;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool in = (int)k0 + cpos[q] < K;
+            dma16_to_lds(a, in ? aoff[q] + k0 : aoff[q] - cpos[q], d + (uint32_t)offsetof(GpStage, a) + (q * 256 + wave * 64) * 16);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool in = (int)k0 + cpos[q] < K;
+            dma16_to_lds(w, in ? boff[q] + k0 : boff[q] - cpos[q], d + (uint32_t)offsetof(GpStage, b) + (q * 256 + wave * 64) * 16);
+          }
+          uint32_t v = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int blk = 4 * s + b;
+            v |= (uint32_t)(blk < nblk ? srow[blk] : 127) << (8 * b);
+          }
+          sreg = v;
+        }
       };
 
       v4f tot[4][4], cur[4][4];
@@ -234,6 +279,20 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t* __r
       issue(0, 0);
       for (int s = 0; s < nsteps; ++s) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (TAIL) {
+          // this stage's scale dwords, and zeros in the chunks past K
+          GpStage& S = st[s & 1];
+          if (wave < 2) S.as[sr] = sreg;
+          else S.bs[sr] = sreg;
+          if (s == nsteps - 1) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (s * KSTEP + cpos[q] >= K) {
+                S.a[q * 256 + tid] = u32x4{0u, 0u, 0u, 0u};
+                S.b[q * 256 + tid] = u32x4{0u, 0u, 0u, 0u};
+              }
+          }
+        }
         lds_barrier();
         if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
         compute(st[s & 1]);
@@ -270,22 +329,34 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t* __r
 
 hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,
                              int M, int N, int K, void* y, bool bf16_out, hipStream_t stream, const char** variant) {
+  const bool tail = K % KSTEP != 0;
   if (M >= GEMM_PREFILL_MIN_M) {
     const int tiles = ((M + GP_BM - 1) / GP_BM) * ((N + GP_BN - 1) / GP_BN);
     const int per_xcd = tiles / XCDS_GEMM < 64 ? (tiles + XCDS_GEMM - 1) / XCDS_GEMM : 64;   // 2 per CU at most
     const dim3 gp(per_xcd * XCDS_GEMM);
-    if (bf16_out) hipLaunchKernelGGL((gemm_prefill_kernel<true>), gp, dim3(256), 0, stream, a, a_sc, w, w_sc, M, N, K, y);
-    else hipLaunchKernelGGL((gemm_prefill_kernel<false>), gp, dim3(256), 0, stream, a, a_sc, w, w_sc, M, N, K, y);
-    *variant = bf16_out ? "gemm:prefill128x128_bf16" : "gemm:prefill128x128_f32";
+#define MX_GP(B, T) hipLaunchKernelGGL((gemm_prefill_kernel<B, T>), gp, dim3(256), 0, stream, a, a_sc, w, w_sc, M, N, K, y)
+    if (bf16_out) { if (tail) MX_GP(true, true); else MX_GP(true, false); }
+    else { if (tail) MX_GP(false, true); else MX_GP(false, false); }
+#undef MX_GP
+    *variant = bf16_out ? (tail ? "gemm:prefill128x128_ktail_bf16" : "gemm:prefill128x128_bf16")
+                        : (tail ? "gemm:prefill128x128_ktail_f32" : "gemm:prefill128x128_f32");
     return hipGetLastError();
   }
   const dim3 grid(N / 16), block(256);
   const bool whole = K == 4 * KPART;
-  if (bf16_out && whole) hipLaunchKernelGGL((gemm_decode_kernel<true, true>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
-  else if (bf16_out) hipLaunchKernelGGL((gemm_decode_kernel<true, false>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
-  else if (whole) hipLaunchKernelGGL((gemm_decode_kernel<false, true>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
-  else hipLaunchKernelGGL((gemm_decode_kernel<false, false>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y);
-  *variant = bf16_out ? "gemm:decode16_kpart4_bf16" : "gemm:decode16_kpart4_f32";
+#define MX_GD(B, W, T) hipLaunchKernelGGL((gemm_decode_kernel<B, W, T>), grid, block, 0, stream, a, a_sc, w, w_sc, M, N, K, y)
+  if (bf16_out) {
+    if (whole) MX_GD(true, true, false);
+    else if (tail) MX_GD(true, false, true);
+    else MX_GD(true, false, false);
+  } else {
+    if (whole) MX_GD(false, true, false);
+    else if (tail) MX_GD(false, false, true);
+    else MX_GD(false, false, false);
+  }
+#undef MX_GD
+  *variant = bf16_out ? (tail ? "gemm:decode16_kpart4_ktail_bf16" : "gemm:decode16_kpart4_bf16")
+                      : (tail ? "gemm:decode16_kpart4_ktail_f32" : "gemm:decode16_kpart4_f32");
   return hipGetLastError();
 }
 

@@ -37,12 +37,18 @@ bool ffn_path_supported(int path, int H, int I);
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant);
 void set_ffn_phase_events(const hipEvent_t* ev, int n);
 
+constexpr int GEMM_PREFILL_MIN_M = 320;  // dense GEMM: rows from which the tiled kernel beats the decode kernel (measured)
 hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,
                              int M, int N, int K, void* y, bool bf16_out, hipStream_t stream, const char** variant);
 
 size_t router_logits_ws_bytes(int T, int H, int E);
 hipError_t launch_router_logits(const uint16_t* h, int T, int H, const uint16_t* wg, int E, float* logits, void* ws,
                                 hipStream_t stream, const char** variant);
+
+size_t shared_ws_bytes(int T, int H, int I);
+hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H, const uint8_t* w13,
+                                const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,
+                                void* ws, hipStream_t stream, const char** variant);
 
 int num_cus();
 hipError_t launch_check_requant(uint32_t lo, uint32_t hi, unsigned long long* nbad, hipStream_t stream);

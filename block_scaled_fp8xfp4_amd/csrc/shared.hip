@@ -1,0 +1,71 @@
+// Shared expert: a dense SwiGLU MLP applied to every row, with block-32 FP8
+// operands ("New Deepseek 4.1 flash recipe" thread, post #6, "Kernel by
+// kernel against B12X": the shared expert's two kernels per call, on a side
+// stream; DeepSeek-V4.1-Flash-4x-DGX-Spark-TP4 README, settings table, row
+// "Kernels", and its boot-log lines: the shared expert's down weight is
+// (5120, 576) and was padded to K = 640 for the kernels there).
+//
+// h = x . W13^T (fp32, dense FP8 GEMM), a = silu(gate) * up requantized to
+// E4M3 block-32 by the routed experts' own routine, y = a . W2^T with K = I
+// (576 is 4.5 MFMA steps: the GEMM kernels zero the half step in registers
+// or LDS, no padded copy of the weight exists).  The GEMMs keep the dense
+// projection's canonical order, so rows do not depend on the batch.
+#include "mx_device.hpp"
+#include "mx_launch.hpp"
+
+namespace mx {
+
+// One thread per pair of adjacent intermediate columns: 16 lanes (a DPP row)
+// cover one block of 32, so the block's amax is a row maximum in registers.
+// h row t: gate at [0, I), up at [I, 2I).
+__global__ __launch_bounds__(256) void swiglu_requant_kernel(const float* __restrict__ h, int T, int I,
+                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ q_sc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // pair index over [T][I / 2]
+  const int64_t n = (int64_t)T * (I / 2);
+  const bool ok = i < n;                                        // whole DPP rows are in or out (I / 2 % 16 == 0)
+  const int64_t t = ok ? i / (I / 2) : 0;
+  const int c = ok ? (int)(i % (I / 2)) * 2 : 0;
+  const float* hr = h + t * 2 * I;
+  float a0 = 0.f, a1 = 0.f;
+  if (ok) {
+    const float2 g = *reinterpret_cast<const float2*>(hr + c);
+    const float2 u = *reinterpret_cast<const float2*>(hr + I + c);
+    a0 = swiglu(g.x, u.x);
+    a1 = swiglu(g.y, u.y);
+  }
+  const float amax = row16_max(fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
+  const uint32_t sc = e8m0_code_for_amax(amax, 8);
+  if (!ok) return;
+  *reinterpret_cast<uint16_t*>(q + t * I + c) = (uint16_t)requant2_e4m3(a0, a1, sc);
+  if ((c & 31) == 0) q_sc[t * (I / 32) + c / 32] = (uint8_t)sc;
+}
+
+size_t shared_ws_bytes(int T, int H, int I) {
+  (void)H;
+  const size_t hb = ((size_t)T * 2 * I * 4 + 255) / 256 * 256;
+  const size_t qb = ((size_t)T * I + 255) / 256 * 256;
+  return hb + qb + ((size_t)T * (I / 32) + 255) / 256 * 256;
+}
+
+hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H, const uint8_t* w13,
+                                const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,
+                                void* ws, hipStream_t stream, const char** variant) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* h = reinterpret_cast<float*>(base);
+  uint8_t* q = base + ((size_t)T * 2 * I * 4 + 255) / 256 * 256;
+  uint8_t* q_sc = q + ((size_t)T * I + 255) / 256 * 256;
+  const char* v = "";
+  hipError_t e = launch_block_gemm(x, x_sc, w13, w13_sc, T, 2 * I, H, h, false, stream, &v);
+  if (e != hipSuccess) return e;
+  const int64_t pairs = (int64_t)T * (I / 2);
+  hipLaunchKernelGGL(swiglu_requant_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, stream, h, T, I, q,
+                     q_sc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_block_gemm(q, q_sc, w2, w2_sc, T, H, I, y, false, stream, &v);
+  *variant = T >= GEMM_PREFILL_MIN_M ? "shared:gemm_prefill+swiglu_requant+gemm_prefill"
+                                     : "shared:gemm_decode+swiglu_requant+gemm_decode";
+  return e;
+}
+
+}  // namespace mx

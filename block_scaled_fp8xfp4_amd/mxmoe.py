@@ -18,7 +18,8 @@ MX_OUT_BF16, MX_OUT_F32 = 0, 1
 # every entry point declared in include/mxmoe.h
 EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logits", "moe_route_workspace_bytes", "moe_route", "moe_route_live", "moe_expert_ffn_workspace_bytes",
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
-           "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events")
+           "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events",
+           "moe_shared_expert_workspace_bytes", "moe_shared_expert")
 
 _lib = None
 
@@ -58,6 +59,10 @@ def load():
     lib.moe_expert_ffn.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, P, I32, I32, P, P, SZ, P]
     lib.fp8_block_gemm.restype = I32
     lib.fp8_block_gemm.argtypes = [P, P, P, P, I32, I32, I32, P, I32, P]
+    lib.moe_shared_expert_workspace_bytes.restype = SZ
+    lib.moe_shared_expert_workspace_bytes.argtypes = [I32, I32, I32]
+    lib.moe_shared_expert.restype = I32
+    lib.moe_shared_expert.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, SZ, P]
     lib.mx_status_string.restype = ctypes.c_char_p
     lib.mx_status_string.argtypes = [I32]
     lib.mx_last_variant.restype = ctypes.c_char_p
@@ -176,6 +181,21 @@ def fp8_block_gemm(a, a_sc, w, w_sc, y, y_dtype, stream=None):
     N = w.shape[0]
     _check(load().fp8_block_gemm(_ptr(a), _ptr(a_sc), _ptr(w), _ptr(w_sc), M, N, K, _ptr(y), y_dtype,
                                  _stream(stream)), "fp8_block_gemm")
+
+
+def moe_shared_expert_workspace_bytes(T, H, I):
+    return load().moe_shared_expert_workspace_bytes(T, H, I)
+
+
+def moe_shared_expert(x, x_sc, w13, w13_sc, w2, w2_sc, y, ws, stream=None):
+    """y [T, H] fp32 = shared expert of x (FP8 [T, H] + scales); w13 [2I, H], w2 [H, I] FP8 + scales."""
+    T, H = x.shape
+    I = w2.shape[1]
+    if tuple(w13.shape) != (2 * I, H) or tuple(y.shape) != (T, H):
+        raise ValueError("moe_shared_expert: shape mismatch")
+    _check(load().moe_shared_expert(_ptr(x), _ptr(x_sc), T, H, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I,
+                                    _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_shared_expert")
 
 
 def check_requant(lo, hi, mismatches, stream=None):

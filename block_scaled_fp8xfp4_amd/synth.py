@@ -21,6 +21,8 @@ Workloads (sizes, distributions and structure), one per seed 0..4:
          replacement, popularity Zipf(1.1))
   prefill T=8192, same layer; logits N(0,1)
 Activations are N(0,1) rounded to bf16; weights are N(0, 0.02^2) in fp32.
+Shared expert: W13 [2I][H] and W2 [H][I], N(0, 0.02^2) in fp32, from the
+stream SeedSequence([seed, 9]) (quantized to E4M3 block-32 by each side).
 Router gate (the linear map whose scores the top-k gate ranks): bf16-valued
 N(0, 1/H) rows [E][H] from the stream SeedSequence([seed, 7]), so that the
 workload's bf16 hidden rows give logits of unit variance, like the drawn
@@ -203,3 +205,15 @@ def router_gate(cfg, E=None, H=None):
 def hidden_rows(seed, T, H):
     """bf16-valued N(0,1) hidden rows [T][H] of an arbitrary (small) shape."""
     return _to_bf16_values(_normal(np.random.SeedSequence([seed, 8]), (T, H)))
+
+
+def shared_expert_weights(cfg, H=None, I=None):
+    """fp32 shared-expert weights (W13 [2I][H], W2 [H][I]), N(0, 0.02^2)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    H = cfg.H if H is None else H
+    I = cfg.I if I is None else I
+    g = _gen(np.random.SeedSequence([cfg.seed, 9]))
+    w13 = g.standard_normal((2 * I, H), dtype=np.float32) * np.float32(WEIGHT_STD)
+    w2 = g.standard_normal((H, I), dtype=np.float32) * np.float32(WEIGHT_STD)
+    return w13, w2

@@ -197,11 +197,37 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H,
  * a FP8 [M][K] + a_sc SC [M][K/32];  w FP8 [N][K] + w_sc SC [N][K/32].
  * y[m][n] = sum_k a[m][k] * w[n][k] (decoded), fp32 accumulate in one fixed
  * order per element; y is [M][N] bf16 (MX_OUT_BF16, RNE of the fp32 result)
- * or fp32 (MX_OUT_F32).  Supported: K % 128 == 0, N % 16 == 0, M >= 1.
+ * or fp32 (MX_OUT_F32).  Supported: K % 32 == 0 (a K that is not a multiple
+ * of 128 ends in a partial MFMA step, zero-filled on both operands; scale
+ * rows then need no alignment), K <= 16384, N % 16 == 0, M >= 1.
  */
 mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc,
                          const uint8_t* w, const uint8_t* w_sc,
                          int M, int N, int K, void* y, int y_dtype, void* stream);
+
+/*
+ * Shared expert: a dense SwiGLU MLP on every row with block-32 FP8 operands
+ * (post #6 "Kernel by kernel against B12X": the shared expert's two kernels
+ * per call; TP4 README, settings table, row "Kernels", and its boot-log
+ * lines: the shared expert's down weight (5120, 576), K padded to 640 there;
+ * here K = I is used as is).
+ * x   FP8 [T][H] + x_sc SC [T][H/32];  w13 FP8 [2I][H] + w13_sc SC [2I][H/32]
+ * (rows [0, I) gate, [I, 2I) up);  w2 FP8 [H][I] + w2_sc SC [H][I/32].
+ * y   fp32 [T][H] = requant_fp8(silu(x.gate^T) * (x.up^T)) . w2^T, each GEMM
+ *     in the dense projection's fixed order (fp8_block_gemm), the requant
+ *     the routed experts' (E4M3 block-32 along I).
+ * Supported: H % 32 == 0, I % 32 == 0 (no K % 128 restriction), H, I <=
+ * 16384, T*H and T*2I < 2^31.  x, w13, w2 16-byte aligned; scales and y
+ * 4-byte aligned.  ws: moe_shared_expert_workspace_bytes(T, H, I) bytes
+ * (256-byte aligned, contents ignored): the fp32 gate/up values
+ * [T][2I], then the FP8 intermediate [T][I] and its scales [T][I/32], each
+ * 256-byte aligned.  Asynchronous on stream.
+ */
+size_t    moe_shared_expert_workspace_bytes(int T, int H, int I);
+mx_status moe_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H,
+                            const uint8_t* w13, const uint8_t* w13_sc,
+                            const uint8_t* w2, const uint8_t* w2_sc, int I,
+                            float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Name of a status code (static string). */
 const char* mx_status_string(mx_status s);

@@ -129,7 +129,7 @@ def gemm(lib, M=1, N=64, K=256, ydt=0, a=FAKE):
 def test_gemm_rejects_bad_arguments(lib):
     assert gemm(lib, M=0) == mxmoe.MX_EINVAL
     assert gemm(lib, K=100) == mxmoe.MX_EINVAL
-    assert gemm(lib, K=96) == mxmoe.MX_EUNSUPPORTED
+    assert gemm(lib, K=16384 + 128) == mxmoe.MX_EUNSUPPORTED
     assert gemm(lib, N=40) == mxmoe.MX_EUNSUPPORTED
     assert gemm(lib, ydt=5) == mxmoe.MX_EINVAL
     assert gemm(lib, a=None) == mxmoe.MX_EINVAL
@@ -158,6 +158,24 @@ def test_router_logits_rejects_bad_arguments(lib):
     assert logits(lib, ws_bytes=need - 1) == mxmoe.MX_EWORKSPACE
     assert logits(lib, T=0, h=None, out=None, ws=None) == mxmoe.MX_OK   # nothing to do, nothing launched
     assert mxmoe.moe_router_logits_workspace_bytes(1, 100, 8) == 0      # invalid shape
+
+
+def shared(lib, T=4, H=256, I=64, x=FAKE, y=FAKE, ws=FAKE_WS, ws_bytes=1 << 30):
+    return lib.moe_shared_expert(x, FAKE, T, H, FAKE, FAKE, FAKE, FAKE, I, y, ws, ws_bytes, None)
+
+
+def test_shared_expert_rejects_bad_arguments(lib):
+    assert shared(lib, T=-1) == mxmoe.MX_EINVAL
+    assert shared(lib, H=100) == mxmoe.MX_EINVAL
+    assert shared(lib, I=48) == mxmoe.MX_EINVAL
+    assert shared(lib, H=16384 + 32) == mxmoe.MX_EUNSUPPORTED
+    assert shared(lib, x=None) == mxmoe.MX_EINVAL
+    assert shared(lib, y=ctypes.c_void_p((1 << 20) + 2)) == mxmoe.MX_EINVAL
+    assert shared(lib, ws=None) == mxmoe.MX_EWORKSPACE
+    need = mxmoe.moe_shared_expert_workspace_bytes(4, 256, 64)
+    assert need >= 4 * 128 * 4 + 4 * 64 + 4 * 2
+    assert shared(lib, ws_bytes=need - 1) == mxmoe.MX_EWORKSPACE
+    assert shared(lib, T=0, x=None, y=None, ws=None) == mxmoe.MX_OK       # nothing to do, nothing launched
 
 
 def test_path_switch(lib):

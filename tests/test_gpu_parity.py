@@ -255,13 +255,15 @@ def test_gemm_dense_workload(M):
     check_gemm(inp.a[:M], inp.w, rows=None if M == 1 else np.arange(0, 16, 3, dtype=np.int32))
 
 
-@pytest.mark.parametrize("M,N,K", [(21, 48, 384), (1, 16, 128), (40, 272, 2176), (3, 4096, 1024)])
+@pytest.mark.parametrize("M,N,K", [(21, 48, 384), (1, 16, 128), (40, 272, 2176), (3, 4096, 1024),
+                                   (1, 64, 576), (5, 4096, 576), (16, 272, 96), (3, 48, 32), (7, 32, 1120)])
 def test_gemm_shapes(M, N, K):
     a, w = gemm_case(M, N, K, M + N + K)
     check_gemm(a, w)
 
 
-@pytest.mark.parametrize("M,N,K", [(320, 128, 1024), (333, 272, 2176), (520, 4096, 4096)])
+@pytest.mark.parametrize("M,N,K", [(320, 128, 1024), (333, 272, 2176), (520, 4096, 4096),
+                                   (333, 272, 576), (330, 128, 1120), (321, 64, 32)])
 def test_gemm_prefill_shapes(M, N, K):
     """The tiled kernel (M >= 320): ragged row and column tiles, a partial
     last K part; sampled rows against the oracle."""
@@ -283,6 +285,23 @@ def test_gemm_prefill_rows_equal_decode_rows():
     full = host(full)
     for m0, m1 in [(0, 1), (127, 128), (128, 144), (320, 333)]:
         y = torch.empty((m1 - m0, 272), dtype=torch.float32, device="cuda")
+        mxmoe.fp8_block_gemm(dev(aq[m0:m1]), dev(asc[m0:m1]), dev(wq), dev(wsc), y, mxmoe.MX_OUT_F32)
+        assert mxmoe.last_variant().startswith("gemm:decode")
+        assert np.array_equal(host(y), full[m0:m1]), (m0, m1)
+
+
+def test_gemm_k_tail_rows_equal_across_kernels():
+    """K = 576 (4.5 MFMA steps, scale rows of 18 bytes): rows of the tiled
+    kernel equal the decode kernel's, bit for bit."""
+    a, w = gemm_case(333, 4096, 576, 13)
+    aq, asc = oracle.quantize_e4m3(a)
+    wq, wsc = oracle.quantize_e4m3(w)
+    full = torch.empty((333, 4096), dtype=torch.float32, device="cuda")
+    mxmoe.fp8_block_gemm(dev(aq), dev(asc), dev(wq), dev(wsc), full, mxmoe.MX_OUT_F32)
+    assert "ktail" in mxmoe.last_variant() and mxmoe.last_variant().startswith("gemm:prefill")
+    full = host(full)
+    for m0, m1 in [(0, 1), (100, 116), (332, 333)]:
+        y = torch.empty((m1 - m0, 4096), dtype=torch.float32, device="cuda")
         mxmoe.fp8_block_gemm(dev(aq[m0:m1]), dev(asc[m0:m1]), dev(wq), dev(wsc), y, mxmoe.MX_OUT_F32)
         assert mxmoe.last_variant().startswith("gemm:decode")
         assert np.array_equal(host(y), full[m0:m1]), (m0, m1)

@@ -1,0 +1,104 @@
+"""GPU parity of the shared expert (moe_shared_expert: FP8 gate/up GEMM,
+SwiGLU + E4M3 requant, FP8 down GEMM with K = I = 576 unpadded) against the
+oracle through the C-ABI, staged on identical inputs like the routed FFN,
+on the decode, verification and prefill row counts; rows bitwise
+independent of the batch."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_fp8xfp4_amd import mxmoe, synth
+from gpu_common import assert_close, dev, host, say
+from test_gpu_parity import E2E_TOL, check_requant
+
+pytestmark = pytest.mark.gpu
+
+
+class Shared:
+    def __init__(self, cfg, H=None, I=None, T=None):
+        inp = synth.moe_inputs(cfg)
+        c = inp.cfg
+        self.H = c.H if H is None else H
+        self.I = c.I if I is None else I
+        x = inp.x if H is None else synth.hidden_rows(c.seed, c.T, self.H)
+        x = x if T is None else np.resize(x, (T, self.H))
+        w13, w2 = synth.shared_expert_weights(c, self.H, self.I)
+        self.x, self.x_sc = oracle.quantize_e4m3(x)
+        self.w13, self.w13_sc = oracle.quantize_e4m3(w13)
+        self.w2, self.w2_sc = oracle.quantize_e4m3(w2)
+        self.d = {k: dev(getattr(self, k)) for k in ("x", "x_sc", "w13", "w13_sc", "w2", "w2_sc")}
+
+    def gpu(self, rows=None):
+        x, xs = self.d["x"], self.d["x_sc"]
+        if rows is not None:
+            idx = dev(np.asarray(rows, np.int64))
+            x, xs = x[idx].contiguous(), xs[idx].contiguous()
+        T = x.shape[0]
+        y = torch.empty((T, self.H), dtype=torch.float32, device="cuda")
+        ws = torch.full((mxmoe.moe_shared_expert_workspace_bytes(T, self.H, self.I),), 0xFF, dtype=torch.uint8,
+                        device="cuda")
+        mxmoe.moe_shared_expert(x, xs, self.d["w13"], self.d["w13_sc"], self.d["w2"], self.d["w2_sc"], y, ws)
+        variant = mxmoe.last_variant()
+        I = self.I
+        hb = ((T * 2 * I * 4 + 255) // 256) * 256
+        qb = ((T * I + 255) // 256) * 256
+        wsh = host(ws)
+        h = wsh[:T * 2 * I * 4].view(np.float32).reshape(T, 2 * I)
+        q = wsh[hb:hb + T * I].reshape(T, I)
+        q_sc = wsh[hb + qb:hb + qb + T * (I // 32)].reshape(T, I // 32)
+        return host(y), h, q, q_sc, variant
+
+
+def staged_parity(S, rows, what, e2e_tol=E2E_TOL):
+    y, h, q, q_sc, variant = S.gpu()
+    rows = np.asarray(rows, np.int32)
+    # (i) gate/up GEMM
+    h_ref = oracle.block_gemm(S.x, S.x_sc, S.w13, S.w13_sc, rows=rows)
+    assert_close(h[rows], h_ref, what + " gate/up")
+    # (ii) SwiGLU + requant on the GPU's own h
+    q_ref, sc_ref, a_ref = oracle.swiglu_requant(h[rows])
+    flips = check_requant(q[rows], q_sc[rows], q_ref, sc_ref, a_ref)
+    assert flips <= max(2, len(rows) * S.I // 10000), flips
+    # (iii) down GEMM from the GPU's intermediate
+    y_ref2 = oracle.block_gemm(q, q_sc, S.w2, S.w2_sc, rows=rows)
+    assert_close(y[rows], y_ref2, what + " down")
+    # end to end
+    ref, *_ = oracle.shared_expert(S.x, S.x_sc, S.w13, S.w13_sc, S.w2, S.w2_sc, rows=rows)
+    err = np.abs(y[rows] - ref).max() / np.abs(ref).max()
+    say(f"{what}: end-to-end max|diff|/max|ref| = {err:.2e} ({variant})")
+    assert err <= e2e_tol
+    return y, variant
+
+
+@pytest.mark.parametrize("name", ["decode", "verify"])
+def test_shared_expert_workloads(name):
+    S = Shared(name)
+    T = S.x.shape[0]
+    _, variant = staged_parity(S, np.arange(T), f"shared {name}")
+    assert "decode" in variant
+
+
+def test_shared_expert_prefill_sampled_rows():
+    S = Shared("prefill")
+    rows = np.concatenate([np.random.default_rng(9).choice(8192, 24, replace=False), [0, 8191]])
+    _, variant = staged_parity(S, rows, "shared prefill")
+    assert "prefill" in variant
+
+
+@pytest.mark.parametrize("H,I", [(256, 64), (384, 96), (1152, 160)])
+def test_shared_expert_small_shapes(H, I):
+    S = Shared("tiny", H=H, I=I)
+    # a short intermediate: one requant flip is a larger share of y (as for the routed FFN)
+    staged_parity(S, np.arange(S.x.shape[0]), f"shared H={H} I={I}", e2e_tol=3e-2)
+
+
+def test_shared_expert_rows_do_not_depend_on_the_batch():
+    """Rows of a 400-row call (tiled GEMMs) equal the same rows run alone and
+    in 16-row batches (decode GEMMs), bit for bit."""
+    S = Shared("verify", T=400)
+    full, *_ = S.gpu()
+    for rows in ([0], [399], list(range(100, 116)), [5, 250, 17]):
+        part, *_ , v = S.gpu(rows)
+        assert "decode" in v
+        assert np.array_equal(part, full[rows]), rows
