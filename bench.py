@@ -74,6 +74,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay one HIP graph per step instead of eager launches")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="decode step: prefetch the dense projection's weights on a side stream from the step's start")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 256 MiB buffer 5 times (reference kernel for the HBM byte counters)")
     args = ap.parse_args()
@@ -148,12 +150,24 @@ def main():
         gcopies = [(gq, gsc)] + [(gq.clone(), gsc.clone()) for _ in range(R - 1)]
         torch.cuda.synchronize()
 
+        side = torch.cuda.Stream() if args.prefetch else None     # default priority
+        main = torch.cuda.current_stream()
+
         def step(i):
             w13q, w13s, w2q, w2s = copies[i % R]
+            g, gs = gcopies[i % R]
+            if side is not None:
+                # the dense weights stream into cache (each 16-row slice into the
+                # L2 of the XCD whose workgroup will read it) while route and FFN run
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    mxmoe.prefetch(g, 16 * dense.cfg.K)
+                    mxmoe.prefetch(gs, 16 * (dense.cfg.K // 32))
             route(logits, surv)
             ffn(xq, xsc, route, w13q, w13s, w2q, w2s)
-            g, gs = gcopies[i % R]
             mxmoe.fp8_block_gemm(aq, asc, g, gs, yg, mxmoe.MX_OUT_BF16)
+            if side is not None:
+                main.wait_stream(side)
 
         route(logits, surv)
         ffn(xq, xsc, route, *copies[0])
@@ -256,7 +270,8 @@ def main():
                                    f"FP8 block-32 activations, + dense FP8 block-32 projection M={T}, K=N=4096",
                        "rows": T, "hidden": H, "experts": E, "top_k": k, "intermediate": I,
                        "touched_experts": touched, "bytes_per_step": step_bytes, "weight_copies": R,
-                       "launch": "hip_graph_per_step" if args.graph else "eager"},
+                       "launch": "hip_graph_per_step" if args.graph else "eager",
+                       "prefetch": bool(args.prefetch)},
         })
         return inp, touched
 

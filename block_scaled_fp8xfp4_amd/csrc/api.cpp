@@ -214,6 +214,17 @@ mx_status moe_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H,
   return from_hip(e);
 }
 
+mx_status mx_prefetch(const void* p, uint64_t bytes, uint64_t chunk_bytes, void* stream) {
+  if (bytes == 0) return MX_OK;
+  if (!p || !aligned(p, 16)) return MX_EINVAL;
+  if (chunk_bytes == 0) chunk_bytes = 65536;
+  if (chunk_bytes % 16 != 0) return MX_EINVAL;
+  if ((bytes + chunk_bytes - 1) / chunk_bytes > (uint64_t(1) << 31) - 1) return MX_EUNSUPPORTED;
+  const hipError_t e = mx::launch_prefetch(p, bytes, chunk_bytes, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) g_variant = "prefetch:lds_dma";
+  return from_hip(e);
+}
+
 mx_status mx_check_requant(uint32_t lo, uint32_t hi, unsigned long long* mismatches, void* stream) {
   if (!mismatches || !aligned(mismatches, 8) || lo > hi || hi > 0x7F800000u) return MX_EINVAL;
   return from_hip(mx::launch_check_requant(lo, hi, mismatches, static_cast<hipStream_t>(stream)));

@@ -50,6 +50,8 @@ hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, in
                                 const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,
                                 void* ws, hipStream_t stream, const char** variant);
 
+hipError_t launch_prefetch(const void* p, uint64_t bytes, uint64_t chunk, hipStream_t stream);
+
 int num_cus();
 hipError_t launch_check_requant(uint32_t lo, uint32_t hi, unsigned long long* nbad, hipStream_t stream);
 

@@ -95,3 +95,33 @@ hipError_t launch_check_requant(uint32_t lo, uint32_t hi, unsigned long long* nb
 }
 
 }  // namespace mx
+
+namespace mx {
+
+// Weight prefetch (spark-ds41f README, "Current baseline": L2 weight prefetch
+// during decode, the next layer's weights and scale words streamed in while
+// latency-bound kernels run; TP4 README, settings table, row "L2 prefetch": a
+// side-stream kernel during idle phases, data untouched).  Workgroup i reads
+// chunk i of the range, so the chunk lands in the L2 of the XCD that runs
+// workgroup i and in the memory-side cache (MALL) shared by every XCD.  The
+// reads are LDS DMA into a scratch row per wavefront (no register ever holds
+// them, nothing is kept); the workgroup waits for all of them before it ends.
+// Whole 16-byte units only (p 16-byte aligned, chunk a multiple of 16).
+__global__ __launch_bounds__(256) void prefetch_kernel(const uint8_t* __restrict__ p, uint64_t bytes, uint64_t chunk) {
+  __shared__ u32x4 scratch[256];
+  const int wave = threadIdx.x >> 6;
+  const uint64_t c0 = (uint64_t)blockIdx.x * chunk;
+  const uint64_t c1 = c0 + chunk < bytes ? c0 + chunk : bytes;
+  for (uint64_t off = c0 + (uint64_t)threadIdx.x * 16; off + 16 <= c1; off += 256 * 16)
+    dma16_to_lds(p + off, &scratch[wave * 64]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+hipError_t launch_prefetch(const void* p, uint64_t bytes, uint64_t chunk, hipStream_t stream) {
+  const uint64_t n = (bytes + chunk - 1) / chunk;
+  hipLaunchKernelGGL(prefetch_kernel, dim3((unsigned)n), dim3(256), 0, stream, static_cast<const uint8_t*>(p), bytes,
+                     chunk);
+  return hipGetLastError();
+}
+
+}  // namespace mx

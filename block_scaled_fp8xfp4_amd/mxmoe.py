@@ -19,7 +19,7 @@ MX_OUT_BF16, MX_OUT_F32 = 0, 1
 EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logits", "moe_route_workspace_bytes", "moe_route", "moe_route_live", "moe_expert_ffn_workspace_bytes",
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
            "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events",
-           "moe_shared_expert_workspace_bytes", "moe_shared_expert")
+           "moe_shared_expert_workspace_bytes", "moe_shared_expert", "mx_prefetch")
 
 _lib = None
 
@@ -63,6 +63,8 @@ def load():
     lib.moe_shared_expert_workspace_bytes.argtypes = [I32, I32, I32]
     lib.moe_shared_expert.restype = I32
     lib.moe_shared_expert.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, SZ, P]
+    lib.mx_prefetch.restype = I32
+    lib.mx_prefetch.argtypes = [P, ctypes.c_uint64, ctypes.c_uint64, P]
     lib.mx_status_string.restype = ctypes.c_char_p
     lib.mx_status_string.argtypes = [I32]
     lib.mx_last_variant.restype = ctypes.c_char_p
@@ -196,6 +198,12 @@ def moe_shared_expert(x, x_sc, w13, w13_sc, w2, w2_sc, y, ws, stream=None):
     _check(load().moe_shared_expert(_ptr(x), _ptr(x_sc), T, H, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I,
                                     _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_shared_expert")
+
+
+def prefetch(t, chunk_bytes=0, stream=None, nbytes=None):
+    """Read tensor t's bytes (or its first nbytes) into cache; see mx_prefetch."""
+    n = t.numel() * t.element_size() if nbytes is None else nbytes
+    _check(load().mx_prefetch(_ptr(t), n, chunk_bytes, _stream(stream)), "mx_prefetch")
 
 
 def check_requant(lo, hi, mismatches, stream=None):

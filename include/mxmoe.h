@@ -229,6 +229,23 @@ mx_status moe_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H,
                             const uint8_t* w2, const uint8_t* w2_sc, int I,
                             float* y, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Weight prefetch (spark-ds41f README, "Current baseline": the next layer's
+ * weights and scale words stream into L2 while latency-bound kernels run;
+ * TP4 README, settings table, row "L2 prefetch": a side-stream kernel in
+ * the idle phases of a decode step, data untouched).  Reads [p, p + bytes)
+ * and discards it, so that a later kernel finds it in cache: workgroup i
+ * reads bytes [i*chunk_bytes, (i+1)*chunk_bytes), which land in the L2 of
+ * the XCD that runs it and in the memory-side cache (MALL) shared by all
+ * XCDs.  A chunk_bytes equal to a consumer kernel's per-workgroup slice
+ * (same block count) puts each slice in the L2 of its consumer's XCD.
+ * chunk_bytes 0 means 64 KiB.  Whole 16-byte units only (a trailing partial
+ * unit is not read).  p 16-byte aligned, chunk_bytes % 16 == 0 (else
+ * MX_EINVAL).  Writes nothing; asynchronous on stream (use a side stream
+ * to overlap it with latency-bound work).
+ */
+mx_status mx_prefetch(const void* p, uint64_t bytes, uint64_t chunk_bytes, void* stream);
+
 /* Name of a status code (static string). */
 const char* mx_status_string(mx_status s);
 

@@ -178,6 +178,13 @@ def test_shared_expert_rejects_bad_arguments(lib):
     assert shared(lib, T=0, x=None, y=None, ws=None) == mxmoe.MX_OK       # nothing to do, nothing launched
 
 
+def test_prefetch_rejects_bad_arguments(lib):
+    assert lib.mx_prefetch(None, 64, 0, None) == mxmoe.MX_EINVAL
+    assert lib.mx_prefetch(ctypes.c_void_p((1 << 20) + 4), 64, 0, None) == mxmoe.MX_EINVAL   # alignment
+    assert lib.mx_prefetch(FAKE, 64, 24, None) == mxmoe.MX_EINVAL                             # chunk % 16
+    assert lib.mx_prefetch(None, 0, 0, None) == mxmoe.MX_OK                                   # nothing to read
+
+
 def test_path_switch(lib):
     old = mxmoe.set_ffn_path(1)
     assert mxmoe.set_ffn_path(old) == 1
