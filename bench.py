@@ -74,6 +74,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay one HIP graph per step instead of eager launches")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode step at T=1: moe_route + moe_expert_ffn instead of moe_layer_decode1")
     ap.add_argument("--prefetch", action="store_true",
                     help="decode step: prefetch the dense projection's weights on a side stream from the step's start")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -150,6 +152,7 @@ def main():
         gcopies = [(gq, gsc)] + [(gq.clone(), gsc.clone()) for _ in range(R - 1)]
         torch.cuda.synchronize()
 
+        fused = T == 1 and not args.unfused
         side = torch.cuda.Stream() if args.prefetch else None     # default priority
         main = torch.cuda.current_stream()
 
@@ -163,8 +166,13 @@ def main():
                 with torch.cuda.stream(side):
                     mxmoe.prefetch(g, 16 * dense.cfg.K)
                     mxmoe.prefetch(gs, 16 * (dense.cfg.K // 32))
-            route(logits, surv)
-            ffn(xq, xsc, route, w13q, w13s, w2q, w2s)
+            if fused:
+                # one row: the gate runs inside the gate/up kernel (moe_layer_decode1)
+                mxmoe.moe_layer_decode1(logits, k, surv, 0.2, xq, xsc, w13q, w13s, w2q, w2s, E, I, route.ids,
+                                        route.w, route.offsets, route.perm, route.slot_pos, ffn.y, ffn.ws)
+            else:
+                route(logits, surv)
+                ffn(xq, xsc, route, w13q, w13s, w2q, w2s)
             mxmoe.fp8_block_gemm(aq, asc, g, gs, yg, mxmoe.MX_OUT_BF16)
             if side is not None:
                 main.wait_stream(side)
@@ -173,6 +181,7 @@ def main():
         ffn(xq, xsc, route, *copies[0])
         ffn_variant = mxmoe.last_variant()
         step(0)
+        step_variant = "moe_layer_decode1 + fp8_block_gemm" if fused else "moe_route + moe_expert_ffn + fp8_block_gemm"
         torch.cuda.synchronize()
         if not args.graph:
             run_step = step
@@ -201,7 +210,11 @@ def main():
         # graph, or eager), bracketed by events on the launch stream
         def ffn_calls():
             for i in range(R):
-                ffn(xq, xsc, route, *copies[i % R])
+                if fused:
+                    mxmoe.moe_layer_decode1(logits, k, surv, 0.2, xq, xsc, *copies[i % R], E, I, route.ids, route.w,
+                                            route.offsets, route.perm, route.slot_pos, ffn.y, ffn.ws)
+                else:
+                    ffn(xq, xsc, route, *copies[i % R])
         if not args.graph:
             run_ffn = ffn_calls
         else:
@@ -220,8 +233,10 @@ def main():
         torch.cuda.synchronize()
         ffn_ms = f0.elapsed_time(f1) / (reps * R)
         ms = total_ms / args.steps
-        ffn_bytes = touched * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * H * 4
+        ffn_bytes = touched * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * H * 4 + (T * E * 4 if fused else 0)
         achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+        if fused:
+            ffn_variant = "layer1:gu_decode_topk+down_combine1"
         if cfg.streams:
             # the same step with router-live verification rows: rows below the
             # confidence threshold take their anchor's experts instead of skipping
@@ -262,7 +277,7 @@ def main():
             "unit": "GB/s",
             "ms_per_step": round(ms, 5),
             "pct_hbm_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-            "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn (" + ffn_variant + ")",
+            "roofline": {"bound": "hbm", "kernel": ("moe_layer_decode1 (" if fused else "moe_expert_ffn (") + ffn_variant + ")",
                          "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(cfg.name),
                          "bytes_per_launch": ffn_bytes, "avg_launch_ms": round(ffn_ms, 5)},
@@ -270,7 +285,7 @@ def main():
                                    f"FP8 block-32 activations, + dense FP8 block-32 projection M={T}, K=N=4096",
                        "rows": T, "hidden": H, "experts": E, "top_k": k, "intermediate": I,
                        "touched_experts": touched, "bytes_per_step": step_bytes, "weight_copies": R,
-                       "launch": "hip_graph_per_step" if args.graph else "eager",
+                       "launch": "hip_graph_per_step" if args.graph else "eager", "step_calls": step_variant,
                        "prefetch": bool(args.prefetch)},
         })
         return inp, touched

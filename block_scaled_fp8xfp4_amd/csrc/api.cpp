@@ -174,6 +174,32 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H, co
   return from_hip(e);
 }
 
+mx_status moe_layer_decode1(const float* logits, int E, int k, const float* survival, float skip_below,
+                            const uint8_t* x, const uint8_t* x_sc, int H, const uint8_t* w13, const uint8_t* w13_sc,
+                            const uint8_t* w2, const uint8_t* w2_sc, int I, int32_t* topk_ids, float* topk_w,
+                            int32_t* expert_offsets, int32_t* perm, int32_t* slot_pos, float* y, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (E < 1 || E > mx::MAX_E || k < 1 || k > E || k > mx::MAX_K || H < 128 || I < 32) return MX_EINVAL;
+  if (H % 32 != 0 || I % 32 != 0) return MX_EINVAL;
+  if (H % 128 != 0 || H > 128 * 8 * mx::MAX_PARTS || I > mx::MAX_I || !mx::ffn_path_supported(1, H, I))
+    return MX_EUNSUPPORTED;
+  if (!logits || !x || !x_sc || !w13 || !w13_sc || !w2 || !w2_sc || !topk_ids || !topk_w || !expert_offsets ||
+      !perm || !slot_pos || !y)
+    return MX_EINVAL;
+  if (!aligned(logits, 4) || !aligned(survival, 4) || !aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
+      !aligned(y, 16) || !aligned(x_sc, 4) || !aligned(w13_sc, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      !aligned(expert_offsets, 4) || !aligned(perm, 4) || !aligned(slot_pos, 4))
+    return MX_EINVAL;
+  if (!ws || ws_bytes < mx::ffn_ws_bytes(1, H, E, I, k)) return MX_EWORKSPACE;
+  if (!aligned(ws, 256)) return MX_EINVAL;
+  const mx::FfnArgs a{x, x_sc, 1, H, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y};
+  const mx::FusedRoute fr{logits, survival, skip_below, topk_ids, topk_w, expert_offsets, perm, slot_pos};
+  const char* v = "";
+  const hipError_t e = mx::launch_ffn(a, ws, 1, static_cast<hipStream_t>(stream), &v, &fr);
+  if (e == hipSuccess) g_variant = v;
+  return from_hip(e);
+}
+
 mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc, int M, int N,
                          int K, void* y, int y_dtype, void* stream) {
   if (!a || !a_sc || !w || !w_sc || !y) return MX_EINVAL;

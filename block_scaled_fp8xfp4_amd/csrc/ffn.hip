@@ -38,6 +38,7 @@
 // combine_kernel adds w_tj * o_tj over the slots in order j = 0..k-1.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
+#include "route_device.hpp"
 
 namespace mx {
 
@@ -239,10 +240,17 @@ constexpr int DEC_SPITCH = DEC_MAX_STEPS + 1;     // LDS pitch (dwords) of the s
 // of every pair.  ONE (T = 1): every pair is row 0, whose activations are
 // requested before the route is read.  EXACT: H = 128 NS, so every address
 // offset is a constant.
-template <int NS, bool EXACT, bool ONE>
+//
+// RPER > 0 (single row, fused with the gate): every wavefront ranks the
+// row's logits itself (wave_topk with RPER logits per lane) instead of
+// reading a route; its k experts in ascending order are the items, expert
+// of rank r at bucket position r.  Workgroup 0's first wavefront writes the
+// route outputs exactly as the single-row route kernel does, for the down
+// kernel and the caller.
+template <int NS, bool EXACT, bool ONE, int RPER>
 __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* __restrict__ qws,
                                                            uint8_t* __restrict__ qsc_ws, float* __restrict__ h,
-                                                           int Tk, int R) {
+                                                           int Tk, int R, FusedRoute fr) {
   __shared__ int tok[DEC_ROWS];
   __shared__ float hb[16 * DEC_HPITCH];
   __shared__ uint32_t bsc[4][16 * DEC_SPITCH];                 // per wavefront: [row][step] scale dwords
@@ -261,12 +269,43 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
     if (tid < nsteps) xsv = reinterpret_cast<const uint32_t*>(a.x_sc)[tid];
   }
   WaveExperts we;                                               // every wavefront reads the expert list itself
-  wave_experts_load(a.offsets, a.E, we);
-  const int nitems = wave_experts_scan(a.E, we) * nb;
+  int ridx = 0, rrank = 0, nitems;
+  if (RPER > 0) {
+    float rval;
+    wave_topk<(RPER > 0 ? RPER : 1)>(fr.logits, a.E, a.k, ridx, rval);
+    const bool live = fr.survival == nullptr || !(fr.survival[0] < fr.skip_below);
+    for (int i = 0; i < a.k; ++i) rrank += __builtin_amdgcn_readlane(ridx, i) < ridx ? 1 : 0;
+    if (blockIdx.x == 0 && wave == 0) {                         // the route outputs, as the single-row route kernel
+      const float wt = slot_weight(rval, a.k);
+      if (lane < a.k) {
+        fr.ids[lane] = ridx;
+        fr.w[lane] = wt;
+        fr.slot_pos[lane] = live ? rrank : -1;
+        fr.perm[live ? rrank : lane] = live ? lane : -1;
+      }
+      for (int e = lane; e <= a.E; e += 64) {
+        int below = 0;
+        for (int i = 0; i < a.k; ++i) below += __builtin_amdgcn_readlane(ridx, i) < e ? 1 : 0;
+        fr.offsets[e] = live ? below : 0;
+      }
+    }
+    nitems = live ? a.k * nb : 0;
+  } else {
+    wave_experts_load(a.offsets, a.E, we);
+    nitems = wave_experts_scan(a.E, we) * nb;
+  }
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int blk = item % nb;
     int e, p0, cnt;
-    wave_tile(we, a.E, item / nb, e, p0, cnt);
+    if (RPER > 0) {                                             // the expert of rank item / nb
+      const int r = item / nb;
+      const unsigned long long m = __ballot(lane < a.k && rrank == r);
+      e = __builtin_amdgcn_readlane(ridx, __builtin_ctzll(m));
+      p0 = r;
+      cnt = 1;
+    } else {
+      wave_tile(we, a.E, item / nb, e, p0, cnt);
+    }
     if (p0 < 0 || p0 + cnt > Tk) cnt = 0;                       // malformed route: skip
     const int n0 = min(R, cnt);
     lds_barrier();                                              // the previous item's LDS reads are done
@@ -1136,7 +1175,24 @@ static inline void phase(int i, hipStream_t stream) {
   if (g_phase_on) (void)hipEventRecord(g_phase_ev[i], stream);
 }
 
-hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant) {
+// gate/up of one row: the NS / EXACT variant for H = 128 hs
+template <int RP>
+static void launch_gu_one(int hs, dim3 g0, dim3 b0, size_t lds, hipStream_t stream, const FfnArgs& a, uint8_t* qws,
+                          uint8_t* qsc, float* h, int Tk, int R, const FusedRoute& fr) {
+#define MX_GU1(NS_, EX_) \
+  hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, true, RP>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R, fr)
+  if (hs == 32) MX_GU1(32, true);
+  else if (hs == 16) MX_GU1(16, true);
+  else if (hs == 8) MX_GU1(8, true);
+  else if (hs <= 4) MX_GU1(4, false);
+  else if (hs <= 8) MX_GU1(8, false);
+  else if (hs <= 16) MX_GU1(16, false);
+  else MX_GU1(32, false);
+#undef MX_GU1
+}
+
+hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
+                      const FusedRoute* fr) {
   const int Tk = a.T * a.k;
   uint8_t* base = static_cast<uint8_t*>(ws);
   size_t oq, oqs, oh, oo;
@@ -1161,15 +1217,12 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     const int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
     const int hs = a.H / KSTEP, is = (a.I + KSTEP - 1) / KSTEP;
     const dim3 g0(gu_grid), b0(256);
-#define MX_GU(NS_, EX_, ONE_) hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, ONE_>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R)
+#define MX_GU(NS_, EX_, ONE_) \
+  hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, ONE_, 0>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R, FusedRoute{})
     if (a.T == 1) {
-      if (hs == 32) MX_GU(32, true, true);
-      else if (hs == 16) MX_GU(16, true, true);
-      else if (hs == 8) MX_GU(8, true, true);
-      else if (hs <= 4) MX_GU(4, false, true);
-      else if (hs <= 8) MX_GU(8, false, true);
-      else if (hs <= 16) MX_GU(16, false, true);
-      else MX_GU(32, false, true);
+      if (!fr) launch_gu_one<0>(hs, g0, b0, lds, stream, a, qws, qsc, h, Tk, R, FusedRoute{});
+      else if (a.E <= 256) launch_gu_one<4>(hs, g0, b0, lds, stream, a, qws, qsc, h, Tk, R, *fr);
+      else launch_gu_one<16>(hs, g0, b0, lds, stream, a, qws, qsc, h, Tk, R, *fr);
     } else {
       if (hs == 32) MX_GU(32, true, false);
       else if (hs == 16) MX_GU(16, true, false);
@@ -1187,7 +1240,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       else if (is <= 5) hipLaunchKernelGGL(down_combine1_kernel<5>, g1, b1, 0, stream, a, qws, qsc, Tk);
       else if (is <= 8) hipLaunchKernelGGL(down_combine1_kernel<8>, g1, b1, 0, stream, a, qws, qsc, Tk);
       else hipLaunchKernelGGL(down_combine1_kernel<16>, g1, b1, 0, stream, a, qws, qsc, Tk);
-      *variant = "ffn:gu_decode+down_combine1";
+      *variant = fr ? "layer1:gu_decode_topk+down_combine1" : "ffn:gu_decode+down_combine1";
       phase(2, stream);                                         // the down kernel also combines
       phase(3, stream);
       return hipGetLastError();

@@ -30,11 +30,17 @@ struct FfnArgs {
   const uint8_t* w13; const uint8_t* w13_sc; const uint8_t* w2; const uint8_t* w2_sc; int E; int I;
   float* y;
 };
+// single-row layer: the gate runs inside the gate/up kernel (route outputs written there)
+struct FusedRoute {
+  const float* logits; const float* survival; float skip_below;
+  int32_t* ids; float* w; int32_t* offsets; int32_t* perm; int32_t* slot_pos;
+};
 size_t ffn_ws_bytes(int T, int H, int E, int I, int k);
 void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h, size_t* off_o);
 // path: 0 automatic, 1 decode kernels, 2 prefill kernels
 bool ffn_path_supported(int path, int H, int I);
-hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant);
+hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
+                      const FusedRoute* fr = nullptr);
 void set_ffn_phase_events(const hipEvent_t* ev, int n);
 
 constexpr int GEMM_PREFILL_MIN_M = 320;  // dense GEMM: rows from which the tiled kernel beats the decode kernel (measured)

@@ -1,0 +1,73 @@
+// Top-k of one row by one wavefront and the softmax over the picks, shared
+// by the route kernels and the fused single-row layer (the MoE top-k gate of
+// the "New Deepseek 4.1 flash recipe" thread, post #6, "How it works"; exact
+// ties by lowest position, post #4, "Exact indexer selections").
+#pragma once
+#include "mx_device.hpp"
+
+extern "C" __device__ unsigned int __ockl_wfred_max_u32(unsigned int);
+extern "C" __device__ unsigned int __ockl_wfred_min_u32(unsigned int);
+
+namespace mx {
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// One wavefront ranks the row at l.  PER = logits per lane (E <= 64 * PER);
+// lanes j < k end with (expert, logit) of slot j.
+template <int PER>
+__device__ void wave_topk(const float* __restrict__ l, int E, int k, int& out_idx, float& out_val) {
+  const int lane = threadIdx.x & 63;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = l[min(lane + 64 * i, E - 1)];   // branch-free: all loads in flight together
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? order_key(v[i]) : 0u;   // 0: below every logit
+  out_idx = 0;
+  out_val = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t bk = key[0];                                       // this lane's best: ties keep the lower index
+    int bi = 0;
+#pragma unroll
+    for (int i = 1; i < PER; ++i)
+      if (key[i] > bk) { bk = key[i]; bi = i; }
+    const uint32_t m = __ockl_wfred_max_u32(bk);
+    const unsigned long long tied = __ballot(bk == m);
+    int idx;
+    if (__popcll(tied) == 1) idx = __builtin_amdgcn_readlane(lane + 64 * bi, __builtin_ctzll(tied));
+    else idx = (int)__ockl_wfred_min_u32(bk == m ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
+    if (lane == (idx & 63)) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i == bi) key[i] = 0u;
+    }
+    if (lane == j) {
+      out_idx = idx;
+      out_val = key_value(m);
+    }
+  }
+}
+
+// softmax over the k picked logits: w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), in double
+__device__ __forceinline__ float slot_weight(float val, int k) {
+  const int lane = threadIdx.x & 63;
+  const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), 0));   // slot 0's logit
+  const double ex = lane < k ? exp((double)val - (double)v0) : 0.0;
+  double den = 0.0;
+  for (int j = 0; j < k; ++j) {
+    const long long bits = __double_as_longlong(ex);
+    const int lo = __builtin_amdgcn_readlane((int)(bits & 0xFFFFFFFFll), j);
+    const int hi = __builtin_amdgcn_readlane((int)(bits >> 32), j);
+    den += __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+  }
+  return (float)(ex / den);
+}
+
+}  // namespace mx

@@ -19,7 +19,8 @@ MX_OUT_BF16, MX_OUT_F32 = 0, 1
 EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logits", "moe_route_workspace_bytes", "moe_route", "moe_route_live", "moe_expert_ffn_workspace_bytes",
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
            "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events",
-           "moe_shared_expert_workspace_bytes", "moe_shared_expert", "mx_prefetch")
+           "moe_shared_expert_workspace_bytes", "moe_shared_expert", "mx_prefetch",
+           "moe_layer_decode1")
 
 _lib = None
 
@@ -63,6 +64,8 @@ def load():
     lib.moe_shared_expert_workspace_bytes.argtypes = [I32, I32, I32]
     lib.moe_shared_expert.restype = I32
     lib.moe_shared_expert.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, SZ, P]
+    lib.moe_layer_decode1.restype = I32
+    lib.moe_layer_decode1.argtypes = [P, I32, I32, P, F32, P, P, I32, P, P, P, P, I32, P, P, P, P, P, P, P, SZ, P]
     lib.mx_prefetch.restype = I32
     lib.mx_prefetch.argtypes = [P, ctypes.c_uint64, ctypes.c_uint64, P]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -176,6 +179,16 @@ def moe_expert_ffn(x, x_sc, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_
     _check(load().moe_expert_ffn(_ptr(x), _ptr(x_sc), T, H, _ptr(topk_w), _ptr(expert_offsets), _ptr(perm),
                                  _ptr(slot_pos), k, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), E, I, _ptr(y),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_layer_decode1(logits, k, survival, skip_below, x, x_sc, w13, w13_sc, w2, w2_sc, E, I, topk_ids, topk_w,
+                      expert_offsets, perm, slot_pos, y, ws, stream=None):
+    """Route + routed-expert FFN of one row (logits [1, E] or [E]) in two launches."""
+    H = x.shape[-1]
+    _check(load().moe_layer_decode1(_ptr(logits), E, k, _ptr(survival), float(skip_below), _ptr(x), _ptr(x_sc), H,
+                                    _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I, _ptr(topk_ids), _ptr(topk_w),
+                                    _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(y), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_decode1")
 
 
 def fp8_block_gemm(a, a_sc, w, w_sc, y, y_dtype, stream=None):

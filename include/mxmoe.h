@@ -191,6 +191,28 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H,
                          float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The routed-expert layer of ONE row in two launches: moe_route and
+ * moe_expert_ffn for T = 1 fused, the top-k gate running inside the gate/up
+ * kernel (every workgroup ranks the row's E logits itself, so the experts'
+ * weight loads start without waiting for a route kernel).  Same arguments
+ * and results as moe_route (T = 1, skip mode) followed by moe_expert_ffn
+ * (T = 1), bit for bit: topk_ids, topk_w, expert_offsets, perm, slot_pos
+ * are written as moe_route writes them, y as moe_expert_ffn.  ws:
+ * moe_expert_ffn_workspace_bytes(1, H, E, I, k) bytes.  Supported: the
+ * moe_expert_ffn decode-path shapes (H % 128 == 0, H <= 4096, I <= 2048).
+ * (Forum thread post #6, "How it works": the MoE top-k gate and the routed
+ * experts; "Kernel by kernel against B12X": router and routed experts are
+ * the decode step's largest groups after the dense projections.)
+ */
+mx_status moe_layer_decode1(const float* logits, int E, int k, const float* survival, float skip_below,
+                            const uint8_t* x, const uint8_t* x_sc, int H,
+                            const uint8_t* w13, const uint8_t* w13_sc,
+                            const uint8_t* w2, const uint8_t* w2_sc, int I,
+                            int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                            int32_t* perm, int32_t* slot_pos, float* y,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dense block-32 FP8 GEMM (post #2 "Known issues and next steps": dense FP8
  * GEMMs are the largest remaining decode lever; post #6 "How it works":
  * MXFP8 projections, decode rows on small row tiles).

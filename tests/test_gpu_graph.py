@@ -14,8 +14,8 @@ from gpu_common import dev, host, moe_workload, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["decode", "verify"])
-def test_graph_replays_match_eager(name):
+@pytest.mark.parametrize("name,fused", [("decode", False), ("decode", True), ("verify", False)])
+def test_graph_replays_match_eager(name, fused):
     inp, r, layer = moe_workload(name)
     c = inp.cfg
     say(f"graph replay: {name}")
@@ -31,8 +31,13 @@ def test_graph_replays_match_eager(name):
     L = layer.d
 
     def step():
-        route(logits, surv)
-        ffn(L["x"], L["x_sc"], route, L["w13"], L["w13_sc"], L["w2"], L["w2_sc"])
+        if fused:                                        # one row: the gate inside the gate/up kernel
+            mxmoe.moe_layer_decode1(logits, c.k, surv, 0.2, L["x"], L["x_sc"], L["w13"], L["w13_sc"], L["w2"],
+                                    L["w2_sc"], c.E, c.I, route.ids, route.w, route.offsets, route.perm,
+                                    route.slot_pos, ffn.y, ffn.ws)
+        else:
+            route(logits, surv)
+            ffn(L["x"], L["x_sc"], route, L["w13"], L["w13_sc"], L["w2"], L["w2_sc"])
         mxmoe.fp8_block_gemm(a_q, a_sc, g_q, g_sc, yg, mxmoe.MX_OUT_BF16)
 
     step()
