@@ -660,11 +660,14 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
 }
 
 // ========================================================== prefill path ==
-constexpr int GU_BM = 128;
+// (measured: 256-row tiles, eight wavefronts and one workgroup per CU, which
+// halve the weight re-reads, ran at 505-539 us against 474 us, bitwise equal)
+constexpr int GU_BM = 128;                        // expert tile rows
 constexpr int GU_BN = 256;                        // W13 rows per tile (128 intermediate columns)
 constexpr int GU_ICOLS = GU_BN / 2;
 constexpr int GU_STAGES = 2;                      // LDS stages per workgroup
-constexpr int GU_WG_PER_CU = 4 / GU_STAGES;       // workgroups resident per CU (LDS-bound)
+constexpr int GU_NT = 2 * GU_BM;                  // threads: one wavefront per 64 rows x 64 columns
+constexpr int GU_WG_PER_CU = GU_BM == 128 ? 4 / GU_STAGES : 1;   // workgroups resident per CU (LDS-bound)
 
 __device__ __forceinline__ int a_phys(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }   // 16-byte chunk
 __device__ __forceinline__ int b_phys(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
@@ -688,10 +691,11 @@ struct GuStage {
 // LDS slot, so the buffers come out XOR-swizzled by 16-byte chunk and the 16
 // rows one MFMA operand read touches fall in distinct banks.
 template <int NSTG>
-__global__ __launch_bounds__(256, 4 / NSTG) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
-                                                                   uint8_t* __restrict__ qsc_ws, int Tk,
-                                                                   int* __restrict__ queue) {
-  constexpr int DMA_PER_STAGE = 10;               // per thread: 4 A + 4 B chunks, 1 A + 1 B scale dword
+__global__ __launch_bounds__(GU_NT, GU_WG_PER_CU) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
+                                                                         uint8_t* __restrict__ qsc_ws, int Tk,
+                                                                         int* __restrict__ queue) {
+  constexpr int NBD = GU_BN * 4 / GU_NT;          // B chunk DMAs per thread per stage
+  constexpr int DMA_PER_STAGE = 4 + NBD + 2;      // per thread: 4 A + NBD B chunks, 1 A + 1 B scale dword
   __shared__ int tile_start[MAX_E + 1];
   __shared__ int tok[GU_BM];
   __shared__ GuStage st[NSTG];
@@ -737,13 +741,17 @@ __global__ __launch_bounds__(256, 4 / NSTG) void gu_prefill_kernel(FfnArgs a, ui
     // row whose results are discarded: rows and columns are independent)
     // (byte offsets from wavefront-uniform bases: the activations, and this
     // expert's weights and scales; T * H < 2^32 is checked at the boundary)
-    uint32_t aoff[4], boff[4];
+    uint32_t aoff[4], boff[NBD];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int p = j * 256 + tid;
+      const int p = j * GU_NT + tid;
       const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
       const int t = tok[r];
       aoff[j] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)H + c * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < NBD; ++j) {
+      const int p = j * GU_NT + tid;
       const int rb = p >> 2, cb = (p & 3) ^ ((rb >> 2) & 3);
       const int icol = rb & 127;
       const int r13 = (rb < 128 ? 0 : I) + c0 + (icol < ncols ? icol : 0);
@@ -752,7 +760,9 @@ __global__ __launch_bounds__(256, 4 / NSTG) void gu_prefill_kernel(FfnArgs a, ui
     const int ra = wave * 32 + (lane & 31);                     // A scale row of this lane (lanes < 32)
     const int tas = tok[ra];
     const uint32_t asoff = (uint32_t)(tas < 0 ? 0 : tas) * (uint32_t)(H / 32);
-    const int rbs = wave * 64 + lane, icol_s = rbs & 127;
+    // B scale row of this lane; with more than four wavefronts the others
+    // repeat the first four's transfers (same source, same LDS slot)
+    const int rbs = (wave & 3) * 64 + lane, icol_s = rbs & 127;
     const uint32_t bsoff = (uint32_t)((rbs < 128 ? 0 : I) + c0 + (icol_s < ncols ? icol_s : 0)) * (uint32_t)(H / 32);
     const uint8_t* w13e = a.w13 + (int64_t)e * 2 * I * (H / 2);
     const uint8_t* w13se = a.w13_sc + (int64_t)e * 2 * I * (H / 32);
@@ -761,12 +771,12 @@ __global__ __launch_bounds__(256, 4 / NSTG) void gu_prefill_kernel(FfnArgs a, ui
       const uint32_t d = st_lds + buf * (uint32_t)sizeof(GuStage);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        dma16_to_lds(a.x + s * KSTEP, aoff[j], d + (uint32_t)offsetof(GuStage, a) + (j * 256 + wave * 64) * 16);
+        dma16_to_lds(a.x + s * KSTEP, aoff[j], d + (uint32_t)offsetof(GuStage, a) + (j * GU_NT + wave * 64) * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dma16_to_lds(w13e + s * 64, boff[j], d + (uint32_t)offsetof(GuStage, b) + (j * 256 + wave * 64) * 16);
+      for (int j = 0; j < NBD; ++j)
+        dma16_to_lds(w13e + s * 64, boff[j], d + (uint32_t)offsetof(GuStage, b) + (j * GU_NT + wave * 64) * 16);
       if (lane < 32) dma4_to_lds(a.x_sc + s * 4, asoff, d + (uint32_t)offsetof(GuStage, as) + wave * 32 * 4);
-      dma4_to_lds(w13se + s * 4, bsoff, d + (uint32_t)offsetof(GuStage, bs) + wave * 64 * 4);
+      dma4_to_lds(w13se + s * 4, bsoff, d + (uint32_t)offsetof(GuStage, bs) + (wave & 3) * 64 * 4);
     };
 
     v4f acc[4][8];
@@ -1261,7 +1271,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     gu_grid = (gu_grid + XCDS - 1) / XCDS * XCDS;
     dn_grid = (dn_grid + XCDS - 1) / XCDS * XCDS;
     hipLaunchKernelGGL(clear_i32_kernel, dim3(1), dim3(64), 0, stream, queue, 64);
-    hipLaunchKernelGGL(gu_prefill_kernel<GU_STAGES>, dim3(gu_grid), dim3(256), 0, stream, a, qws, qsc, Tk, queue);
+    hipLaunchKernelGGL(gu_prefill_kernel<GU_STAGES>, dim3(gu_grid), dim3(GU_NT), 0, stream, a, qws, qsc, Tk, queue);
     phase(1, stream);
     if (a.I <= 2 * KSTEP)
       hipLaunchKernelGGL(down_prefill_kernel<2>, dim3(dn_grid), dim3(DN_NT), 0, stream, a, qws, qsc, o, junk, Tk, queue + 32);
