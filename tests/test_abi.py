@@ -152,10 +152,11 @@ def test_router_logits_rejects_bad_arguments(lib):
     assert logits(lib, h=ctypes.c_void_p((1 << 20) + 8)) == mxmoe.MX_EINVAL   # 16-byte alignment
     assert logits(lib, out=ctypes.c_void_p((1 << 20) + 2)) == mxmoe.MX_EINVAL
     assert logits(lib, ws=ctypes.c_void_p((1 << 24) + 64)) == mxmoe.MX_EINVAL
-    need = mxmoe.moe_router_logits_workspace_bytes(4, 256, 8)
-    assert need >= 4 * 8 * 4                                            # at least one part sum per element
-    assert logits(lib, ws=None) == mxmoe.MX_EWORKSPACE
-    assert logits(lib, ws_bytes=need - 1) == mxmoe.MX_EWORKSPACE
+    need = mxmoe.moe_router_logits_workspace_bytes(100, 256, 8)
+    assert need >= 100 * 8 * 4                                          # at least one part sum per element
+    assert logits(lib, T=100, ws=None) == mxmoe.MX_EWORKSPACE
+    assert logits(lib, T=100, ws_bytes=need - 1) == mxmoe.MX_EWORKSPACE
+    assert mxmoe.moe_router_logits_workspace_bytes(16, 256, 8) == 0       # one launch, no workspace
     assert logits(lib, T=0, h=None, out=None, ws=None) == mxmoe.MX_OK   # nothing to do, nothing launched
     assert mxmoe.moe_router_logits_workspace_bytes(1, 100, 8) == 0      # invalid shape
 

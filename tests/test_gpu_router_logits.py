@@ -14,6 +14,11 @@ from gpu_common import assert_close, dev, host, say
 pytestmark = pytest.mark.gpu
 
 PREFILL_MIN_T = 1024     # rows from which the tiled kernel runs
+ONE_MAX_T = 16           # rows up to which one workgroup per expert runs
+
+
+def few_rows_variant(T):
+    return "logits:one" if T <= ONE_MAX_T else "logits:splitk"
 # fp32 accumulation of bf16 products (exact in fp32): each 32-product MFMA
 # step, 8-step chains and the ordered sum of H/256 parts each add at most a
 # few units of 2^-24 of the running magnitude; 2^-16 of sum |h w| bounds all
@@ -51,6 +56,8 @@ def check(hf, wf, rows=None, what=""):
 @pytest.mark.parametrize("T,H,E", [
     (4, 256, 8),          # the tiny layer
     (1, 4096, 256),       # decode row
+    (16, 4096, 256),      # last row count of the one-workgroup-per-expert kernel
+    (3, 5120, 40),        # 20 parts: waves take two parts
     (48, 4096, 256),      # verification rows
     (21, 96, 40),         # K of 3 steps (one short part), ragged experts
     (17, 5120, 24),       # 20 parts
@@ -61,7 +68,7 @@ def check(hf, wf, rows=None, what=""):
 def test_few_rows_kernel(T, H, E):
     say(f"router logits T={T} H={H} E={E}")
     _, v = check(synth.hidden_rows(T + H, T, H), synth.router_gate("decode", E=E, H=H), what=f"{T}x{H}x{E}")
-    assert v.startswith("logits:splitk")
+    assert v.startswith(few_rows_variant(T))
 
 
 @pytest.mark.parametrize("T,H,E", [
@@ -101,7 +108,7 @@ def test_one_hot_rows_are_exact(T):
     hf = np.zeros((T, H), np.float32)
     hf[np.arange(T), cols] = 1.0
     got, v = run(bits(hf), bits(wf))
-    assert v.startswith("logits:splitk" if T < PREFILL_MIN_T else "logits:prefill")
+    assert v.startswith(few_rows_variant(T) if T < PREFILL_MIN_T else "logits:prefill")
     assert np.array_equal(got, wf[:, cols].T)
 
 
@@ -114,7 +121,7 @@ def test_rows_do_not_depend_on_the_batch():
     assert v.startswith("logits:prefill")
     for t0, t1 in [(0, 1), (63, 64), (64, 80), (200, 327), (77, 1100), (1099, 1100)]:
         part, v = run(hb[t0:t1], wb)
-        assert v.startswith("logits:splitk")
+        assert v.startswith(few_rows_variant(t1 - t0))
         assert np.array_equal(part, full[t0:t1]), (t0, t1)
     part, v = run(hb[5:1100], wb)                # another tiling of the same rows
     assert v.startswith("logits:prefill")
