@@ -42,7 +42,7 @@
 
 namespace mx {
 
-constexpr int DEC_MAX_STEPS = 32;                 // decode gate/up: H <= 4096 held in registers
+constexpr int DEC_MAX_STEPS = 40;                 // decode gate/up: H <= 5120 held in registers
 constexpr int DOWN_MAX_STEPS = MAX_I / KSTEP;     // 16
 constexpr int PF_ROWS = 64;                       // prefill expert tile rows
 constexpr int PF_NCOLS = 256;                     // prefill down: W2 rows per workgroup
@@ -264,6 +264,22 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
   uint32_t* xslds = reinterpret_cast<uint32_t*>(dyn_lds + (size_t)R * pitch);   // [R][nsteps]
   u32x4 xv[DEC_ROWS];
   uint32_t xsv = 0x7F7F7F7Fu;
+  // the parts of the rows' activations and scales past what one thread per
+  // 16-byte chunk / scale dword covers (H > 4096): staged directly
+  auto stage_rest = [&](int nr) {
+    for (int idx = tid; idx < nr * chunks; idx += 256) {
+      const int r = idx / chunks, c = idx % chunks;
+      if (c < 256) continue;
+      const int t = ONE ? 0 : tok[r];
+      *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + c * 16) =
+          t >= 0 ? ldg16(a.x + (int64_t)t * H + c * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int idx = tid + 256; idx < nr * nsteps; idx += 256) {
+      const int r = idx / nsteps, c = idx % nsteps;
+      const int t = ONE ? 0 : tok[r];
+      xslds[idx] = t >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)t * (H / 32))[c] : 0x7F7F7F7Fu;
+    }
+  };
   if (ONE) {
     xv[0] = tid < chunks ? ldg16(a.x + tid * 16) : u32x4{0u, 0u, 0u, 0u};
     if (tid < nsteps) xsv = reinterpret_cast<const uint32_t*>(a.x_sc)[tid];
@@ -330,9 +346,10 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
     // this wavefront's 16 rows of scales: one contiguous span of 16 * nsteps dwords
     const int64_t wrow0 = (int64_t)e * 2 * I + (wave < 2 ? 0 : I) + blk * 32 + (wave & 1) * 16;
     const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.w13_sc + wrow0 * (H / 32));
-    uint32_t bsv[8];
+    constexpr int NBSV = (16 * NS + 63) / 64;                    // scale dwords per lane
+    uint32_t bsv[NBSV];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NBSV; ++i) {
       const int idx = lane + 64 * i;
       bsv[i] = idx < 16 * nsteps ? ssrc[idx] : 0u;
     }
@@ -342,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
     for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (EXACT || s < nsteps ? s : nsteps - 1) * 64);
     // stage what the first pass needs (its loads were issued before the weights)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NBSV; ++i) {
       const int idx = lane + 64 * i;
       if (idx < 16 * nsteps) bsc[wave][(idx / nsteps) * spitch + idx % nsteps] = bsv[i];
     }
@@ -355,6 +372,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
         if (r < n0 && tid < chunks) *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + tid * 16) = xv[r];
       if (tid < n0 * nsteps) xslds[tid] = xsv;
     }
+    if (chunks > 256 || (ONE ? 1 : n0) * nsteps > 256) stage_rest(ONE ? 1 : n0);   // H > 4096
     lds_barrier();
     const uint32_t* bsrow = &bsc[wave][col * spitch];
     // One pass over rows [r0, r0 + nrows) whose activations are in LDS.  Every
@@ -424,6 +442,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
         for (int r = 0; r < DEC_ROWS; ++r)
           if (r < nrows && tid < chunks) *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + tid * 16) = xv[r];
         if (tid < nrows * nsteps) xslds[tid] = xsv;
+        if (chunks > 256 || nrows * nsteps > 256) stage_rest(nrows);   // H > 4096
         lds_barrier();
       }
       run_pass(r0, nrows);
@@ -1192,12 +1211,14 @@ static void launch_gu_one(int hs, dim3 g0, dim3 b0, size_t lds, hipStream_t stre
 #define MX_GU1(NS_, EX_) \
   hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, true, RP>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R, fr)
   if (hs == 32) MX_GU1(32, true);
+  else if (hs == 40) MX_GU1(40, true);
   else if (hs == 16) MX_GU1(16, true);
   else if (hs == 8) MX_GU1(8, true);
   else if (hs <= 4) MX_GU1(4, false);
   else if (hs <= 8) MX_GU1(8, false);
   else if (hs <= 16) MX_GU1(16, false);
-  else MX_GU1(32, false);
+  else if (hs <= 32) MX_GU1(32, false);
+  else MX_GU1(40, false);
 #undef MX_GU1
 }
 
@@ -1235,12 +1256,14 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       else launch_gu_one<16>(hs, g0, b0, lds, stream, a, qws, qsc, h, Tk, R, *fr);
     } else {
       if (hs == 32) MX_GU(32, true, false);
+      else if (hs == 40) MX_GU(40, true, false);
       else if (hs == 16) MX_GU(16, true, false);
       else if (hs == 8) MX_GU(8, true, false);
       else if (hs <= 4) MX_GU(4, false, false);
       else if (hs <= 8) MX_GU(8, false, false);
       else if (hs <= 16) MX_GU(16, false, false);
-      else MX_GU(32, false, false);
+      else if (hs <= 32) MX_GU(32, false, false);
+      else MX_GU(40, false, false);
     }
 #undef MX_GU
     phase(1, stream);

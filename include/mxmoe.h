@@ -199,7 +199,7 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H,
  * (T = 1), bit for bit: topk_ids, topk_w, expert_offsets, perm, slot_pos
  * are written as moe_route writes them, y as moe_expert_ffn.  ws:
  * moe_expert_ffn_workspace_bytes(1, H, E, I, k) bytes.  Supported: the
- * moe_expert_ffn decode-path shapes (H % 128 == 0, H <= 4096, I <= 2048).
+ * moe_expert_ffn decode-path shapes (H % 128 == 0, H <= 5120, I <= 2048).
  * (Forum thread post #6, "How it works": the MoE top-k gate and the routed
  * experts; "Kernel by kernel against B12X": router and routed experts are
  * the decode step's largest groups after the dense projections.)

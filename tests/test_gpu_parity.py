@@ -316,3 +316,31 @@ def test_gemm_rows_do_not_depend_on_M():
         y = torch.empty((m1 - m0, 256), dtype=torch.float32, device="cuda")
         mxmoe.fp8_block_gemm(dev(aq[m0:m1]), dev(asc[m0:m1]), dev(wq), dev(wsc), y, mxmoe.MX_OUT_F32)
         assert np.array_equal(host(y), full[m0:m1])
+
+
+# ------------------------------------------------ the pages' own layer shape
+def test_ffn_pages_shape_both_paths():
+    """One TP4 rank's routed layer as the pages size it (384 experts, hidden
+    5120, intermediate slice 576), top-8: the decode path (fused single row
+    and T = 4) and the prefill kernels on the same rows, against the oracle,
+    bitwise equal to each other."""
+    inp = synth.small_moe(61, 4, 5120, 384, 8, 576)
+    r = oracle.route(inp.logits, 8)
+    layer = Layer(inp, np.unique(r["ids"]))
+    say("pages shape H=5120 E=384 I=576: decode path")
+    y_dec = ffn_parity(inp, r, layer, what="pages shape decode")
+    old = mxmoe.set_ffn_path(2)
+    try:
+        y_pre, _, _ = layer.gpu_y()
+    finally:
+        mxmoe.set_ffn_path(old)
+    assert mxmoe.last_variant().startswith("ffn:gu_prefill")
+    assert np.array_equal(host(y_pre), y_dec)
+    # the single-row fused layer on row 0
+    d = layer.d
+    route1 = Route(1, 384, 8)
+    ffn1 = ExpertFFN(1, 5120, 384, 576, 8)
+    mxmoe.moe_layer_decode1(dev(inp.logits[:1]), 8, None, 0.2, d["x"][:1].contiguous(), d["x_sc"][:1].contiguous(),
+                            d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], 384, 576, route1.ids, route1.w,
+                            route1.offsets, route1.perm, route1.slot_pos, ffn1.y, ffn1.ws)
+    assert np.array_equal(host(ffn1.y)[0], y_dec[0])
