@@ -12,6 +12,7 @@ constexpr int MAX_K = 16;        // top-k
 constexpr int MAX_I = 2048;      // expert intermediate (decode LDS staging)
 constexpr int MAX_PARTS = 16;    // K parts of 1024 -> H, K <= 16384
 constexpr int ROUTE_CHUNK = 256; // rows per bucketing chunk
+constexpr int ROUTE_FUSED_MAX_T = 32;  // rows ranked inside the single-workgroup route (more: a top-k launch first)
 constexpr int LG_MAX_H = 16384;     // router logits: hidden width
 constexpr int LG_PREFILL_MIN_T = 1024; // router logits: rows from which the tiled kernel runs (measured crossover)
 

@@ -130,6 +130,17 @@ __global__ __launch_bounds__(64) void route1_kernel(const float* __restrict__ lo
   }
 }
 
+// Gather chunk c's experts (-1 for dead rows) into LDS.
+__device__ int load_chunk_ids(const int32_t* __restrict__ ids, int T, int k, const float* __restrict__ survival,
+                              float skip_below, int c, int32_t* ids_lds) {
+  const int c0 = c * ROUTE_CHUNK, nrows = min(ROUTE_CHUNK, T - c0);
+  for (int p = threadIdx.x; p < nrows * k; p += blockDim.x) {
+    const int t = c0 + p / k;
+    ids_lds[p] = row_live(survival, skip_below, t) ? ids[(int64_t)c0 * k + p] : -1;
+  }
+  return nrows;
+}
+
 // ----------------------------------------------------------- up to 256 rows
 // Exclusive scan of v over the threads of the block (any multiple of 64 up to
 // 1024 threads); every thread gets its prefix, and the total.
@@ -194,7 +205,11 @@ __device__ void scatter_chunk(const RowMasks& cm, const int32_t* ids_lds, int c0
 
 // The whole route for 1 < T <= 256 in one workgroup: one wavefront per row
 // for the top-k, then the bitmask counting sort over all the block's threads.
-template <int PER>
+// TOPK false: the rows were ranked by topk_kernel (one wavefront per row over
+// many CUs: one CU ranking more than a few rows is bound by its own issue
+// rate), and this workgroup only buckets ids (bucket_survival: the rows that
+// join the buckets, NULL for all).
+template <int PER, bool TOPK>
 __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                            const float* __restrict__ survival, float skip_below,
                                                            const int32_t* __restrict__ anchor,
@@ -206,12 +221,16 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
   __shared__ int32_t base[MAX_E];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int i = threadIdx.x; i < E * 4; i += blockDim.x) (&cm.m[0][0])[i] = 0ull;
-  for (int t = wave; t < T; t += nw) {
-    bool live;
-    int src;
-    row_mode(survival, skip_below, anchor, T, t, live, src);
-    const int idx = topk_row<PER>(logits, t, src, E, k, live, ids, w, slot_pos);
-    if (lane < k) ids_lds[t * k + lane] = live ? idx : -1;
+  if (TOPK) {
+    for (int t = wave; t < T; t += nw) {
+      bool live;
+      int src;
+      row_mode(survival, skip_below, anchor, T, t, live, src);
+      const int idx = topk_row<PER>(logits, t, src, E, k, live, ids, w, slot_pos);
+      if (lane < k) ids_lds[t * k + lane] = live ? idx : -1;
+    }
+  } else {
+    load_chunk_ids(ids, T, k, survival, skip_below, 0, ids_lds);
   }
   lds_barrier();
   for (int p = threadIdx.x; p < T * k; p += blockDim.x) {
@@ -251,17 +270,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   int src;
   row_mode(survival, skip_below, anchor, T, t, live, src);
   topk_row<PER>(logits, t, src, E, k, live, ids, w, slot_pos);
-}
-
-// Gather chunk c's experts (-1 for dead rows) into LDS.
-__device__ int load_chunk_ids(const int32_t* __restrict__ ids, int T, int k, const float* __restrict__ survival,
-                              float skip_below, int c, int32_t* ids_lds) {
-  const int c0 = c * ROUTE_CHUNK, nrows = min(ROUTE_CHUNK, T - c0);
-  for (int p = threadIdx.x; p < nrows * k; p += blockDim.x) {
-    const int t = c0 + p / k;
-    ids_lds[p] = row_live(survival, skip_below, t) ? ids[(int64_t)c0 * k + p] : -1;
-  }
-  return nrows;
 }
 
 // Multi-chunk path, step 1: per-chunk counts -> counts[c][e].
@@ -340,11 +348,17 @@ static void launch_route_per(const float* logits, int T, int E, int k, const flo
     hipLaunchKernelGGL((route1_kernel<PER>), dim3(1), dim3(64), 0, stream, logits, E, k, survival, skip_below, anchor,
                        ids, w, offsets, perm, slot_pos);
     *variant = anchor ? "route_live:one_row_wavefront" : "route:one_row_wavefront";
-  } else if (nchunks <= 1) {
+  } else if (T <= ROUTE_FUSED_MAX_T) {
     const int threads = 64 * (T < 16 ? T : 16);
-    hipLaunchKernelGGL((route_small_kernel<PER>), dim3(1), dim3(threads), 0, stream, logits, T, E, k, survival,
+    hipLaunchKernelGGL((route_small_kernel<PER, true>), dim3(1), dim3(threads), 0, stream, logits, T, E, k, survival,
                        skip_below, anchor, ids, w, offsets, perm, slot_pos);
     *variant = anchor ? "route_live:fused_single_workgroup" : "route:fused_single_workgroup";
+  } else if (nchunks <= 1) {
+    hipLaunchKernelGGL((topk_kernel<PER>), dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, survival,
+                       skip_below, anchor, ids, w, slot_pos);
+    hipLaunchKernelGGL((route_small_kernel<PER, false>), dim3(1), dim3(1024), 0, stream, logits, T, E, k,
+                       bucket_survival, skip_below, anchor, ids, w, offsets, perm, slot_pos);
+    *variant = anchor ? "route_live:topk_wave+bucket_single_workgroup" : "route:topk_wave+bucket_single_workgroup";
   } else {
     int32_t* counts = static_cast<int32_t*>(ws);
     hipLaunchKernelGGL((topk_kernel<PER>), dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, survival,

@@ -20,38 +20,39 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 }
 
 // One wavefront ranks the row at l.  PER = logits per lane (E <= 64 * PER);
-// lanes j < k end with (expert, logit) of slot j.
+// lanes j < k end with (expert, logit) of slot j.  Lane l holds the block of
+// logits [PER l, PER l + PER), so lane order is index order: of the lanes
+// whose best key equals the round's maximum, the lowest one holds the lowest
+// index, and within a lane a strict comparison keeps the lowest position.
+// Each round is branch-free: one wavefront maximum, one ballot, one readlane.
 template <int PER>
 __device__ void wave_topk(const float* __restrict__ l, int E, int k, int& out_idx, float& out_val) {
   const int lane = threadIdx.x & 63;
   float v[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) v[i] = l[min(lane + 64 * i, E - 1)];   // branch-free: all loads in flight together
+  for (int i = 0; i < PER; ++i) v[i] = l[min(PER * lane + i, E - 1)];   // all loads in flight together
   uint32_t key[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? order_key(v[i]) : 0u;   // 0: below every logit
+  for (int i = 0; i < PER; ++i) key[i] = PER * lane + i < E ? order_key(v[i]) : 0u;   // 0: below every logit
   out_idx = 0;
   out_val = 0.0f;
   for (int j = 0; j < k; ++j) {
     uint32_t bk = key[0];                                       // this lane's best: ties keep the lower index
     int bi = 0;
 #pragma unroll
-    for (int i = 1; i < PER; ++i)
-      if (key[i] > bk) { bk = key[i]; bi = i; }
+    for (int i = 1; i < PER; ++i) {
+      const bool gt = key[i] > bk;
+      bk = gt ? key[i] : bk;
+      bi = gt ? i : bi;
+    }
     const uint32_t m = __ockl_wfred_max_u32(bk);
-    const unsigned long long tied = __ballot(bk == m);
-    int idx;
-    if (__popcll(tied) == 1) idx = __builtin_amdgcn_readlane(lane + 64 * bi, __builtin_ctzll(tied));
-    else idx = (int)__ockl_wfred_min_u32(bk == m ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
-    if (lane == (idx & 63)) {
+    const int wl = (int)__builtin_ctzll(__ballot(bk == m));    // lowest lane holding the maximum
+    const int wbi = __builtin_amdgcn_readlane(bi, wl);
+    const bool mine = lane == wl;
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (i == bi) key[i] = 0u;
-    }
-    if (lane == j) {
-      out_idx = idx;
-      out_val = key_value(m);
-    }
+    for (int i = 0; i < PER; ++i) key[i] = (mine && i == wbi) ? 0u : key[i];
+    out_idx = lane == j ? PER * wl + wbi : out_idx;
+    out_val = lane == j ? key_value(m) : out_val;
   }
 }
 
