@@ -100,6 +100,11 @@ def test_route_edge_cases():
     check_route(rng.standard_normal((3, 1)).astype(np.float32), 1)              # E = 1
     check_route(rng.standard_normal((64, 32)).astype(np.float32), 4, np.zeros(64, np.float32))   # all dead
     check_route(rng.standard_normal((700, 256)).astype(np.float32), 8)          # ragged last chunk
+    # around the row count where ranking moves out of the single bucketing workgroup
+    for T, variant in ((32, "route:fused_single_workgroup"), (33, "route:topk_wave+bucket_single_workgroup"),
+                       (256, "route:topk_wave+bucket_single_workgroup")):
+        check_route(ties[:T], 8, surv[:T])
+        assert mxmoe.last_variant() == variant, (T, mxmoe.last_variant())
 
 
 # ----------------------------------------------------------------- expert FFN

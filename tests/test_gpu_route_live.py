@@ -68,6 +68,10 @@ def test_every_route_kernel():
     anchor = anchors_of(40, 8)
     anchor[[1, 2, 3, 4]] = [-5, 40, 3, 1]                       # out of range, self, a reusing anchor
     check_route_live(ties, 4, surv, anchor, 0.1)
+    assert mxmoe.last_variant() == "route_live:topk_wave+bucket_single_workgroup"
+    # the same rows, few enough to be ranked inside the bucketing workgroup
+    check_route_live(ties[:24], 4, surv[:24], np.minimum(anchor[:24], 23), 0.1)
+    assert mxmoe.last_variant() == "route_live:fused_single_workgroup"
     # no survival: every row keeps its own experts (the plain gate with every row live)
     lg = rng.standard_normal((20, 32)).astype(np.float32)
     g, r = check_route_live(lg, 2, None, anchors_of(20, 5), 0.1)
