@@ -486,12 +486,17 @@ __device__ void stage_q_rows(const uint8_t* __restrict__ qws, const uint8_t* __r
   }
 }
 
+// Workgroups per CU of the persistent down kernel: three while its registers
+// allow (measured at the verification batch: 39 us against 43 us with two;
+// one workgroup per item instead of a persistent grid: 70 us)
+#define DN_WG_PER_CU(NS) ((NS) <= 5 ? 3 : 2)
+
 // Down: one workgroup per (expert, 128 W2 rows), 32 rows (two 16-row tiles)
 // per wavefront.  W2 first (NS >= I / 128 steps in registers), then the
 // expert's intermediate rows, 16 per pass, from the workspace into LDS;
 // writes o.
 template <int NS>
-__global__ __launch_bounds__(256, 2) void down_decode_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
+__global__ __launch_bounds__(256, DN_WG_PER_CU(NS)) void down_decode_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
                                                              const uint8_t* __restrict__ qsc_ws,
                                                              float* __restrict__ o, int Tk) {
   __shared__ __attribute__((aligned(16))) uint8_t qlds[DN_ROWS][MAX_I + 16];
@@ -1279,7 +1284,8 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       return hipGetLastError();
     }
     const int dn_items = max_active * (a.H / 128);
-    const dim3 g2(dn_items < cus * 2 ? dn_items : cus * 2), b2(256);
+    const int dn_occ = DN_WG_PER_CU(is <= 2 ? 2 : is <= 5 ? 5 : is <= 8 ? 8 : 16);
+    const dim3 g2(dn_items < cus * dn_occ ? dn_items : cus * dn_occ), b2(256);
     if (is <= 2) hipLaunchKernelGGL(down_decode_kernel<2>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
     else if (is <= 5) hipLaunchKernelGGL(down_decode_kernel<5>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
     else if (is <= 8) hipLaunchKernelGGL(down_decode_kernel<8>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
