@@ -97,6 +97,8 @@ def test_route_edge_cases():
     surv = rng.random(300).astype(np.float32)
     check_route(ties, 8, surv)                                                  # multi-chunk with dead rows
     check_route(rng.standard_normal((5, 1024)).astype(np.float32), 16)           # E = 1024, k = 16
+    check_route(rng.standard_normal((100, 1024)).astype(np.float32), 16, surv[:100])   # the same, ranked over CUs
+    check_route(rng.standard_normal((40, 512)).astype(np.float32), 8, surv[:40])        # E = 512
     check_route(rng.standard_normal((3, 1)).astype(np.float32), 1)              # E = 1
     check_route(rng.standard_normal((64, 32)).astype(np.float32), 4, np.zeros(64, np.float32))   # all dead
     check_route(rng.standard_normal((700, 256)).astype(np.float32), 8)          # ragged last chunk
