@@ -284,7 +284,9 @@ def main():
             "config": {"workload": f"{cfg.name} MoE layer step: T={T}, H={H}, E={E}, top-{k}, I={I}, MXFP4 experts, "
                                    f"FP8 block-32 activations, + dense FP8 block-32 projection M={T}, K=N=4096",
                        "rows": T, "hidden": H, "experts": E, "top_k": k, "intermediate": I,
-                       "touched_experts": touched, "bytes_per_step": step_bytes, "weight_copies": R,
+                       "touched_experts": touched, "experts_of_all_rows": len(all_ids),
+                       "weight_bytes_skipped": (len(all_ids) - touched) * EXPERT_BYTES(H, I),
+                       "bytes_per_step": step_bytes, "weight_copies": R,
                        "launch": "hip_graph_per_step" if args.graph else "eager", "step_calls": step_variant,
                        "prefetch": bool(args.prefetch)},
         })
