@@ -12,7 +12,7 @@ from test_gpu_parity import ffn_parity
 pytestmark = pytest.mark.gpu
 
 
-def sweep_shapes(n=6, seed=2026):
+def sweep_shapes(n=12, seed=2026):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
