@@ -14,6 +14,11 @@ namespace {
 
 thread_local const char* g_variant = "";
 std::atomic<int> g_ffn_path{0};
+thread_local float* g_diag_h = nullptr;          // mx_set_ffn_diag: gate/up values of this thread's FFN calls
+thread_local size_t g_diag_h_bytes = 0;
+
+// The diagnostic gate/up buffer must hold T*k rows of 2I floats.
+bool diag_h_fits(int64_t Tk, int I) { return g_diag_h == nullptr || g_diag_h_bytes >= (size_t)Tk * 2 * I * 4; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -136,9 +141,16 @@ mx_status moe_route_live(const float* logits, int T, int E, int k, const float* 
                       slot_pos, ws, ws_bytes, stream);
 }
 
-mx_status moe_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h, size_t* off_o) {
-  if (T < 0 || H < 128 || I < 32 || k < 1 || !off_q || !off_q_sc || !off_h || !off_o) return MX_EINVAL;
-  mx::ffn_ws_layout(T, H, I, k, off_q, off_q_sc, off_h, off_o);
+mx_status moe_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_o) {
+  if (T < 0 || H < 128 || I < 32 || k < 1 || !off_q || !off_q_sc || !off_o) return MX_EINVAL;
+  mx::ffn_ws_layout(T, H, I, k, off_q, off_q_sc, off_o);
+  return MX_OK;
+}
+
+mx_status mx_set_ffn_diag(float* h, size_t h_bytes) {
+  if (h != nullptr && !aligned(h, 16)) return MX_EINVAL;
+  g_diag_h = h;
+  g_diag_h_bytes = h ? h_bytes : 0;
   return MX_OK;
 }
 
@@ -162,14 +174,15 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H, co
       !aligned(w13_sc, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) || !aligned(perm, 4) ||
       !aligned(slot_pos, 4))
     return MX_EINVAL;
-  if (!ws || ws_bytes < mx::ffn_ws_bytes(T, H, E, I, k)) return MX_EWORKSPACE;
+  // the kernels of the requested path (automatic: either path) must support (H, I): never a silent fallback
+  const int path = mx::ffn_resolve_path(g_ffn_path.load(), (int64_t)T * k, H, I);
+  if (path == 0) return MX_EUNSUPPORTED;
+  if (!ws || ws_bytes < mx::ffn_ws_bytes(T, H, E, I, k) || !diag_h_fits((int64_t)T * k, I)) return MX_EWORKSPACE;
   if (!aligned(ws, 256)) return MX_EINVAL;
-  const int path = g_ffn_path.load();
-  if (!mx::ffn_path_supported(path, H, I)) return MX_EUNSUPPORTED;
   if (T == 0) { g_variant = "ffn:empty"; return MX_OK; }
   const mx::FfnArgs a{x, x_sc, T, H, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y};
   const char* v = "";
-  const hipError_t e = mx::launch_ffn(a, ws, path, static_cast<hipStream_t>(stream), &v);
+  const hipError_t e = mx::launch_ffn(a, ws, path, static_cast<hipStream_t>(stream), &v, nullptr, g_diag_h);
   if (e == hipSuccess) g_variant = v;
   return from_hip(e);
 }
@@ -181,7 +194,7 @@ mx_status moe_layer_decode1(const float* logits, int E, int k, const float* surv
                             size_t ws_bytes, void* stream) {
   if (E < 1 || E > mx::MAX_E || k < 1 || k > E || k > mx::MAX_K || H < 128 || I < 32) return MX_EINVAL;
   if (H % 32 != 0 || I % 32 != 0) return MX_EINVAL;
-  if (H % 128 != 0 || H > 128 * 8 * mx::MAX_PARTS || I > mx::MAX_I || !mx::ffn_path_supported(1, H, I))
+  if (H % 128 != 0 || H > 128 * 8 * mx::MAX_PARTS || I > mx::MAX_I || mx::ffn_resolve_path(1, k, H, I) != 1)
     return MX_EUNSUPPORTED;
   if (!logits || !x || !x_sc || !w13 || !w13_sc || !w2 || !w2_sc || !topk_ids || !topk_w || !expert_offsets ||
       !perm || !slot_pos || !y)
@@ -190,12 +203,12 @@ mx_status moe_layer_decode1(const float* logits, int E, int k, const float* surv
       !aligned(y, 16) || !aligned(x_sc, 4) || !aligned(w13_sc, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
       !aligned(expert_offsets, 4) || !aligned(perm, 4) || !aligned(slot_pos, 4))
     return MX_EINVAL;
-  if (!ws || ws_bytes < mx::ffn_ws_bytes(1, H, E, I, k)) return MX_EWORKSPACE;
+  if (!ws || ws_bytes < mx::ffn_ws_bytes(1, H, E, I, k) || !diag_h_fits(k, I)) return MX_EWORKSPACE;
   if (!aligned(ws, 256)) return MX_EINVAL;
   const mx::FfnArgs a{x, x_sc, 1, H, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y};
   const mx::FusedRoute fr{logits, survival, skip_below, topk_ids, topk_w, expert_offsets, perm, slot_pos};
   const char* v = "";
-  const hipError_t e = mx::launch_ffn(a, ws, 1, static_cast<hipStream_t>(stream), &v, &fr);
+  const hipError_t e = mx::launch_ffn(a, ws, 1, static_cast<hipStream_t>(stream), &v, &fr, g_diag_h);
   if (e == hipSuccess) g_variant = v;
   return from_hip(e);
 }
@@ -206,7 +219,10 @@ mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w
   if (M < 1 || N < 1 || K < 32 || K % 32 != 0) return MX_EINVAL;
   if (y_dtype != MX_OUT_BF16 && y_dtype != MX_OUT_F32) return MX_EINVAL;
   if (N % 16 != 0 || K > 128 * 8 * mx::MAX_PARTS) return MX_EUNSUPPORTED;
-  if ((int64_t)M * N >= (int64_t(1) << 31) || (int64_t)M * K >= (int64_t(1) << 40)) return MX_EUNSUPPORTED;
+  // the tiled kernel addresses both operands with 32-bit byte offsets
+  if ((int64_t)M * N >= (int64_t(1) << 31) || (int64_t)M * K >= (int64_t(1) << 32) ||
+      (int64_t)N * K >= (int64_t(1) << 32))
+    return MX_EUNSUPPORTED;
   if (!aligned(a, 16) || !aligned(w, 16) || !aligned(a_sc, 4) || !aligned(w_sc, 4) || !aligned(y, 4)) return MX_EINVAL;
   const char* v = "";
   const hipError_t e =

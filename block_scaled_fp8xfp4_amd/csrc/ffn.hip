@@ -5,7 +5,10 @@
 // TileLang": SwiGLU with per-block FP8 quantization, reductions in a fixed
 // order; DeepSeek-V4.1-Flash-4x-DGX-Spark-TP4 README, settings table, row
 // "Experts": per-slot buffer and a fixed-order sum instead of atomics, 64-row
-// tiles for 576-wide experts at prefill sizes).
+// tiles for 576-wide experts at prefill sizes).  The prefill kernels here use
+// 128-row expert tiles for gate/up and 32-row tiles for the down projection
+// (measured faster on MI355X than 64-row tiles; a tile never changes a
+// result, since every element runs the same chain).
 //
 // Both paths evaluate every output element with the same MFMA chain (all K
 // steps in order, see mx_device.hpp) and the same SwiGLU/requant routine, so
@@ -30,8 +33,9 @@
 //                       wavefronts; gathered activation rows and weight rows
 //                       staged through swizzled, double-buffered LDS one MFMA
 //                       step at a time; SwiGLU + requant in the epilogue.
-//   down_prefill_kernel 64-row tile x 256 W2 rows per workgroup; the tile's
-//                       whole intermediate (K = I) sits in LDS.
+//   down_prefill_kernel (expert, 256 W2 rows) items: the W2 rows stay in
+//                       registers while the expert's 32-row tiles of the
+//                       intermediate stream through LDS.
 //   Both run persistent grids whose blocks are remapped so that each XCD
 //   walks a contiguous range of (expert, row tile, column tile) items and
 //   shares weights and activations in its own L2.
@@ -44,7 +48,6 @@ namespace mx {
 
 constexpr int DEC_MAX_STEPS = 40;                 // decode gate/up: H <= 5120 held in registers
 constexpr int DOWN_MAX_STEPS = MAX_I / KSTEP;     // 16
-constexpr int PF_ROWS = 64;                       // prefill expert tile rows
 constexpr int PF_NCOLS = 256;                     // prefill down: W2 rows per workgroup
 constexpr int PF_MAX_I = 608;                     // prefill down: W2 slice of 256 rows x (I/32 + 1) chunks in LDS
 constexpr int XCDS = 8;
@@ -237,7 +240,8 @@ constexpr int DEC_SPITCH = DEC_MAX_STEPS + 1;     // LDS pitch (dwords) of the s
 // in LDS (16 rows x H / 32 bytes, one coalesced span).  The four 16 x 16
 // results meet in LDS, where one pass turns each row's 32 gate/up pairs into
 // one requantized block.  Writes q, its scale, and the fp32 h = [gate | up]
-// of every pair.  ONE (T = 1): every pair is row 0, whose activations are
+// of every pair when h is non-null (diagnostics).  ONE (T = 1): every pair
+// is row 0, whose activations are
 // requested before the route is read.  EXACT: H = 128 NS, so every address
 // offset is a constant.
 //
@@ -412,8 +416,10 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
           const uint32_t d = requant2_e4m3(v0, v1, sc);
           *reinterpret_cast<uint16_t*>(qws + p * I + blk * 32 + c) = (uint16_t)d;
           if ((tid & 15) == 0) qsc_ws[p * nb + blk] = (uint8_t)sc;
-          *reinterpret_cast<float2*>(h + p * 2 * I + blk * 32 + c) = gg;
-          *reinterpret_cast<float2*>(h + p * 2 * I + I + blk * 32 + c) = uu;
+          if (h != nullptr) {                                   // diagnostics only
+            *reinterpret_cast<float2*>(h + p * 2 * I + blk * 32 + c) = gg;
+            *reinterpret_cast<float2*>(h + p * 2 * I + I + blk * 32 + c) = uu;
+          }
         }
       }
     };
@@ -709,14 +715,15 @@ struct GuStage {
 // + 64): four 16-row A tiles against eight 16-row B tiles (4 gate + 4 up).
 // One MFMA step (K = 128) per stage; the gathered activation rows (16 KB),
 // the weight rows (16 KB) and their scale dwords go straight from global
-// memory into one of four LDS buffers (no registers), three stages ahead of
-// the matrix cores; within a stage each activation fragment is read from LDS
+// memory into one of NSTG LDS buffers (no registers), NSTG - 1 stages ahead
+// of the matrix cores; within a stage each activation fragment is read from LDS
 // while the previous one is multiplied.  Each lane fetches the global chunk that belongs at its
 // LDS slot, so the buffers come out XOR-swizzled by 16-byte chunk and the 16
 // rows one MFMA operand read touches fall in distinct banks.
 template <int NSTG>
 __global__ __launch_bounds__(GU_NT, GU_WG_PER_CU) void gu_prefill_kernel(FfnArgs a, uint8_t* __restrict__ qws,
-                                                                         uint8_t* __restrict__ qsc_ws, int Tk,
+                                                                         uint8_t* __restrict__ qsc_ws,
+                                                                         float* __restrict__ h, int Tk,
                                                                          int* __restrict__ queue) {
   constexpr int NBD = GU_BN * 4 / GU_NT;          // B chunk DMAs per thread per stage
   constexpr int DMA_PER_STAGE = 4 + NBD + 2;      // per thread: 4 A + NBD B chunks, 1 A + 1 B scale dword
@@ -901,6 +908,13 @@ __global__ __launch_bounds__(GU_NT, GU_WG_PER_CU) void gu_prefill_kernel(FfnArgs
               qrow[cb + col] = (uint8_t)d;
               qrow[cb + 16 + col] = (uint8_t)(d >> 8);
               if (col == 0) qsc_ws[(int64_t)(p0 + row) * nb + cb / 32] = (uint8_t)sc;
+              if (h != nullptr) {                               // diagnostics only: the fp32 gate/up values
+                float* hrow = h + (int64_t)(p0 + row) * 2 * I;
+                hrow[cb + col] = acc[m][2 * blk][i];
+                hrow[cb + 16 + col] = acc[m][2 * blk + 1][i];
+                hrow[I + cb + col] = acc[m][4 + 2 * blk][i];
+                hrow[I + cb + 16 + col] = acc[m][5 + 2 * blk][i];
+              }
             }
           }
         }
@@ -1172,30 +1186,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // ================================================================= host ===
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-// workspace: [q: Tk*I][q_sc: Tk*I/32][h: Tk*2I fp32][o: Tk*H fp32], each 256-byte aligned
-void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h, size_t* off_o) {
+// workspace: [q: Tk*I][q_sc: Tk*I/32][o: Tk*H fp32][queue counters][scratch row], each 256-byte aligned
+void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_o) {
   const size_t Tk = (size_t)T * k;
   *off_q = 0;
   *off_q_sc = align256(Tk * I);
-  *off_h = *off_q_sc + align256(Tk * (I / 32));
-  *off_o = *off_h + align256(Tk * 2 * I * 4);
+  *off_o = *off_q_sc + align256(Tk * (I / 32));
   (void)H;
 }
 
 size_t ffn_ws_bytes(int T, int H, int E, int I, int k) {
   (void)E;
-  size_t q, qs, h, o;
-  ffn_ws_layout(T, H, I, k, &q, &qs, &h, &o);
+  size_t q, qs, o;
+  ffn_ws_layout(T, H, I, k, &q, &qs, &o);
   return o + align256((size_t)T * k * H * 4) + 256 + 256;      // + the work-queue counters + a scratch row (64 floats)
 }
 
 // Row pairs at or below which the decode kernels are chosen.
 constexpr int DECODE_MAX_PAIRS = 1024;
 
-bool ffn_path_supported(int path, int H, int I) {
-  if (path == 1) return H <= KSTEP * DEC_MAX_STEPS;
-  if (path == 2) return I <= PF_MAX_I && H % PF_NCOLS == 0;
-  return true;
+static bool decode_path_ok(int H, int I) { return H % KSTEP == 0 && H <= KSTEP * DEC_MAX_STEPS && I <= MAX_I; }
+static bool prefill_path_ok(int H, int I) { return H % PF_NCOLS == 0 && I <= PF_MAX_I; }
+
+int ffn_resolve_path(int path, int64_t Tk, int H, int I) {
+  const bool dec = decode_path_ok(H, I), pre = prefill_path_ok(H, I);
+  if (path == 1) return dec ? 1 : 0;
+  if (path == 2) return pre ? 2 : 0;
+  if (dec && (Tk <= DECODE_MAX_PAIRS || !pre)) return 1;
+  return pre ? 2 : 0;
 }
 
 // Diagnostic phase events of this thread's FFN calls (set_ffn_phase_events).
@@ -1228,23 +1246,21 @@ static void launch_gu_one(int hs, dim3 g0, dim3 b0, size_t lds, hipStream_t stre
 }
 
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
-                      const FusedRoute* fr) {
+                      const FusedRoute* fr, float* h) {
   const int Tk = a.T * a.k;
+  // the caller validated the shape; a path that cannot run it is never launched
+  path = ffn_resolve_path(path, Tk, a.H, a.I);
+  if (path == 0) return hipErrorInvalidValue;
   uint8_t* base = static_cast<uint8_t*>(ws);
-  size_t oq, oqs, oh, oo;
-  ffn_ws_layout(a.T, a.H, a.I, a.k, &oq, &oqs, &oh, &oo);
+  size_t oq, oqs, oo;
+  ffn_ws_layout(a.T, a.H, a.I, a.k, &oq, &oqs, &oo);
   uint8_t* qws = base + oq;
   uint8_t* qsc = base + oqs;
-  float* h = reinterpret_cast<float*>(base + oh);
   float* o = reinterpret_cast<float*>(base + oo);
   int* queue = reinterpret_cast<int*>(base + oo + align256((size_t)Tk * a.H * 4));   // work-queue counters
   float* junk = reinterpret_cast<float*>(base + oo + align256((size_t)Tk * a.H * 4) + 256);   // scratch row
   const int cus = num_cus();
   const int max_active = a.E < Tk ? a.E : Tk;
-  if (path == 0) {
-    const bool dec_ok = ffn_path_supported(1, a.H, a.I), pre_ok = ffn_path_supported(2, a.H, a.I);
-    path = ((Tk <= DECODE_MAX_PAIRS && dec_ok) || !pre_ok) ? 1 : 2;
-  }
   phase(0, stream);
   if (path == 1) {
     const int R = a.T < DEC_ROWS ? a.T : DEC_ROWS;               // rows of one expert never exceed T
@@ -1252,6 +1268,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     const int gu_items = max_active * (a.I / 32);
     const int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
     const int hs = a.H / KSTEP, is = (a.I + KSTEP - 1) / KSTEP;
+    if (hs > DEC_MAX_STEPS || is > DOWN_MAX_STEPS) return hipErrorInvalidValue;   // the kernels' register arrays hold every step
     const dim3 g0(gu_grid), b0(256);
 #define MX_GU(NS_, EX_, ONE_) \
   hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, ONE_, 0>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R, FusedRoute{})
@@ -1300,13 +1317,13 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     gu_grid = (gu_grid + XCDS - 1) / XCDS * XCDS;
     dn_grid = (dn_grid + XCDS - 1) / XCDS * XCDS;
     hipLaunchKernelGGL(clear_i32_kernel, dim3(1), dim3(64), 0, stream, queue, 64);
-    hipLaunchKernelGGL(gu_prefill_kernel<GU_STAGES>, dim3(gu_grid), dim3(GU_NT), 0, stream, a, qws, qsc, Tk, queue);
+    hipLaunchKernelGGL(gu_prefill_kernel<GU_STAGES>, dim3(gu_grid), dim3(GU_NT), 0, stream, a, qws, qsc, h, Tk, queue);
     phase(1, stream);
     if (a.I <= 2 * KSTEP)
       hipLaunchKernelGGL(down_prefill_kernel<2>, dim3(dn_grid), dim3(DN_NT), 0, stream, a, qws, qsc, o, junk, Tk, queue + 32);
     else
       hipLaunchKernelGGL(down_prefill_kernel<5>, dim3(dn_grid), dim3(DN_NT), 0, stream, a, qws, qsc, o, junk, Tk, queue + 32);
-    *variant = "ffn:gu_prefill64+down_prefill64+combine";
+    *variant = "ffn:gu_prefill128+down_prefill32+combine";
     phase(2, stream);
   }
   const dim3 cgrid((a.H / 4 + 255) / 256, a.T < 65535 ? a.T : 65535);

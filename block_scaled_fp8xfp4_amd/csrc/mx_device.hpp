@@ -138,15 +138,19 @@ __device__ __forceinline__ uint32_t encode_e2m1(float v, uint32_t sc) {
   return code | sign;
 }
 
-// SwiGLU of one gate/up pair in fp32: silu(g) * u, silu(g) = g / (1 + e^-g),
-// with the hardware exponential and reciprocal (a few ulp; the FP8 requant
-// that follows keeps 3 mantissa bits).  Contraction is off so every kernel
-// that inlines it rounds identically.
+// SwiGLU of one gate/up pair: silu(g) * u, silu(g) = g / (1 + e^-g),
+// evaluated in double (exponential of the device math library, IEEE
+// division) and rounded once to fp32.  The rounding of a into the FP8
+// requant that follows then depends on the fp32 gate/up values alone, not on
+// the precision of a short fp32 evaluation (with the hardware exponential and
+// reciprocal, a few results per 10^5 landed on the other side of an E4M3
+// rounding midpoint).  Contraction is off so every kernel that inlines it
+// rounds identically.
 __device__ __forceinline__ float swiglu(float g, float u) {
 #pragma clang fp contract(off)
-  const float d = 1.0f + __expf(-g);
-  const float s = g * __builtin_amdgcn_rcpf(d);
-  return s * u;
+  const double gd = (double)g;
+  const double s = gd / (1.0 + exp(-gd));
+  return (float)(s * (double)u);
 }
 
 // Maximum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), in

@@ -37,11 +37,14 @@ struct FusedRoute {
   int32_t* ids; float* w; int32_t* offsets; int32_t* perm; int32_t* slot_pos;
 };
 size_t ffn_ws_bytes(int T, int H, int E, int I, int k);
-void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h, size_t* off_o);
-// path: 0 automatic, 1 decode kernels, 2 prefill kernels
-bool ffn_path_supported(int path, int H, int I);
+void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_o);
+// path: 0 automatic, 1 decode kernels, 2 prefill kernels.  Returns the path
+// that runs T*k pairs of an (H, I) layer under the requested setting, or 0
+// when no kernel supports the shape (then nothing may be launched).
+int ffn_resolve_path(int path, int64_t Tk, int H, int I);
+// h: NULL, or fp32 [T*k][2I] that receives the gate/up values (diagnostics)
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
-                      const FusedRoute* fr = nullptr);
+                      const FusedRoute* fr = nullptr, float* h = nullptr);
 void set_ffn_phase_events(const hipEvent_t* ev, int n);
 
 constexpr int GEMM_PREFILL_MIN_M = 320;  // dense GEMM: rows from which the tiled kernel beats the decode kernel (measured)

@@ -87,12 +87,11 @@ class ExpertFFN:
         return self.y
 
     def ws_views(self):
-        """Workspace regions as tensors: q [T*k, I], q_sc [T*k, I/32] (uint8),
-        h [T*k, 2I] (fp32, decode path only) and o [T*k, H] (fp32)."""
+        """Workspace regions as tensors: q [T*k, I], q_sc [T*k, I/32] (uint8)
+        and o [T*k, H] (fp32, T > 1)."""
         Tk, H, I = self.T * self.k, self.H, self.I
-        oq, oqs, oh, oo = mxmoe.moe_ws_layout(self.T, H, I, self.k)
+        oq, oqs, oo = mxmoe.moe_ws_layout(self.T, H, I, self.k)
         q = self.ws[oq:oq + Tk * I].view(Tk, I)
         sc = self.ws[oqs:oqs + Tk * (I // 32)].view(Tk, I // 32)
-        h = self.ws[oh:oh + Tk * 2 * I * 4].view(torch.float32).view(Tk, 2 * I)
         o = self.ws[oo:oo + Tk * H * 4].view(torch.float32).view(Tk, H)
-        return q, sc, h, o
+        return q, sc, o

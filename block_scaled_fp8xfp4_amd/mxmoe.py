@@ -20,7 +20,7 @@ EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logit
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
            "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events",
            "moe_shared_expert_workspace_bytes", "moe_shared_expert", "mx_prefetch",
-           "moe_layer_decode1")
+           "moe_layer_decode1", "mx_set_ffn_diag")
 
 _lib = None
 
@@ -55,7 +55,9 @@ def load():
     lib.moe_expert_ffn_workspace_bytes.restype = SZ
     lib.moe_expert_ffn_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.moe_ws_layout.restype = I32
-    lib.moe_ws_layout.argtypes = [I32, I32, I32, I32, P, P, P, P]
+    lib.moe_ws_layout.argtypes = [I32, I32, I32, I32, P, P, P]
+    lib.mx_set_ffn_diag.restype = I32
+    lib.mx_set_ffn_diag.argtypes = [P, SZ]
     lib.moe_expert_ffn.restype = I32
     lib.moe_expert_ffn.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, P, I32, I32, P, P, SZ, P]
     lib.fp8_block_gemm.restype = I32
@@ -167,8 +169,8 @@ def moe_expert_ffn_workspace_bytes(T, H, E, I, k):
 
 
 def moe_ws_layout(T, H, I, k):
-    """Byte offsets (q, q_sc, h, o) of the FFN workspace regions."""
-    offs = [ctypes.c_size_t() for _ in range(4)]
+    """Byte offsets (q, q_sc, o) of the FFN workspace regions."""
+    offs = [ctypes.c_size_t() for _ in range(3)]
     _check(load().moe_ws_layout(T, H, I, k, *[ctypes.byref(o) for o in offs]), "moe_ws_layout")
     return tuple(o.value for o in offs)
 
@@ -224,6 +226,15 @@ def check_requant(lo, hi, mismatches, stream=None):
     finite floats with magnitude bits in [lo, hi), both signs, whose E4M3 code
     from the FFN's hardware conversion differs from the quantize encoder's."""
     _check(load().mx_check_requant(lo, hi, _ptr(mismatches), _stream(stream)), "mx_check_requant")
+
+
+def set_ffn_diag(h):
+    """Have this thread's later FFN calls also write their fp32 gate/up values
+    into h (float32 device tensor of at least T*k*2I elements); None stops it."""
+    if h is None:
+        _check(load().mx_set_ffn_diag(None, 0), "mx_set_ffn_diag")
+        return
+    _check(load().mx_set_ffn_diag(_ptr(h), h.numel() * h.element_size()), "mx_set_ffn_diag")
 
 
 def set_phase_events(events):

@@ -172,17 +172,20 @@ mx_status moe_route(const float* logits, int T, int E, int k,
  * Every product is accumulated in fp32 on the matrix cores in one fixed
  * order per output element, the same for every batch size and path.
  * Supported: H % 128 == 0, I % 32 == 0, 1 <= k <= 16, T*k < 2^31,
- *            T*H < 2^32 (the activations fit 32-bit byte offsets).
+ *            T*H < 2^32 (the activations fit 32-bit byte offsets), and a
+ *            layer shape that the kernels of the selected path implement
+ *            (mx_set_ffn_path; automatic = either): the decode kernels take
+ *            H <= 5120 and I <= 2048, the prefill kernels H % 256 == 0 and
+ *            I <= 608.  Any other (H, I) returns MX_EUNSUPPORTED before
+ *            anything is launched (e.g. H = 6144 with I = 1024).
  * ws: device scratch of at least moe_expert_ffn_workspace_bytes(T,H,E,I,k)
  *     bytes (256-byte aligned).  Its layout is documented for diagnostics
  *     and filled in by moe_ws_layout(): the FP8 intermediate q [T*k][I] and
  *     its scales SC [T*k][I/32] (row p = bucket position, written by every
- *     path), the fp32 gate/up values h [T*k][2I] (written by the decode
- *     path only) and the fp32 per-slot outputs o [T*k][H] (every path).
+ *     path) and the fp32 per-slot outputs o [T*k][H] (T > 1).
  */
 size_t    moe_expert_ffn_workspace_bytes(int T, int H, int E, int I, int k);
-mx_status moe_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_h,
-                        size_t* off_o);
+mx_status moe_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_o);
 mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H,
                          const float* topk_w, const int32_t* expert_offsets,
                          const int32_t* perm, const int32_t* slot_pos, int k,
@@ -221,7 +224,9 @@ mx_status moe_layer_decode1(const float* logits, int E, int k, const float* surv
  * order per element; y is [M][N] bf16 (MX_OUT_BF16, RNE of the fp32 result)
  * or fp32 (MX_OUT_F32).  Supported: K % 32 == 0 (a K that is not a multiple
  * of 128 ends in a partial MFMA step, zero-filled on both operands; scale
- * rows then need no alignment), K <= 16384, N % 16 == 0, M >= 1.
+ * rows then need no alignment), K <= 16384, N % 16 == 0, M >= 1, M*N < 2^31,
+ * and M*K, N*K < 2^32 (operands addressed with 32-bit byte offsets); beyond
+ * these MX_EUNSUPPORTED.  a, w 16-byte aligned; a_sc, w_sc, y 4-byte aligned.
  */
 mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc,
                          const uint8_t* w, const uint8_t* w_sc,
@@ -276,13 +281,27 @@ const char* mx_status_string(mx_status s);
 const char* mx_last_variant(void);
 
 /*
- * Path selection for moe_expert_ffn: 0 = automatic (by T*k), 1 = decode
- * kernels (16-row tiles, weights streamed straight to registers), 2 =
- * prefill kernels (64-row tiles staged through LDS).  Both paths give
- * bitwise identical results; this exists so tests can prove it.  Process-
- * wide; returns the previous setting, or MX_EINVAL for other values.
+ * Path selection for moe_expert_ffn: 0 = automatic (by T*k and the layer
+ * shape), 1 = decode kernels (16-row matrix-core tiles, weights streamed
+ * straight to registers), 2 = prefill kernels (128-row gate/up tiles and
+ * 32-row down tiles staged through LDS).  Both paths give bitwise identical
+ * results; this exists so tests can prove it.  A shape the selected path
+ * does not implement makes moe_expert_ffn return MX_EUNSUPPORTED.
+ * Process-wide; returns the previous setting, or MX_EINVAL for other values.
  */
 int mx_set_ffn_path(int path);
+
+/*
+ * Diagnostic gate/up output (for parity tests of the gate/up GEMM: the
+ * product path never writes it).  With h set, every later moe_expert_ffn and
+ * moe_layer_decode1 call of this thread, on either path, also writes the fp32
+ * gate/up values of every live pair to h: row p = bucket position, [2I]
+ * floats (gate columns, then up columns), the values the SwiGLU consumed.
+ * h: caller-owned device memory, 16-byte aligned; h_bytes its size.  A call
+ * whose T*k*2I*4 bytes exceed h_bytes returns MX_EWORKSPACE.  h = NULL stops
+ * the writes.  MX_EINVAL for a misaligned h.
+ */
+mx_status mx_set_ffn_diag(float* h, size_t h_bytes);
 
 /*
  * Diagnostic for the intermediate requant (FP8 E4M3 under the block's E8M0

@@ -55,6 +55,8 @@ def _load():
     lib.or_moe_rows.argtypes = [P, P, i32, P, P, P, i32, P, P, P, P, i32, i32, P, i32, P, i32]
     lib.or_pair_ffn.restype = i32
     lib.or_pair_ffn.argtypes = [P, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P]
+    lib.or_gate_up_pairs.restype = i32
+    lib.or_gate_up_pairs.argtypes = [P, P, i32, P, P, i32, P, P, i32, P, i32]
     lib.or_down_combine.restype = i32
     lib.or_down_combine.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, P, i32, P, i32]
     lib.or_swiglu_requant.restype = i32
@@ -204,6 +206,20 @@ def pair_ffn(x, x_sc, t, e, w13, w13_sc, w2, w2_sc):
     _load().or_pair_ffn(_p(x), _p(x_sc), H, int(t), int(e), _p(w13), _p(w13_sc), _p(w2), _p(w2_sc),
                         I, _p(h), _p(a), _p(q), _p(q_sc), _p(o))
     return dict(h=h, a=a, q=q, q_sc=q_sc, o=o)
+
+
+def gate_up_pairs(x, x_sc, ts, es, w13, w13_sc, threads=0):
+    """fp32 gate/up values h [n, 2I] of the pairs (ts[i], es[i]) (gate columns, then up)."""
+    x, x_sc = _c(x, np.uint8), _c(x_sc, np.uint8)
+    H = x.shape[1]
+    I = w13.shape[1] // 2
+    ts, es = _c(ts, np.int32), _c(es, np.int32)
+    w13, w13_sc = _c(w13, np.uint8), _c(w13_sc, np.uint8)
+    h = np.empty((len(ts), 2 * I), np.float32)
+    if _load().or_gate_up_pairs(_p(x), _p(x_sc), H, _p(ts), _p(es), len(ts), _p(w13), _p(w13_sc), I, _p(h),
+                                threads):
+        raise ValueError("bad gate_up_pairs arguments")
+    return h
 
 
 def swiglu_requant(h):

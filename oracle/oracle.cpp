@@ -435,6 +435,16 @@ int or_swiglu_requant(const float* h, int64_t n, int I, uint8_t* q, uint8_t* q_s
   return 0;
 }
 
+// Gate/up values of n (token, expert) pairs, one thread per pair: h [n][2I],
+// row i = gate_up(ts[i], es[i]) (diagnostics of the gate/up GEMM alone).
+int or_gate_up_pairs(const uint8_t* x, const uint8_t* x_sc, int H, const int32_t* ts, const int32_t* es, int n,
+                     const uint8_t* w13, const uint8_t* w13_sc, int I, float* h, int threads) {
+  if (H % 32 || I % 32 || n < 0) return -1;
+  const Layer L{x, x_sc, H, w13, w13_sc, nullptr, nullptr, I};
+  parallel_for(n, threads, [&](int64_t i) { gate_up(L, ts[i], es[i], h + i * 2 * I); });
+  return 0;
+}
+
 // One pair with its intermediates (diagnostics): h[2I], a[I], q[I], q_sc[I/32], o[H].
 int or_pair_ffn(const uint8_t* x, const uint8_t* x_sc, int H, int t, int e,
                 const uint8_t* w13, const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I,

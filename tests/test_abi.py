@@ -50,9 +50,11 @@ def test_workspace_sizes_are_pure_host_functions(lib):
     assert mxmoe.moe_route_workspace_bytes(8192, 256, 8) >= 32 * 256 * 4
     b = mxmoe.moe_expert_ffn_workspace_bytes(8192, 4096, 256, 576, 8)
     assert b >= 65536 * 4096 * 4 + 65536 * 576
-    oq, oqs, oh, oo = mxmoe.moe_ws_layout(8192, 4096, 576, 8)
-    assert oq == 0 and oqs >= 65536 * 576 and oh >= oqs + 65536 * 18 and oo >= oh + 65536 * 1152 * 4
+    oq, oqs, oo = mxmoe.moe_ws_layout(8192, 4096, 576, 8)
+    assert oq == 0 and oqs >= 65536 * 576 and oo >= oqs + 65536 * 18
     assert oo + 65536 * 4096 * 4 <= b
+    # no fp32 gate/up region: those values go to the caller's diagnostic buffer only
+    assert b < oo + 65536 * 4096 * 4 + 65536 * 1152 * 4
     assert mxmoe.moe_expert_ffn_workspace_bytes(1, 64, 1, 32, 1) == 0       # H < 128: invalid
 
 
@@ -122,11 +124,69 @@ def test_ffn_rejects_bad_arguments(lib):
     assert ffn(lib, T=1 << 20, H=4096, k=1) == mxmoe.MX_EUNSUPPORTED             # T*H >= 2^32
 
 
+@pytest.mark.parametrize("H,I", [(6144, 1024), (5248, 576), (5376, 640), (16384, 2048)])
+def test_ffn_rejects_shapes_no_path_implements(lib, H, I):
+    """(H, I) beyond the decode kernels (H <= 5120, I <= 2048) and the prefill
+    kernels (H % 256 == 0, I <= 608) is refused on the host, whatever T, for
+    the automatic setting and for each forced path; nothing runs silently."""
+    for T in (1, 48, 8192):
+        assert ffn(lib, T=T, H=H, I=I, k=8, E=256) == mxmoe.MX_EUNSUPPORTED, (T, H, I)
+    for path in (1, 2):
+        old = mxmoe.set_ffn_path(path)
+        try:
+            assert ffn(lib, T=48, H=H, I=I, k=8, E=256) == mxmoe.MX_EUNSUPPORTED, (path, H, I)
+        finally:
+            mxmoe.set_ffn_path(old)
+    assert layer1(lib, H=H, I=I) == mxmoe.MX_EUNSUPPORTED
+
+
+def test_ffn_forced_path_rejects_what_that_path_lacks(lib):
+    old = mxmoe.set_ffn_path(1)
+    try:
+        assert ffn(lib, T=4, H=5248, I=64) == mxmoe.MX_EUNSUPPORTED             # decode: H > 5120
+        assert ffn(lib, T=4, H=6144, I=64, ws=None) == mxmoe.MX_EUNSUPPORTED    # reported before the workspace
+    finally:
+        mxmoe.set_ffn_path(old)
+    old = mxmoe.set_ffn_path(2)
+    try:
+        assert ffn(lib, T=4, H=4096, I=640) == mxmoe.MX_EUNSUPPORTED            # prefill: I > 608
+        assert ffn(lib, T=4, H=384, I=64) == mxmoe.MX_EUNSUPPORTED              # prefill: H % 256
+    finally:
+        mxmoe.set_ffn_path(old)
+
+
+def layer1(lib, H=256, I=64, E=8, k=2, ws=FAKE_WS, ws_bytes=1 << 30):
+    return lib.moe_layer_decode1(FAKE, E, k, None, 0.2, FAKE, FAKE, H, FAKE, FAKE, FAKE, FAKE, I, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_layer_decode1_rejects_bad_arguments(lib):
+    assert layer1(lib, k=0) == mxmoe.MX_EINVAL
+    assert layer1(lib, k=9, E=8) == mxmoe.MX_EINVAL
+    assert layer1(lib, H=320) == mxmoe.MX_EUNSUPPORTED
+    assert layer1(lib, ws=None) == mxmoe.MX_EWORKSPACE
+
+
+def test_ffn_diagnostic_buffer(lib):
+    """mx_set_ffn_diag: misaligned buffers are refused; a call whose gate/up
+    values do not fit the buffer fails with MX_EWORKSPACE before any launch."""
+    assert lib.mx_set_ffn_diag(ctypes.c_void_p((1 << 20) + 4), 1 << 20) == mxmoe.MX_EINVAL
+    assert lib.mx_set_ffn_diag(FAKE, 4 * 2 * 2 * 64 * 4 - 4) == mxmoe.MX_OK   # T*k*2I*4 - 4 bytes
+    try:
+        assert ffn(lib, T=4, k=2, I=64) == mxmoe.MX_EWORKSPACE
+        assert layer1(lib, k=8, I=64) == mxmoe.MX_EWORKSPACE                  # 1 row x k = 8 pairs do not fit
+    finally:
+        assert lib.mx_set_ffn_diag(None, 0) == mxmoe.MX_OK
+
+
 def gemm(lib, M=1, N=64, K=256, ydt=0, a=FAKE):
     return lib.fp8_block_gemm(a, FAKE, FAKE, FAKE, M, N, K, FAKE, ydt, None)
 
 
 def test_gemm_rejects_bad_arguments(lib):
+    assert gemm(lib, M=(1 << 20), N=1024, K=4096) == mxmoe.MX_EUNSUPPORTED   # M*K >= 2^32 (32-bit operand offsets)
+    assert gemm(lib, M=16, N=(1 << 19), K=8192) == mxmoe.MX_EUNSUPPORTED     # N*K >= 2^32
+    assert gemm(lib, M=(1 << 16), N=(1 << 15), K=64) == mxmoe.MX_EUNSUPPORTED   # M*N >= 2^31
     assert gemm(lib, M=0) == mxmoe.MX_EINVAL
     assert gemm(lib, K=100) == mxmoe.MX_EINVAL
     assert gemm(lib, K=16384 + 128) == mxmoe.MX_EUNSUPPORTED

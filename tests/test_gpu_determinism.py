@@ -1,0 +1,123 @@
+"""Determinism of the kernels that pace their global -> LDS transfers by hand
+(explicit vmcnt counts the compiler cannot check) and hand out work through
+atomic queues: the prefill gate/up and down kernels, the tiled dense GEMM and
+the tiled router logits (forum thread post #4, "512K context", "Quality and
+correctness" and "Testing": pipeline stages reused before their data landed
+gave wrong results under co-resident load until fenced; post #6, "A race in
+TileLang's warp-specialized pipeline").
+
+Each call is repeated 200 times on its full-size workload and every result is
+compared bit for bit with the first; then the same calls run while a
+bandwidth-heavy copy streams on a second stream (default priority), so other
+work shares the CUs, the caches and the memory system.  Each loop stops at its
+first mismatch."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_fp8xfp4_amd import mxmoe, synth
+from block_scaled_fp8xfp4_amd.layer import ExpertFFN, RouterLogits
+from gpu_common import dev, moe_workload, say
+
+pytestmark = pytest.mark.gpu
+
+REPEATS = 200
+STRESSED = 100
+
+
+class Stressor:
+    """Copies between two 512 MiB buffers on a second stream (default priority)."""
+
+    def __init__(self):
+        n = 128 << 20
+        self.src = torch.randn(n, device="cuda")
+        self.dst = torch.empty_like(self.src)
+        self.stream = torch.cuda.Stream()
+        self.stream.wait_stream(torch.cuda.current_stream())
+
+    def enqueue(self, copies):
+        with torch.cuda.stream(self.stream):
+            for _ in range(copies):
+                self.dst.copy_(self.src)
+
+    def drain(self):
+        self.stream.synchronize()
+
+
+def repeat_bitwise(call, outs, what, copies):
+    """Run call() REPEATS times alone, then STRESSED times beside the stressor;
+    every run's outputs must equal the first run's bit for bit."""
+    call()
+    ref = [o.clone() for o in outs]
+    for i in range(REPEATS):
+        call()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), f"{what}: repeat {i} differs from the first run"
+    st = Stressor()
+    try:
+        for i in range(STRESSED):
+            st.enqueue(copies)
+            call()
+            for o, r in zip(outs, ref):
+                assert torch.equal(o, r), f"{what}: run {i} beside the copy stream differs from the first run"
+            if i % 10 == 9:
+                st.drain()
+    finally:
+        st.drain()
+    say(f"{what}: {REPEATS} repeats + {STRESSED} beside a copy stream, all bitwise equal")
+
+
+def test_prefill_ffn_is_deterministic():
+    """The 8192-token routed layer on the prefill kernels: y and the FP8
+    intermediate (codes and scales)."""
+    inp, r, layer = moe_workload("prefill")
+    c = inp.cfg
+    route = layer.gpu_route()
+    ffn = ExpertFFN(c.T, c.H, c.E, c.I, c.k)
+    d = layer.d
+
+    def call():
+        ffn(d["x"], d["x_sc"], route, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"])
+
+    call()
+    assert mxmoe.last_variant().startswith("ffn:gu_prefill")
+    q, qsc, _ = ffn.ws_views()
+    P = c.T * c.k
+    repeat_bitwise(call, [ffn.y, q[:P], qsc[:P]], "prefill FFN", copies=6)
+
+
+def test_prefill_gemm_is_deterministic():
+    """The tiled dense GEMM at M = 8192, K = N = 4096 (bf16 and fp32 out)."""
+    inp = synth.dense_inputs()
+    wq, wsc = oracle.quantize_e4m3(inp.w)
+    a = synth.hidden_rows(11, 8192, 4096)
+    aq, asc = oracle.quantize_e4m3(a)
+    da, dasc, dw, dwsc = dev(aq), dev(asc), dev(wq), dev(wsc)
+    y16 = torch.empty((8192, 4096), dtype=torch.bfloat16, device="cuda")
+    y32 = torch.empty((8192, 4096), dtype=torch.float32, device="cuda")
+
+    def call():
+        mxmoe.fp8_block_gemm(da, dasc, dw, dwsc, y16, mxmoe.MX_OUT_BF16)
+        mxmoe.fp8_block_gemm(da, dasc, dw, dwsc, y32, mxmoe.MX_OUT_F32)
+
+    call()
+    assert mxmoe.last_variant().startswith("gemm:prefill")
+    repeat_bitwise(call, [y16, y32], "prefill GEMM", copies=2)
+
+
+def test_prefill_router_logits_are_deterministic():
+    """The tiled router logits at T = 8192, H = 4096, E = 256."""
+    inp = synth.moe_inputs("prefill")
+    c = inp.cfg
+    hidden = dev(inp.x).to(torch.bfloat16)
+    gate = dev(synth.router_gate("prefill")).to(torch.bfloat16)
+    logits = torch.empty((c.T, c.E), dtype=torch.float32, device="cuda")
+    rl = RouterLogits(c.T, c.H, c.E)
+
+    def call():
+        rl(hidden, gate, logits)
+
+    call()
+    assert mxmoe.last_variant().startswith("logits:prefill")
+    repeat_bitwise(call, [logits], "prefill router logits", copies=1)

@@ -16,7 +16,7 @@ def run(layer, rows=None, path=0):
     old = mxmoe.set_ffn_path(path)
     try:
         y, route, ffn = layer.gpu_y(rows)
-        q, qsc, _, o = ffn.ws_views()
+        q, qsc, o = ffn.ws_views()
         variant = mxmoe.last_variant()
         return host(y), host(q), host(qsc), route, variant
     finally:

@@ -9,7 +9,7 @@ import torch
 import oracle
 from block_scaled_fp8xfp4_amd import mxmoe, synth
 from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route
-from gpu_common import Layer, dev, host, say, small_workload
+from gpu_common import Layer, assert_close, dev, host, say, small_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -44,9 +44,8 @@ def test_decode_workload_bitwise_and_oracle():
     inp, r, layer = moe_workload("decode")
     y, route = run_both(layer, inp.logits)
     ref = layer.oracle_y(r)
-    err = np.abs(y - ref).max() / np.abs(ref).max()
-    say(f"layer_decode1: end-to-end {err:.2e}")
-    assert err <= 5e-3
+    err, cos = assert_close(y, ref, "layer_decode1 end to end")
+    say(f"layer_decode1: end-to-end {err:.2e}, cosine {cos:.8f}")
 
 
 @pytest.mark.parametrize("shape", [

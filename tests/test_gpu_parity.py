@@ -10,7 +10,8 @@ import torch
 import oracle
 from block_scaled_fp8xfp4_amd import mxmoe, synth
 from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route, quantize
-from gpu_common import Layer, assert_close, dev, host, moe_workload, say, small_workload
+from gpu_common import (Layer, assert_close, dev, ffn_parity, gpu_ffn_with_h, host, moe_workload, say,
+                        small_workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -110,86 +111,12 @@ def test_route_edge_cases():
 
 
 # ----------------------------------------------------------------- expert FFN
-E4M3_MAG = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
-
-
-def check_requant(q_gpu, sc_gpu, q_ref, sc_ref, a_ref):
-    """GPU requant of the GPU's own h against the oracle's requant of the same
-    fp32 h: equal, except where the oracle's a sits on a rounding boundary
-    (fp32 SwiGLU on the GPU, double in the oracle), where the neighbouring
-    code is also a correct result."""
-    n, I = q_ref.shape
-    flips = 0
-    for r in range(n):
-        for b in range(I // 32):
-            blk = a_ref[r, b * 32:(b + 1) * 32].astype(np.float64)
-            if sc_gpu[r, b] != sc_ref[r, b]:
-                amax = np.abs(blk).max()
-                assert abs(amax / 2.0 ** np.round(np.log2(amax)) - 1) < 1e-6, ("scale flip off a boundary", r, b)
-                flips += 1
-                continue
-            X = 2.0 ** (int(sc_ref[r, b]) - 127)
-            for i in np.nonzero(q_gpu[r, b * 32:(b + 1) * 32] != q_ref[r, b * 32:(b + 1) * 32])[0]:
-                cg, cr = int(q_gpu[r, b * 32 + i]), int(q_ref[r, b * 32 + i])
-                t = abs(blk[i] / X)
-                mg, mr = E4M3_MAG[cg & 0x7F], E4M3_MAG[cr & 0x7F]
-                assert abs((cg & 0x7F) - (cr & 0x7F)) == 1, ("non-adjacent codes", r, b, i, cg, cr)
-                assert abs(t - (mg + mr) / 2) <= 1e-6 * t, ("flip off a rounding midpoint", r, b, i, t, mg, mr)
-                flips += 1
-    return flips
-
-
-# End-to-end bar for the seeded workloads.  Every fp32-accumulated stage above
-# meets 2e-3 * max|ref| on identical inputs; the end-to-end comparison also
-# crosses the FP8 requant, where the matrix cores' accumulation (measured at a
-# few 1e-6 relative per 128-long dot product) moves some intermediates across
-# a rounding midpoint, each such flip shifting y by up to ~1e-3 of max|y|.
-E2E_TOL = 5e-3
-
-
-def ffn_parity(inp, r, layer, rows=None, what="", e2e_tol=E2E_TOL, max_pairs=96, route=None):
-    """Staged parity on identical inputs: (i) gate/up h vs the oracle, (ii) the
-    requant of the GPU's h vs the oracle's requant of the same h, (iii) y vs the
-    oracle's down projection + combine of the GPU's intermediate; then the
-    end-to-end y vs the full oracle."""
-    c = inp.cfg
-    old = mxmoe.set_ffn_path(1)             # the decode path publishes h for stage (i)
-    try:
-        y, route, ffn = layer.gpu_y(route=route)
-    finally:
-        mxmoe.set_ffn_path(old)
-    assert np.array_equal(host(route.perm), r["perm"]) and np.array_equal(host(route.offsets), r["offsets"])
-    yg = host(y)
-    q, qsc, h, _ = (host(t) for t in ffn.ws_views())
-    rows = np.arange(c.T, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
-    pairs = [(int(t), j, int(r["slot_pos"][t, j])) for t in rows for j in range(c.k) if r["slot_pos"][t, j] >= 0]
-    sample = pairs if len(pairs) <= max_pairs else [pairs[i] for i in
-                                                    np.random.default_rng(0).choice(len(pairs), max_pairs, False)]
-    # (i) gate/up: fp32 accumulation on the matrix cores vs the oracle's double
-    h_ref = np.stack([oracle.pair_ffn(layer.x, layer.x_sc, t, int(r["ids"][t, j]), layer.w13, layer.w13_sc,
-                                      layer.w2, layer.w2_sc)["h"] for t, j, p in sample]) if sample else None
-    if sample:
-        assert_close(h[[p for _, _, p in sample]], h_ref, what + " gate/up")
-    # (ii) SwiGLU + requant on identical fp32 h
-    P = int(r["offsets"][-1])
-    if P:
-        q_ref, sc_ref, a_ref = oracle.swiglu_requant(h[:P])
-        flips = check_requant(q[:P], qsc[:P], q_ref, sc_ref, a_ref)
-        assert flips <= max(2, P * c.I // 10000), flips
-    # (iii) down + combine from the GPU's intermediate
-    ref2 = oracle.down_combine(q, qsc, r["slot_pos"], r["ids"], r["w"], layer.w2, layer.w2_sc, rows=rows)
-    assert_close(yg[rows], ref2, what + " down+combine")
-    # end-to-end against the full oracle
-    ref = layer.oracle_y(r, rows)
-    err = np.abs(yg[rows] - ref).max() / max(np.abs(ref).max(), 1e-30)
-    g64, r64 = yg[rows].astype(np.float64).ravel(), ref.astype(np.float64).ravel()
-    cos = float(g64 @ r64 / max(np.linalg.norm(g64) * np.linalg.norm(r64), 1e-300)) if np.any(r64) else 1.0
-    say(f"{what}: end-to-end max|diff|/max|ref| = {err:.2e}, cosine = {cos:.8f}")
-    assert err <= e2e_tol, f"{what}: end-to-end {err:.2e} > {e2e_tol}"
-    assert cos >= 0.9999, f"{what}: end-to-end cosine {cos}"
-    live = r["live"].astype(bool)
-    assert np.all(yg[~live] == 0) and not np.any(np.signbit(yg[~live]))
-    return yg
+# Both kernel paths are checked against the oracle on their own outputs
+# (gpu_common.ffn_parity: gate/up of every live pair, the requant bit for bit
+# on identical h, down + combine from the GPU's own intermediate, end to end).
+def both_paths(layer):
+    c = layer.cfg
+    return (1, 2) if c.H % 256 == 0 and c.I <= 608 else (1,)
 
 
 @pytest.mark.parametrize("shape", [
@@ -201,34 +128,41 @@ def ffn_parity(inp, r, layer, rows=None, what="", e2e_tol=E2E_TOL, max_pairs=96,
 def test_ffn_small_shapes(shape):
     inp, r, layer = small_workload(**shape)
     say(f"ffn small {shape}")
-    # with I <= 160 one requant code flip (h differs from the oracle's by the
-    # matrix cores' accumulation) moves y by up to ~1e-2 of max|y|
-    ffn_parity(inp, r, layer, what=str(shape), e2e_tol=3e-2)
+    for path in both_paths(layer):
+        ffn_parity(inp, r, layer, what=str(shape), path=path)
 
 
-def test_ffn_tiny_workload():
+@pytest.mark.parametrize("path", [1, 2])
+def test_ffn_tiny_workload(path):
     inp, r, layer = moe_workload("tiny")
-    ffn_parity(inp, r, layer, what="tiny", e2e_tol=3e-2)
+    ffn_parity(inp, r, layer, what="tiny", path=path)
 
 
-def test_ffn_decode_workload():
+@pytest.mark.parametrize("path", [1, 2])
+def test_ffn_decode_workload(path):
     inp, r, layer = moe_workload("decode")
-    ffn_parity(inp, r, layer, what="decode")
+    ffn_parity(inp, r, layer, what="decode", path=path, strict_e2e=True)
 
 
-def test_ffn_verify_workload():
+@pytest.mark.parametrize("path", [1, 2])
+def test_ffn_verify_workload(path):
     inp, r, layer = moe_workload("verify")
-    yg = ffn_parity(inp, r, layer, what="verify")
+    yg = ffn_parity(inp, r, layer, what="verify", path=path, strict_e2e=True)
     dead = ~r["live"].astype(bool)
     assert dead.any() and np.all(yg[dead] == 0)
 
 
-def test_ffn_prefill_workload_sampled_rows():
+def test_ffn_prefill_workload_prefill_kernels():
+    """The 8192-token chunk on the prefill kernels (the path it takes):
+    every pair of 64 sampled rows (plus the first and last) staged against
+    the oracle; then the decode kernels on the same chunk give the same bits."""
     inp, r, layer = moe_workload("prefill")
-    rows = np.random.default_rng(4).choice(inp.cfg.T, 48, replace=False).astype(np.int32)
+    rows = np.random.default_rng(4).choice(inp.cfg.T, 62, replace=False).astype(np.int32)
     rows = np.concatenate([rows, [0, inp.cfg.T - 1]]).astype(np.int32)
-    say("ffn prefill: GPU run + oracle on 50 sampled rows")
-    ffn_parity(inp, r, layer, rows=rows, what="prefill sample")
+    say("ffn prefill: prefill kernels, oracle on every pair of 64 sampled rows")
+    y_pre = ffn_parity(inp, r, layer, rows=rows, what="prefill sample", path=2)
+    y_dec, _, _, _ = gpu_ffn_with_h(layer, 1)
+    assert np.array_equal(host(y_dec).view(np.uint32), y_pre.view(np.uint32))
 
 
 # ----------------------------------------------------------------- dense GEMM
@@ -334,15 +268,10 @@ def test_ffn_pages_shape_both_paths():
     inp = synth.small_moe(61, 4, 5120, 384, 8, 576)
     r = oracle.route(inp.logits, 8)
     layer = Layer(inp, np.unique(r["ids"]))
-    say("pages shape H=5120 E=384 I=576: decode path")
-    y_dec = ffn_parity(inp, r, layer, what="pages shape decode")
-    old = mxmoe.set_ffn_path(2)
-    try:
-        y_pre, _, _ = layer.gpu_y()
-    finally:
-        mxmoe.set_ffn_path(old)
-    assert mxmoe.last_variant().startswith("ffn:gu_prefill")
-    assert np.array_equal(host(y_pre), y_dec)
+    say("pages shape H=5120 E=384 I=576: decode and prefill paths")
+    y_dec = ffn_parity(inp, r, layer, what="pages shape", path=1)
+    y_pre = ffn_parity(inp, r, layer, what="pages shape", path=2)
+    assert np.array_equal(y_pre.view(np.uint32), y_dec.view(np.uint32))
     # the single-row fused layer on row 0
     d = layer.d
     route1 = Route(1, 384, 8)

@@ -12,7 +12,7 @@ import oracle
 from block_scaled_fp8xfp4_amd import mxmoe, synth
 from block_scaled_fp8xfp4_amd.layer import Route
 from gpu_common import dev, host, moe_workload, say
-from test_gpu_parity import ffn_parity
+from gpu_common import ffn_parity
 
 pytestmark = pytest.mark.gpu
 

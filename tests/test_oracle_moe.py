@@ -185,6 +185,27 @@ def test_gate_up_is_exact_on_integer_operands():
     assert np.all(res["o"] == 0)                                     # zero W2 -> zero output
 
 
+def test_gate_up_pairs_match_float64_matmul_and_pair_ffn():
+    """The batched gate/up diagnostic: each row within one fp32 ulp of a float64
+    matmul of torch/table-decoded operands (catches a transposed operand, a
+    wrong expert or token, a swapped gate/up half), equal to the single-pair
+    oracle's h, and independent of the thread count."""
+    inp = synth.small_moe(seed=12, T=5, H=256, E=6, k=3, I=64)
+    L = quantized_layer(inp)
+    ts = np.array([0, 4, 2, 2, 1, 3], np.int32)
+    es = np.array([5, 0, 1, 3, 5, 2], np.int32)
+    h = oracle.gate_up_pairs(L["x"], L["x_sc"], ts, es, L["w13"], L["w13_sc"])
+    h1 = oracle.gate_up_pairs(L["x"], L["x_sc"], ts, es, L["w13"], L["w13_sc"], threads=1)
+    assert np.array_equal(h, h1)
+    xd = dec_e4m3(L["x"], L["x_sc"])
+    for i, (t, e) in enumerate(zip(ts, es)):
+        ref = dec_e2m1(L["w13"][e], L["w13_sc"][e]) @ xd[t]
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(h[i] - ref) <= ulp)
+        single = oracle.pair_ffn(L["x"], L["x_sc"], t, e, L["w13"], L["w13_sc"], L["w2"], L["w2_sc"])["h"]
+        assert np.array_equal(h[i], single)
+
+
 def test_moe_is_linear_in_the_slots():
     """y_t equals the weighted sum of single-expert (k = 1, w = 1) evaluations."""
     inp = synth.small_moe(seed=9, T=3, H=128, E=6, k=3, I=64)
