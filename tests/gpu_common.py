@@ -109,6 +109,56 @@ def explain_code_differences(q_g, sc_g, a_g, q_r, sc_r, a_r):
     return nel, nsc
 
 
+class Layer:
+    """Oracle-quantized MoE layer (host arrays) plus device copies."""
+
+    def __init__(self, inp, experts=None):
+        c = inp.cfg
+        self.cfg, self.inp = c, inp
+        E, H, I = c.E, c.H, c.I
+        self.x, self.x_sc = oracle.quantize_e4m3(inp.x)
+        self.w13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+        self.w13_sc = np.full((E, 2 * I, H // 32), 127, np.uint8)
+        self.w2 = np.zeros((E, H, I // 2), np.uint8)
+        self.w2_sc = np.full((E, H, I // 32), 127, np.uint8)
+        experts = list(range(E)) if experts is None else sorted(set(int(e) for e in experts))
+        for i in range(0, len(experts), 32):
+            chunk = experts[i:i + 32]
+            w13 = inp.w13(chunk)
+            q, s = oracle.quantize_e2m1(w13.reshape(-1, H))
+            self.w13[chunk] = q.reshape(len(chunk), 2 * I, H // 2)
+            self.w13_sc[chunk] = s.reshape(len(chunk), 2 * I, H // 32)
+            del w13
+            w2 = inp.w2(chunk)
+            q, s = oracle.quantize_e2m1(w2.reshape(-1, I))
+            self.w2[chunk] = q.reshape(len(chunk), H, I // 2)
+            self.w2_sc[chunk] = s.reshape(len(chunk), H, I // 32)
+            del w2
+        self.d = {n: dev(getattr(self, n)) for n in ("x", "x_sc", "w13", "w13_sc", "w2", "w2_sc")}
+
+    def oracle_y(self, r, rows=None):
+        return oracle.moe_rows(self.x, self.x_sc, r["ids"], r["w"], r["live"], self.w13, self.w13_sc,
+                               self.w2, self.w2_sc, rows=rows)
+
+    def gpu_route(self, rows=None):
+        c, inp = self.cfg, self.inp
+        logits = inp.logits if rows is None else inp.logits[rows]
+        surv = inp.survival if (rows is None or inp.survival is None) else inp.survival[rows]
+        route = Route(len(logits), c.E, c.k)
+        route(dev(logits), None if surv is None else dev(surv))
+        return route
+
+    def gpu_y(self, rows=None, route=None):
+        c = self.cfg
+        x = self.d["x"] if rows is None else self.d["x"][dev(np.asarray(rows, np.int64))]
+        x_sc = self.d["x_sc"] if rows is None else self.d["x_sc"][dev(np.asarray(rows, np.int64))]
+        route = self.gpu_route(rows) if route is None else route
+        ffn = ExpertFFN(x.shape[0], c.H, c.E, c.I, c.k)
+        y = ffn(x.contiguous(), x_sc.contiguous(), route, self.d["w13"], self.d["w13_sc"], self.d["w2"],
+                self.d["w2_sc"])
+        return y, route, ffn
+
+
 def gpu_ffn_with_h(layer, path, route=None):
     """Run the routed FFN on the given path (1 decode, 2 prefill kernels) with
     the diagnostic gate/up output on; returns (y, route, ffn, h) on the host
