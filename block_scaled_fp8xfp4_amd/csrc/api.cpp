@@ -187,6 +187,39 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H, co
   return from_hip(e);
 }
 
+size_t moe_expert_ffn_noalloc_max_bytes(void) { return mx::NOALLOC_SCRATCH_BYTES; }
+
+mx_status moe_expert_ffn_noalloc(const uint8_t* x, const uint8_t* x_sc, int T, int H, const float* topk_w,
+                                 const int32_t* expert_offsets, const int32_t* perm, const int32_t* slot_pos, int k,
+                                 const uint8_t* w13, const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc,
+                                 int E, int I, float* y, void* stream) {
+  if (T < 0 || k < 1 || k > mx::MAX_K || E < 1 || E > mx::MAX_E || H < 128 || I < 32) return MX_EINVAL;
+  if (H % 32 != 0 || I % 32 != 0) return MX_EINVAL;
+  if (H % 128 != 0 || H > 128 * 8 * mx::MAX_PARTS || I > mx::MAX_I) return MX_EUNSUPPORTED;
+  if ((int64_t)T * k >= (int64_t(1) << 31)) return MX_EINVAL;
+  if ((int64_t)T * H >= (int64_t(1) << 32)) return MX_EUNSUPPORTED;
+  if (!x || !x_sc || !topk_w || !expert_offsets || !perm || !slot_pos || !w13 || !w13_sc || !w2 || !w2_sc || !y)
+    return MX_EINVAL;
+  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(x_sc, 4) ||
+      !aligned(w13_sc, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) || !aligned(perm, 4) ||
+      !aligned(slot_pos, 4))
+    return MX_EINVAL;
+  const int path = mx::ffn_resolve_path(g_ffn_path.load(), (int64_t)T * k, H, I);
+  if (path == 0) return MX_EUNSUPPORTED;
+  // the built-in scratch holds what moe_expert_ffn_workspace_bytes asks of a caller
+  if (mx::ffn_ws_bytes(T, H, E, I, k) > mx::NOALLOC_SCRATCH_BYTES || !diag_h_fits((int64_t)T * k, I))
+    return MX_EWORKSPACE;
+  if (T == 0) { g_variant = "ffn:empty"; return MX_OK; }
+  void* ws = nullptr;
+  hipError_t e = mx::noalloc_scratch(&ws);
+  if (e != hipSuccess) return MX_EHIP;
+  const mx::FfnArgs a{x, x_sc, T, H, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y};
+  const char* v = "";
+  e = mx::launch_ffn(a, ws, path, static_cast<hipStream_t>(stream), &v, nullptr, g_diag_h);
+  if (e == hipSuccess) g_variant = v;
+  return from_hip(e);
+}
+
 mx_status moe_layer_decode1(const float* logits, int E, int k, const float* survival, float skip_below,
                             const uint8_t* x, const uint8_t* x_sc, int H, const uint8_t* w13, const uint8_t* w13_sc,
                             const uint8_t* w2, const uint8_t* w2_sc, int I, int32_t* topk_ids, float* topk_w,

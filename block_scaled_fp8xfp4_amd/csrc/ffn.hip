@@ -40,6 +40,8 @@
 //   walks a contiguous range of (expert, row tile, column tile) items and
 //   shares weights and activations in its own L2.
 // combine_kernel adds w_tj * o_tj over the slots in order j = 0..k-1.
+#include <atomic>
+
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 #include "route_device.hpp"
@@ -1331,6 +1333,33 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
   else hipLaunchKernelGGL(combine_kernel<MAX_K>, cgrid, dim3(256), 0, stream, o, a.topk_w, a.slot_pos, a.T, a.H, a.k, Tk, a.y);
   phase(3, stream);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------- allocation-free entry ==
+// The FFN workspace of moe_expert_ffn_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): its device address is looked up once per device with
+// hipGetSymbolAddress and cached.
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+static constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::atomic<void*> g_scratch_ptr[NOALLOC_MAX_DEVICES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {                           // first call on this device (it is current): look the copy up
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace mx

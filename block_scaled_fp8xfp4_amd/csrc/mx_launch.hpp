@@ -46,6 +46,11 @@ int ffn_resolve_path(int path, int64_t Tk, int H, int I);
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
                       const FusedRoute* fr = nullptr, float* h = nullptr);
 void set_ffn_phase_events(const hipEvent_t* ev, int n);
+// moe_expert_ffn_noalloc: the library's own device scratch array (per GPU,
+// NOALLOC_SCRATCH_BYTES) in place of a caller workspace; *ptr receives its
+// address on the current device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
 
 constexpr int GEMM_PREFILL_MIN_M = 320;  // dense GEMM: rows from which the tiled kernel beats the decode kernel (measured)
 hipError_t launch_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc,

@@ -20,7 +20,7 @@ EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logit
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
            "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events",
            "moe_shared_expert_workspace_bytes", "moe_shared_expert", "mx_prefetch",
-           "moe_layer_decode1", "mx_set_ffn_diag")
+           "moe_layer_decode1", "mx_set_ffn_diag", "moe_expert_ffn_noalloc", "moe_expert_ffn_noalloc_max_bytes")
 
 _lib = None
 
@@ -60,6 +60,10 @@ def load():
     lib.mx_set_ffn_diag.argtypes = [P, SZ]
     lib.moe_expert_ffn.restype = I32
     lib.moe_expert_ffn.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, P, I32, I32, P, P, SZ, P]
+    lib.moe_expert_ffn_noalloc.restype = I32
+    lib.moe_expert_ffn_noalloc.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, P, I32, I32, P, P]
+    lib.moe_expert_ffn_noalloc_max_bytes.restype = SZ
+    lib.moe_expert_ffn_noalloc_max_bytes.argtypes = []
     lib.fp8_block_gemm.restype = I32
     lib.fp8_block_gemm.argtypes = [P, P, P, P, I32, I32, I32, P, I32, P]
     lib.moe_shared_expert_workspace_bytes.restype = SZ
@@ -181,6 +185,19 @@ def moe_expert_ffn(x, x_sc, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_
     _check(load().moe_expert_ffn(_ptr(x), _ptr(x_sc), T, H, _ptr(topk_w), _ptr(expert_offsets), _ptr(perm),
                                  _ptr(slot_pos), k, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), E, I, _ptr(y),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_expert_ffn_noalloc(x, x_sc, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y,
+                           stream=None):
+    """moe_expert_ffn without a caller workspace (the library's own device scratch array)."""
+    T, H = x.shape
+    _check(load().moe_expert_ffn_noalloc(_ptr(x), _ptr(x_sc), T, H, _ptr(topk_w), _ptr(expert_offsets), _ptr(perm),
+                                         _ptr(slot_pos), k, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), E, I,
+                                         _ptr(y), _stream(stream)), "moe_expert_ffn_noalloc")
+
+
+def moe_expert_ffn_noalloc_max_bytes():
+    return load().moe_expert_ffn_noalloc_max_bytes()
 
 
 def moe_layer_decode1(logits, k, survival, skip_below, x, x_sc, w13, w13_sc, w2, w2_sc, E, I, topk_ids, topk_w,

@@ -194,6 +194,31 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H,
                          float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_expert_ffn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results, bit for bit, as moe_expert_ffn,
+ * with the workspace replaced by a device array inside the library, one per
+ * GPU, of moe_expert_ffn_noalloc_max_bytes() bytes (16 MiB), held from the
+ * library's first use on that GPU until the process ends.  The call itself
+ * allocates and frees nothing.  A shape whose
+ * moe_expert_ffn_workspace_bytes(T, H, E, I, k) exceeds that size returns
+ * MX_EWORKSPACE before anything is launched (at H = 4096, I = 576: up to
+ * about 980 row pairs T*k, e.g. 48 rows at k = 16).  Every call on one GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialized by the caller.  The array keeps
+ * the last call's contents; nothing in it needs to start at zero (the work
+ * queue counters are cleared by a kernel of each call).  Other arguments and
+ * errors as moe_expert_ffn.
+ */
+size_t    moe_expert_ffn_noalloc_max_bytes(void);
+mx_status moe_expert_ffn_noalloc(const uint8_t* x, const uint8_t* x_sc, int T, int H,
+                                 const float* topk_w, const int32_t* expert_offsets,
+                                 const int32_t* perm, const int32_t* slot_pos, int k,
+                                 const uint8_t* w13, const uint8_t* w13_sc,
+                                 const uint8_t* w2, const uint8_t* w2_sc, int E, int I,
+                                 float* y, void* stream);
+
+/*
  * The routed-expert layer of ONE row in two launches: moe_route and
  * moe_expert_ffn for T = 1 fused, the top-k gate running inside the gate/up
  * kernel (every workgroup ranks the row's E logits itself, so the experts'

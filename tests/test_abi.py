@@ -264,3 +264,18 @@ def test_phase_events_reject_bad_arguments(lib):
     assert lib.mx_set_phase_events(None, 3) == mxmoe.MX_EINVAL
     assert lib.mx_set_phase_events(None, 4) == mxmoe.MX_EINVAL
     assert lib.mx_set_phase_events(None, 0) == mxmoe.MX_OK
+
+
+def test_noalloc_rejects_what_does_not_fit(lib):
+    """moe_expert_ffn_noalloc: argument errors as moe_expert_ffn, and a shape
+    whose workspace exceeds the built-in 16 MiB array is refused on the host."""
+    def call(T=4, H=256, E=8, I=64, k=2, x=FAKE):
+        return lib.moe_expert_ffn_noalloc(x, FAKE, T, H, FAKE, FAKE, FAKE, FAKE, k, FAKE, FAKE, FAKE, FAKE, E, I,
+                                          FAKE, None)
+    assert lib.moe_expert_ffn_noalloc_max_bytes() == 16 << 20
+    assert call(k=0) == mxmoe.MX_EINVAL
+    assert call(x=None) == mxmoe.MX_EINVAL
+    assert call(H=6144, I=1024) == mxmoe.MX_EUNSUPPORTED
+    assert mxmoe.moe_expert_ffn_workspace_bytes(8192, 4096, 256, 576, 8) > 16 << 20
+    assert call(T=8192, H=4096, E=256, I=576, k=8) == mxmoe.MX_EWORKSPACE
+    assert call(T=1024, H=4096, E=256, I=576, k=8) == mxmoe.MX_EWORKSPACE
