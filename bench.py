@@ -73,6 +73,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to exceed 1.5 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-verify", action="store_true", help="decode line without the verification-batch object")
     ap.add_argument("--graph", action="store_true", help="replay one HIP graph per step instead of eager launches")
     ap.add_argument("--unfused", action="store_true",
                     help="decode step at T=1: moe_route + moe_expert_ffn instead of moe_layer_decode1")
@@ -266,12 +267,12 @@ def main():
             torch.cuda.synchronize()
             live_ms = l0.elapsed_time(l1) / args.steps
             live_bytes = touched_l * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * E * 4 + T * H * 4 + dense_bytes
-            result["router_live"] = {"reuse_below": thr, "rows_reusing": reusing, "pairs": T * k,
+            live_obj = {"reuse_below": thr, "rows_reusing": reusing, "pairs": T * k,
                                      "touched_experts": touched_l, "ms_per_step": round(live_ms, 5),
                                      "gbs": round(live_bytes / (live_ms * 1e-3) / 1e9, 2),
                                      "variant": live_variant}
             route(logits, surv)                                  # back to the skip-mode routing
-        result.update({
+        out = {
             "metric": "decode weight-stream GB/s (% HBM peak) + prefill expert TFLOP/s (% MFMA peak)",
             "value": round(step_bytes / (ms * 1e-3) / 1e9, 2),
             "unit": "GB/s",
@@ -289,8 +290,10 @@ def main():
                        "bytes_per_step": step_bytes, "weight_copies": R,
                        "launch": "hip_graph_per_step" if args.graph else "eager", "step_calls": step_variant,
                        "prefetch": bool(args.prefetch)},
-        })
-        return inp, touched
+        }
+        if cfg.streams:
+            out["router_live"] = live_obj
+        return inp, touched, out
 
     # ------------------------------------------------------------ dense FP8 GEMM at decode sizes (M = 1, 16)
     def run_dense_decode(steps, warmup):
@@ -494,7 +497,20 @@ def main():
         cpu_cfg = synth.PREFILL
     else:
         cfg = synth.DECODE if args.workload == "decode" else synth.VERIFY
-        inp, touched = run_decode(cfg)
+        inp, touched, main_line = run_decode(cfg)
+        result.update(main_line)
+        if args.workload == "decode" and not args.no_verify:
+            # the speculative-verification batch (48 rows = 8 streams x (anchor + 5
+            # drafts), Zipf(1.1) expert popularity, rows with survival < 0.2 skip
+            # the routed experts): GB/s over the experts the live rows touch
+            _, _, v = run_decode(synth.VERIFY)
+            c = v["config"]
+            result["verify"] = {
+                "workload": c["workload"], "gbs": v["value"], "pct_hbm_peak": v["pct_hbm_peak"],
+                "ms_per_step": v["ms_per_step"], "bytes_per_step": c["bytes_per_step"],
+                "touched_experts": c["touched_experts"], "experts_of_all_rows": c["experts_of_all_rows"],
+                "weight_bytes_skipped": c["weight_bytes_skipped"], "roofline": v["roofline"],
+                "router_live": v.get("router_live")}
         result["dense_decode"] = run_dense_decode(args.steps, args.warmup)
         result["router_logits"] = run_router_logits(cfg, inp, args.steps, args.warmup)
         result["shared_expert"] = run_shared_expert(cfg, inp, args.steps, args.warmup)
@@ -512,13 +528,28 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, workload):
     """The oracle as it stands, timed on the host cores on a bounded sample of
     the same workload (same shapes and distributions)."""
     import oracle
     from block_scaled_fp8xfp4_amd import synth
 
-    threads = min(16, oracle.hardware_threads())
+    # the host's cores, capped by the CPU share this process has on the machine
+    # (OMP_NUM_THREADS when set, as on a shared GPU host: 16 cores per GPU)
+    hw = oracle.hardware_threads()
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(hw, share) if share > 0 else hw
     inp = synth.moe_inputs(cfg)
     r = oracle.route(inp.logits, cfg.k, inp.survival)
     rows = np.arange(min(cfg.T, 4 if workload == "prefill" else cfg.T), dtype=np.int32)
@@ -550,13 +581,15 @@ def cpu_baseline(cfg, workload):
     dt = (time.time() - t0) / reps
     if workload == "prefill":
         flop = live_pairs * (2 * 2 * I * H + 2 * H * I)
-        return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "host_cores": hw,
+                "cpu_model": cpu_model(), "kind": "oracle",
                 "sample": f"{len(rows)} of {cfg.T} prefill rows ({live_pairs} routed pairs), {reps} reps, "
                           f"{dt:.2f} s per rep"}
     touched = len(need)
     step_bytes = touched * EXPERT_BYTES(H, I) + len(rows) * (H + H // 32) + len(rows) * E * 4 \
         + len(rows) * H * 4 + d.cfg.N * (d.cfg.K + d.cfg.K // 32) + (d.cfg.K + d.cfg.K // 32) + d.cfg.N * 2
-    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "host_cores": hw,
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"the full {workload} step ({len(rows)} rows, {touched} experts, dense M=1), {reps} reps, "
                       f"{dt:.3f} s per rep"}
 

@@ -248,11 +248,14 @@ constexpr int DEC_SPITCH = DEC_MAX_STEPS + 1;     // LDS pitch (dwords) of the s
 // offset is a constant.
 //
 // RPER > 0 (single row, fused with the gate): every wavefront ranks the
-// row's logits itself (wave_topk with RPER logits per lane) instead of
-// reading a route; its k experts in ascending order are the items, expert
-// of rank r at bucket position r.  Workgroup 0's first wavefront writes the
-// route outputs exactly as the single-row route kernel does, for the down
-// kernel and the caller.
+// row's logits itself (the wavefront top-k with RPER logits per lane)
+// instead of reading a route.  Item i takes the expert of slot i / nb
+// (descending logit): the wavefront runs only the ranking rounds up to that
+// slot before issuing the expert's weight loads, and the remaining rounds
+// while they are in flight; the pair's bucket position, the rank of its
+// expert among the k in ascending order, is known by then.  Workgroup 0's
+// first wavefront writes the route outputs exactly as the single-row route
+// kernel does, for the down kernel and the caller.
 template <int NS, bool EXACT, bool ONE, int RPER>
 __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* __restrict__ qws,
                                                            uint8_t* __restrict__ qsc_ws, float* __restrict__ h,
@@ -291,26 +294,14 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
     if (tid < nsteps) xsv = reinterpret_cast<const uint32_t*>(a.x_sc)[tid];
   }
   WaveExperts we;                                               // every wavefront reads the expert list itself
-  int ridx = 0, rrank = 0, nitems;
+  constexpr int RP = RPER > 0 ? RPER : 1;
+  TopkState<RP> st;
+  bool live = true;
+  int nitems;
   if (RPER > 0) {
-    float rval;
-    wave_topk<(RPER > 0 ? RPER : 1)>(fr.logits, a.E, a.k, ridx, rval);
-    const bool live = fr.survival == nullptr || !(fr.survival[0] < fr.skip_below);
-    for (int i = 0; i < a.k; ++i) rrank += __builtin_amdgcn_readlane(ridx, i) < ridx ? 1 : 0;
-    if (blockIdx.x == 0 && wave == 0) {                         // the route outputs, as the single-row route kernel
-      const float wt = slot_weight(rval, a.k);
-      if (lane < a.k) {
-        fr.ids[lane] = ridx;
-        fr.w[lane] = wt;
-        fr.slot_pos[lane] = live ? rrank : -1;
-        fr.perm[live ? rrank : lane] = live ? lane : -1;
-      }
-      for (int e = lane; e <= a.E; e += 64) {
-        int below = 0;
-        for (int i = 0; i < a.k; ++i) below += __builtin_amdgcn_readlane(ridx, i) < e ? 1 : 0;
-        fr.offsets[e] = live ? below : 0;
-      }
-    }
+    const float sv = fr.survival != nullptr ? fr.survival[0] : 1.0f;   // in flight with the logits
+    topk_begin<RP>(st, fr.logits, a.E);
+    live = fr.survival == nullptr || !(sv < fr.skip_below);
     nitems = live ? a.k * nb : 0;
   } else {
     wave_experts_load(a.offsets, a.E, we);
@@ -319,11 +310,11 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int blk = item % nb;
     int e, p0, cnt;
-    if (RPER > 0) {                                             // the expert of rank item / nb
-      const int r = item / nb;
-      const unsigned long long m = __ballot(lane < a.k && rrank == r);
-      e = __builtin_amdgcn_readlane(ridx, __builtin_ctzll(m));
-      p0 = r;
+    if (RPER > 0) {                                             // the expert of slot item / nb
+      const int j = item / nb;
+      topk_rounds<RP>(st, j + 1);
+      e = __builtin_amdgcn_readlane(st.idx, j);
+      p0 = 0;                                                   // its bucket position: after the weight loads
       cnt = 1;
     } else {
       wave_tile(we, a.E, item / nb, e, p0, cnt);
@@ -363,6 +354,10 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
     u32x4 bw[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (EXACT || s < nsteps ? s : nsteps - 1) * 64);
+    if (RPER > 0) {                                             // the other slots, while the weights stream in
+      topk_rounds<RP>(st, a.k);
+      for (int i = 0; i < a.k; ++i) p0 += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
+    }
     // stage what the first pass needs (its loads were issued before the weights)
 #pragma unroll
     for (int i = 0; i < NBSV; ++i) {
@@ -410,12 +405,10 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
         const int r = tid >> 4, c = 2 * (tid & 15);
         const float2 gg = *reinterpret_cast<const float2*>(&hb[r * DEC_HPITCH + c]);
         const float2 uu = *reinterpret_cast<const float2*>(&hb[r * DEC_HPITCH + 32 + c]);
-        const float v0 = swiglu(gg.x, uu.x), v1 = swiglu(gg.y, uu.y);
-        const float m = row16_max(fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
+        uint32_t sc;
+        const uint32_t d = swiglu_requant2(gg.x, uu.x, gg.y, uu.y, &sc);   // rows past nrows: discarded
         if (r < nrows) {
           const int64_t p = p0 + r0 + r;
-          const uint32_t sc = e8m0_code_for_amax(m, 8);
-          const uint32_t d = requant2_e4m3(v0, v1, sc);
           *reinterpret_cast<uint16_t*>(qws + p * I + blk * 32 + c) = (uint16_t)d;
           if ((tid & 15) == 0) qsc_ws[p * nb + blk] = (uint8_t)sc;
           if (h != nullptr) {                                   // diagnostics only
@@ -454,6 +447,23 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
         lds_barrier();
       }
       run_pass(r0, nrows);
+    }
+  }
+  if (RPER > 0 && blockIdx.x == 0 && wave == 0) {              // the route outputs, as the single-row route kernel
+    topk_rounds<RP>(st, a.k);
+    int rrank = 0;                                              // lane j: position of slot j's expert in ascending order
+    for (int i = 0; i < a.k; ++i) rrank += __builtin_amdgcn_readlane(st.idx, i) < st.idx ? 1 : 0;
+    const float wt = slot_weight(st.val, a.k);
+    if (lane < a.k) {
+      fr.ids[lane] = st.idx;
+      fr.w[lane] = wt;
+      fr.slot_pos[lane] = live ? rrank : -1;
+      fr.perm[live ? rrank : lane] = live ? lane : -1;
+    }
+    for (int e = lane; e <= a.E; e += 64) {
+      int below = 0;
+      for (int i = 0; i < a.k; ++i) below += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
+      fr.offsets[e] = live ? below : 0;
     }
   }
 }
@@ -898,15 +908,13 @@ __global__ __launch_bounds__(GU_NT, GU_WG_PER_CU) void gu_prefill_kernel(FfnArgs
         for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v0 = swiglu(acc[m][2 * blk][i], acc[m][4 + 2 * blk][i]);
-            const float v1 = swiglu(acc[m][2 * blk + 1][i], acc[m][5 + 2 * blk][i]);
-            const float mx = row16_max(fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
-            const uint32_t sc = e8m0_code_for_amax(mx, 8);
+            uint32_t sc;
+            const uint32_t d = swiglu_requant2(acc[m][2 * blk][i], acc[m][4 + 2 * blk][i], acc[m][2 * blk + 1][i],
+                                               acc[m][5 + 2 * blk][i], &sc);
             const int row = wm * 64 + m * 16 + 4 * g + i;
             const int cb = c0 + wn * 64 + blk * 32;           // first column of the block
             if (row < nrows && cb < I) {
               uint8_t* qrow = qws + (int64_t)(p0 + row) * I;
-              const uint32_t d = requant2_e4m3(v0, v1, sc);
               qrow[cb + col] = (uint8_t)d;
               qrow[cb + 16 + col] = (uint8_t)(d >> 8);
               if (col == 0) qsc_ws[(int64_t)(p0 + row) * nb + cb / 32] = (uint8_t)sc;

@@ -177,6 +177,19 @@ __device__ __forceinline__ uint32_t requant2_e4m3(float a, float b, uint32_t sc)
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ta, tb, 0, false) & 0xFFFFu;
 }
 
+// SwiGLU + E4M3 requant of this lane's two elements of a block of 32 that is
+// spread over the 16 lanes of a DPP row (element 0 of lane c is column c of
+// the block, element 1 column c + 16): a = swiglu(g, u) (double, rounded
+// once), the block's scale code from max |a| (into *sc_out), and the two
+// codes (bits 0..7 and 8..15).  The same routine in every kernel that
+// requantizes an intermediate.
+__device__ __forceinline__ uint32_t swiglu_requant2(float g0, float u0, float g1, float u1, uint32_t* sc_out) {
+  const float a0 = swiglu(g0, u0), a1 = swiglu(g1, u1);
+  const uint32_t sc = e8m0_code_for_amax(row16_max(fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1))), 8);
+  *sc_out = sc;
+  return requant2_e4m3(a0, a1, sc);
+}
+
 // Quantize 32 fp32 values to E4M3: writes 32 code bytes as 8 dwords, returns the scale code.
 __device__ __forceinline__ uint32_t quantize32_e4m3(const float* v, uint32_t* out8) {
   float amax = 0.0f;

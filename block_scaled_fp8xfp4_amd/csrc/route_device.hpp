@@ -20,29 +20,45 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 }
 
 // One wavefront ranks the row at l.  PER = logits per lane (E <= 64 * PER);
-// lanes j < k end with (expert, logit) of slot j.  Lane l holds the block of
-// logits [PER l, PER l + PER), so lane order is index order: of the lanes
-// whose best key equals the round's maximum, the lowest one holds the lowest
-// index, and within a lane a strict comparison keeps the lowest position.
-// Each round is branch-free: one wavefront maximum, one ballot, one readlane.
+// after round j, lane j holds (expert, logit) of slot j.  Lane l holds the
+// block of logits [PER l, PER l + PER), so lane order is index order: of the
+// lanes whose best key equals the round's maximum, the lowest one holds the
+// lowest index, and within a lane a strict comparison keeps the lowest
+// position.  Each round is branch-free: one wavefront maximum, one ballot,
+// one readlane.  The rounds can be run in installments (topk_rounds), so a
+// caller that needs slot j only waits for j + 1 rounds before using it and
+// runs the rest later (e.g. while its loads are in flight).
 template <int PER>
-__device__ void wave_topk(const float* __restrict__ l, int E, int k, int& out_idx, float& out_val) {
+struct TopkState {
+  uint32_t key[PER];
+  int idx;                                                      // lane j: expert of slot j (after round j)
+  float val;                                                    // lane j: its logit
+  int done;                                                     // rounds run so far
+};
+
+template <int PER>
+__device__ __forceinline__ void topk_begin(TopkState<PER>& st, const float* __restrict__ l, int E) {
   const int lane = threadIdx.x & 63;
   float v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) v[i] = l[min(PER * lane + i, E - 1)];   // all loads in flight together
-  uint32_t key[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = PER * lane + i < E ? order_key(v[i]) : 0u;   // 0: below every logit
-  out_idx = 0;
-  out_val = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint32_t bk = key[0];                                       // this lane's best: ties keep the lower index
+  for (int i = 0; i < PER; ++i) st.key[i] = PER * lane + i < E ? order_key(v[i]) : 0u;   // 0: below every logit
+  st.idx = 0;
+  st.val = 0.0f;
+  st.done = 0;
+}
+
+template <int PER>
+__device__ __forceinline__ void topk_rounds(TopkState<PER>& st, int upto) {
+  const int lane = threadIdx.x & 63;
+  for (int j = st.done; j < upto; ++j) {
+    uint32_t bk = st.key[0];                                    // this lane's best: ties keep the lower index
     int bi = 0;
 #pragma unroll
     for (int i = 1; i < PER; ++i) {
-      const bool gt = key[i] > bk;
-      bk = gt ? key[i] : bk;
+      const bool gt = st.key[i] > bk;
+      bk = gt ? st.key[i] : bk;
       bi = gt ? i : bi;
     }
     const uint32_t m = __ockl_wfred_max_u32(bk);
@@ -50,10 +66,21 @@ __device__ void wave_topk(const float* __restrict__ l, int E, int k, int& out_id
     const int wbi = __builtin_amdgcn_readlane(bi, wl);
     const bool mine = lane == wl;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) key[i] = (mine && i == wbi) ? 0u : key[i];
-    out_idx = lane == j ? PER * wl + wbi : out_idx;
-    out_val = lane == j ? key_value(m) : out_val;
+    for (int i = 0; i < PER; ++i) st.key[i] = (mine && i == wbi) ? 0u : st.key[i];
+    st.idx = lane == j ? PER * wl + wbi : st.idx;
+    st.val = lane == j ? key_value(m) : st.val;
   }
+  st.done = upto > st.done ? upto : st.done;
+}
+
+// All k rounds at once: lanes j < k end with (expert, logit) of slot j.
+template <int PER>
+__device__ void wave_topk(const float* __restrict__ l, int E, int k, int& out_idx, float& out_val) {
+  TopkState<PER> st;
+  topk_begin<PER>(st, l, E);
+  topk_rounds<PER>(st, k);
+  out_idx = st.idx;
+  out_val = st.val;
 }
 
 // softmax over the k picked logits: w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), in double

@@ -26,17 +26,15 @@ __global__ __launch_bounds__(256) void swiglu_requant_kernel(const float* __rest
   const int64_t t = ok ? i / (I / 2) : 0;
   const int c = ok ? (int)(i % (I / 2)) * 2 : 0;
   const float* hr = h + t * 2 * I;
-  float a0 = 0.f, a1 = 0.f;
+  float2 g = {0.f, 0.f}, u = {0.f, 0.f};
   if (ok) {
-    const float2 g = *reinterpret_cast<const float2*>(hr + c);
-    const float2 u = *reinterpret_cast<const float2*>(hr + I + c);
-    a0 = swiglu(g.x, u.x);
-    a1 = swiglu(g.y, u.y);
+    g = *reinterpret_cast<const float2*>(hr + c);
+    u = *reinterpret_cast<const float2*>(hr + I + c);
   }
-  const float amax = row16_max(fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
-  const uint32_t sc = e8m0_code_for_amax(amax, 8);
+  uint32_t sc;
+  const uint32_t d = swiglu_requant2(g.x, u.x, g.y, u.y, &sc);
   if (!ok) return;
-  *reinterpret_cast<uint16_t*>(q + t * I + c) = (uint16_t)requant2_e4m3(a0, a1, sc);
+  *reinterpret_cast<uint16_t*>(q + t * I + c) = (uint16_t)d;
   if ((c & 31) == 0) q_sc[t * (I / 32) + c / 32] = (uint8_t)sc;
 }
 
