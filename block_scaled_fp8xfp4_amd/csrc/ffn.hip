@@ -468,6 +468,137 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
   }
 }
 
+// Single row (T = 1), gate/up: one wavefront per (pair, 8 intermediate
+// columns).  Its 16 weight rows are the 8 gate rows and the 8 up rows of
+// those columns (each output column of the matrix core is its own dot
+// product), streamed straight into registers over the whole K; the row's
+// activations are in LDS.  The SwiGLU of the 8 columns, a = silu(gate) * up
+// (double, rounded once to fp32), goes to abuf[j][I], row j = the pair's slot
+// (so that the down kernel can request it before reading the route); the
+// down kernel requantizes it (the block-32 scale needs 32 columns, four
+// wavefronts).
+// One-wavefront workgroups spread the 18.9 MB of a decode step's gate/up
+// weights over every CU, whose outstanding-miss capacity, not HBM, bounds a
+// stream this short.  RPER > 0: the gate runs here, as in gu_decode_kernel
+// (item i takes the expert of slot i / (I / 8); the ranking rounds past that
+// slot run while its weights are in flight); otherwise the pairs come from
+// the route's offsets.
+template <int NS, bool EXACT, int RPER>
+__global__ __launch_bounds__(64) void gu1_kernel(FfnArgs a, float* __restrict__ abuf, float* __restrict__ h, int Tk,
+                                                 FusedRoute fr) {
+  __shared__ __attribute__((aligned(16))) uint8_t xl[NS * KSTEP];
+  __shared__ uint32_t xs[NS];
+  __shared__ uint32_t bsc[16 * (NS + 1)];                       // [row][step] scale dwords, odd pitch
+  const int lane = threadIdx.x;
+  const int col = lane & 15, g = lane >> 4;
+  const int H = EXACT ? NS * KSTEP : a.H, I = a.I, ncg = I / 8;
+  const int nsteps = H / KSTEP, chunks = H / 16, spitch = nsteps | 1;
+  constexpr int XPT = (NS * 8 + 63) / 64;                       // 16-byte activation chunks per lane
+  u32x4 xv[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = lane + 64 * i;
+    xv[i] = (EXACT || c < chunks) ? ldg16(a.x + c * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+  uint32_t xsv = lane < nsteps ? reinterpret_cast<const uint32_t*>(a.x_sc)[lane] : 0x7F7F7F7Fu;
+  WaveExperts we;
+  constexpr int RP = RPER > 0 ? RPER : 1;
+  TopkState<RP> st;
+  bool live = true;
+  int nitems;
+  if (RPER > 0) {
+    const float sv = fr.survival != nullptr ? fr.survival[0] : 1.0f;   // in flight with the logits
+    topk_begin<RP>(st, fr.logits, a.E);
+    live = fr.survival == nullptr || !(sv < fr.skip_below);
+    nitems = live ? a.k * ncg : 0;
+  } else {
+    wave_experts_load(a.offsets, a.E, we);
+    nitems = wave_experts_scan(a.E, we) * ncg;
+  }
+  // the activation row into LDS (its loads were issued first)
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = lane + 64 * i;
+    if (EXACT || c < chunks) *reinterpret_cast<u32x4*>(xl + c * 16) = xv[i];
+  }
+  if (lane < nsteps) xs[lane] = xsv;
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int j = item / ncg, c0 = (item % ncg) * 8;
+    int e, p0 = 0, cnt = 1, slot = j;
+    if (RPER > 0) {
+      topk_rounds<RP>(st, j + 1);
+      e = __builtin_amdgcn_readlane(st.idx, j);
+    } else {
+      wave_tile(we, a.E, j, e, p0, cnt);
+      if (p0 < 0 || p0 >= Tk) cnt = 0;                          // malformed route: skip
+      slot = cnt ? a.perm[p0] : -1;                             // T = 1: perm[p] is the pair's slot
+      if (slot < 0 || slot >= a.k) cnt = 0;
+    }
+    // rows: lanes 0..7 the gate rows c0 + [0, 8), lanes 8..15 the up rows I + c0 + [0, 8)
+    const int64_t ebase = (int64_t)e * 2 * I;
+    const int64_t wrow = ebase + (col < 8 ? c0 + col : I + c0 + col - 8);
+    // scales of the 16 rows: two spans of 8 rows x nsteps dwords
+    constexpr int NBSV = (16 * NS + 63) / 64;
+    uint32_t bsv[NBSV];
+#pragma unroll
+    for (int i = 0; i < NBSV; ++i) {
+      const int idx = lane + 64 * i, r = idx / nsteps, sidx = idx % nsteps;
+      const int64_t sr = ebase + (r < 8 ? c0 + r : I + c0 + r - 8);
+      bsv[i] = idx < 16 * nsteps ? reinterpret_cast<const uint32_t*>(a.w13_sc + sr * (H / 32))[sidx] : 0u;
+    }
+    const uint8_t* wp = a.w13 + wrow * (H / 2) + g * 16;
+    u32x4 bw[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (EXACT || s < nsteps ? s : nsteps - 1) * 64);
+    if (RPER > 0) {                                             // the other slots, while the weights stream in
+      topk_rounds<RP>(st, a.k);
+      for (int i = 0; i < a.k; ++i) p0 += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
+    }
+    lds_barrier();                                              // the previous item's scale reads are done
+#pragma unroll
+    for (int i = 0; i < NBSV; ++i) {
+      const int idx = lane + 64 * i;
+      if (idx < 16 * nsteps) bsc[(idx / nsteps) * spitch + idx % nsteps] = bsv[i];
+    }
+    lds_barrier();
+    if (cnt == 0) continue;
+    // every row of the A tile is the activation row (output row 0 is kept)
+    const uint8_t* arow = xl + g * 16;
+    const uint32_t* bsrow = &bsc[col * spitch];
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (EXACT || s < nsteps) {
+        const u32x4 alo = *reinterpret_cast<const u32x4*>(arow + s * KSTEP);
+        const u32x4 ahi = *reinterpret_cast<const u32x4*>(arow + s * KSTEP + 64);
+        acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, xs[s] >> (8 * g), bsrow[s] >> (8 * g));
+      }
+    }
+    // lanes 0..15 hold output row 0: gate values in lanes 0..7, up values in 8..15
+    const float up = __shfl_down(acc[0], 8, 16);
+    if (h != nullptr && lane < 16)                              // diagnostics only
+      h[(int64_t)p0 * 2 * I + (col < 8 ? c0 + col : I + c0 + col - 8)] = acc[0];
+    if (lane < 8) abuf[(int64_t)slot * I + c0 + lane] = swiglu(acc[0], up);
+  }
+  if (RPER > 0 && blockIdx.x == 0) {                            // the route outputs, as the single-row route kernel
+    topk_rounds<RP>(st, a.k);
+    int rrank = 0;
+    for (int i = 0; i < a.k; ++i) rrank += __builtin_amdgcn_readlane(st.idx, i) < st.idx ? 1 : 0;
+    const float wt = slot_weight(st.val, a.k);
+    if (lane < a.k) {
+      fr.ids[lane] = st.idx;
+      fr.w[lane] = wt;
+      fr.slot_pos[lane] = live ? rrank : -1;
+      fr.perm[live ? rrank : lane] = live ? lane : -1;
+    }
+    for (int e = lane; e <= a.E; e += 64) {
+      int below = 0;
+      for (int i = 0; i < a.k; ++i) below += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
+      fr.offsets[e] = live ? below : 0;
+    }
+  }
+}
+
 // W2 operand of one 16-row tile for NS steps, branch-free: lane (col, g)
 // takes block 4 s + g of its row; blocks past I / 32 load the row's first
 // bytes (in bounds) and are zeroed where the MFMA consumes them.
@@ -577,17 +708,21 @@ __global__ __launch_bounds__(256, DN_WG_PER_CU(NS)) void down_decode_kernel(FfnA
 }
 
 // Single-row decode (T = 1: every touched expert holds exactly one pair, and
-// pair p belongs to the p-th touched expert): down and combine in one kernel.
-// One workgroup per 16 output columns.  The k intermediate rows are gathered
-// into LDS (requested first), wavefront w runs the down chains of slots w and
-// w + 4 (then w + 8 and w + 12 when k > 8) with their W2 rows in registers,
-// and the 16 columns are combined in slot order exactly as the combine
-// kernel does.
+// pair p belongs to the p-th touched expert): requant, down and combine in
+// one kernel.  One workgroup per 16 output columns.  The k fp32 SwiGLU rows
+// of the gate/up kernel are requested first, then each wavefront's W2 rows;
+// while those stream in, the workgroup requantizes the k rows (block-32 E4M3,
+// the routine every path uses) into LDS (workgroup 0 also writes the FP8
+// intermediate to the workspace).  Wavefront w runs the down chains of slots
+// w and w + 4 (then w + 8 and w + 12 when k > 8) with their W2 rows in
+// registers, and the 16 columns are combined in slot order exactly as the
+// combine kernel does.
 template <int NS>
-__global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
-                                                               const uint8_t* __restrict__ qsc_ws, int Tk) {
+__global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const float* __restrict__ abuf,
+                                                               uint8_t* __restrict__ qws,
+                                                               uint8_t* __restrict__ qsc_ws, int Tk) {
   constexpr int QP = NS * KSTEP + 16;                           // LDS pitch of an intermediate row
-  constexpr int QPT = (MAX_K * NS * 8 + 255) / 256;             // 16-byte chunks per thread
+  constexpr int RQP = 8;                                        // 16-byte SwiGLU chunks per thread in flight
   __shared__ int pslot[MAX_K];
   __shared__ float wslot[MAX_K];
   __shared__ float olds[MAX_K][16];
@@ -606,6 +741,23 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
   }
   WaveExperts we;
   wave_experts_load(a.offsets, a.E, we);
+  // the k SwiGLU rows (row j = slot j), requested before any weight, as
+  // 16-byte chunks: chunk ch = tid + 256 i of a round holds floats [4 c, 4 c +
+  // 4) of row j (ch = j I / 4 + c); eight consecutive lanes hold the eight
+  // chunks of one block of 32 (I / 4 is a multiple of 8)
+  const int cpr = I / 4, nch = k * cpr;
+  u32x4 av[RQP];
+  auto load_round = [&](int ch0) {
+    int jr = (ch0 + tid) / cpr, cr = (ch0 + tid) % cpr;
+#pragma unroll
+    for (int i = 0; i < RQP; ++i) {
+      const bool v = jr < k;                                    // whole 8-lane blocks in or out
+      av[i] = v ? *reinterpret_cast<const u32x4*>(abuf + (int64_t)jr * I + 4 * cr) : u32x4{0u, 0u, 0u, 0u};
+      cr += 256;                                                // this thread's next chunk
+      while (cr >= cpr) { cr -= cpr; ++jr; }
+    }
+  };
+  load_round(0);
   if (tid < k) {
     pslot[tid] = my_p;
     wslot[tid] = my_w;
@@ -619,21 +771,6 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
     const int p = j < k ? pslot[j] : -1;
     return p >= 0 && p < Tk;
   };
-  // the k intermediate rows and their scales, requested before any weight
-  const int q16 = I / 16;
-  u32x4 qv[QPT];
-  uint32_t sv[4];
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int idx = tid + 256 * i, j = idx / q16, c = idx % q16;
-    const bool v = j < k && slot_ok(j);
-    qv[i] = v ? ldg16(qws + (int64_t)pslot[j] * I + c * 16) : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i, j = idx / nb, b = idx % nb;
-    sv[i] = (j < k && slot_ok(j)) ? (uint32_t)qsc_ws[(int64_t)pslot[j] * nb + b] : 127u;
-  }
   auto load_pair = [&](int j0, bool (&ok)[2], u32x4 (&bw)[2][NS], uint32_t (&bs)[2][NS]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -673,15 +810,36 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
   u32x4 bwA[2][NS];
   uint32_t bsA[2][NS];
   load_pair(wave, okA, bwA, bsA);
+  // requant (block-32 E4M3 of each SwiGLU row) into LDS while the W2 rows stream in
+  auto requant_round = [&](int ch0) {
+    int jr = (ch0 + tid) / cpr, cr = (ch0 + tid) % cpr;
 #pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int idx = tid + 256 * i, j = idx / q16, c = idx % q16;
-    if (j < k) *reinterpret_cast<u32x4*>(&q1[j][c * 16]) = qv[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i, j = idx / nb, b = idx % nb;
-    if (j < k) s1[j][b] = (uint8_t)sv[i];
+    for (int i = 0; i < RQP; ++i) {
+      if (ch0 + i * 256 < nch) {                                // uniform over the workgroup's pass
+        const float v0 = __uint_as_float(av[i][0]), v1 = __uint_as_float(av[i][1]);
+        const float v2 = __uint_as_float(av[i][2]), v3 = __uint_as_float(av[i][3]);
+        const float m = fmaxf(fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)),
+                              fmaxf(__builtin_fabsf(v2), __builtin_fabsf(v3)));
+        const uint32_t sc = e8m0_code_for_amax(row8_max(m), 8);
+        const uint32_t d = requant2_e4m3(v0, v1, sc) | (requant2_e4m3(v2, v3, sc) << 16);
+        if (jr < k) {
+          const int b = cr / 8;
+          *reinterpret_cast<uint32_t*>(&q1[jr][4 * cr]) = d;
+          if ((cr & 7) == 0) s1[jr][b] = (uint8_t)sc;
+          if (blockIdx.x == 0 && slot_ok(jr)) {                 // the intermediate, for the workspace's readers
+            *reinterpret_cast<uint32_t*>(qws + (int64_t)pslot[jr] * I + 4 * cr) = d;
+            if ((cr & 7) == 0) qsc_ws[(int64_t)pslot[jr] * nb + b] = (uint8_t)sc;
+          }
+        }
+      }
+      cr += 256;
+      while (cr >= cpr) { cr -= cpr; ++jr; }
+    }
+  };
+  requant_round(0);
+  for (int ch0 = 256 * RQP; ch0 < nch; ch0 += 256 * RQP) {     // more than 256 * RQP chunks: further rounds
+    load_round(ch0);
+    requant_round(ch0);
   }
   lds_barrier();
   run_pair(wave, okA, bwA, bsA);
@@ -1209,7 +1367,8 @@ size_t ffn_ws_bytes(int T, int H, int E, int I, int k) {
   (void)E;
   size_t q, qs, o;
   ffn_ws_layout(T, H, I, k, &q, &qs, &o);
-  return o + align256((size_t)T * k * H * 4) + 256 + 256;      // + the work-queue counters + a scratch row (64 floats)
+  // o holds T*k rows of H floats (per-slot outputs) or, at T = 1, of I floats (the SwiGLU rows)
+  return o + align256((size_t)T * k * (H > I ? H : I) * 4) + 256 + 256;   // + work-queue counters + a scratch row
 }
 
 // Row pairs at or below which the decode kernels are chosen.
@@ -1239,10 +1398,9 @@ static inline void phase(int i, hipStream_t stream) {
 
 // gate/up of one row: the NS / EXACT variant for H = 128 hs
 template <int RP>
-static void launch_gu_one(int hs, dim3 g0, dim3 b0, size_t lds, hipStream_t stream, const FfnArgs& a, uint8_t* qws,
-                          uint8_t* qsc, float* h, int Tk, int R, const FusedRoute& fr) {
-#define MX_GU1(NS_, EX_) \
-  hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, true, RP>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R, fr)
+static void launch_gu1(int hs, dim3 grid, hipStream_t stream, const FfnArgs& a, float* abuf, float* h, int Tk,
+                       const FusedRoute& fr) {
+#define MX_GU1(NS_, EX_) hipLaunchKernelGGL((gu1_kernel<NS_, EX_, RP>), grid, dim3(64), 0, stream, a, abuf, h, Tk, fr)
   if (hs == 32) MX_GU1(32, true);
   else if (hs == 40) MX_GU1(40, true);
   else if (hs == 16) MX_GU1(16, true);
@@ -1267,8 +1425,9 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
   uint8_t* qws = base + oq;
   uint8_t* qsc = base + oqs;
   float* o = reinterpret_cast<float*>(base + oo);
-  int* queue = reinterpret_cast<int*>(base + oo + align256((size_t)Tk * a.H * 4));   // work-queue counters
-  float* junk = reinterpret_cast<float*>(base + oo + align256((size_t)Tk * a.H * 4) + 256);   // scratch row
+  const size_t obytes = align256((size_t)Tk * (a.H > a.I ? a.H : a.I) * 4);
+  int* queue = reinterpret_cast<int*>(base + oo + obytes);                 // work-queue counters
+  float* junk = reinterpret_cast<float*>(base + oo + obytes + 256);        // scratch row
   const int cus = num_cus();
   const int max_active = a.E < Tk ? a.E : Tk;
   phase(0, stream);
@@ -1283,9 +1442,12 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
 #define MX_GU(NS_, EX_, ONE_) \
   hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, ONE_, 0>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R, FusedRoute{})
     if (a.T == 1) {
-      if (!fr) launch_gu_one<0>(hs, g0, b0, lds, stream, a, qws, qsc, h, Tk, R, FusedRoute{});
-      else if (a.E <= 256) launch_gu_one<4>(hs, g0, b0, lds, stream, a, qws, qsc, h, Tk, R, *fr);
-      else launch_gu_one<16>(hs, g0, b0, lds, stream, a, qws, qsc, h, Tk, R, *fr);
+      // one wavefront per (pair, 8 intermediate columns); the SwiGLU rows go to the o region
+      const int items = a.k * (a.I / 8);
+      const dim3 g1(items < cus * 8 ? items : cus * 8);
+      if (!fr) launch_gu1<0>(hs, g1, stream, a, o, h, Tk, FusedRoute{});
+      else if (a.E <= 256) launch_gu1<4>(hs, g1, stream, a, o, h, Tk, *fr);
+      else launch_gu1<16>(hs, g1, stream, a, o, h, Tk, *fr);
     } else {
       if (hs == 32) MX_GU(32, true, false);
       else if (hs == 40) MX_GU(40, true, false);
@@ -1301,11 +1463,11 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     phase(1, stream);
     if (a.T == 1) {
       const dim3 g1(a.H / 16), b1(256);
-      if (is <= 2) hipLaunchKernelGGL(down_combine1_kernel<2>, g1, b1, 0, stream, a, qws, qsc, Tk);
-      else if (is <= 5) hipLaunchKernelGGL(down_combine1_kernel<5>, g1, b1, 0, stream, a, qws, qsc, Tk);
-      else if (is <= 8) hipLaunchKernelGGL(down_combine1_kernel<8>, g1, b1, 0, stream, a, qws, qsc, Tk);
-      else hipLaunchKernelGGL(down_combine1_kernel<16>, g1, b1, 0, stream, a, qws, qsc, Tk);
-      *variant = fr ? "layer1:gu_decode_topk+down_combine1" : "ffn:gu_decode+down_combine1";
+      if (is <= 2) hipLaunchKernelGGL(down_combine1_kernel<2>, g1, b1, 0, stream, a, o, qws, qsc, Tk);
+      else if (is <= 5) hipLaunchKernelGGL(down_combine1_kernel<5>, g1, b1, 0, stream, a, o, qws, qsc, Tk);
+      else if (is <= 8) hipLaunchKernelGGL(down_combine1_kernel<8>, g1, b1, 0, stream, a, o, qws, qsc, Tk);
+      else hipLaunchKernelGGL(down_combine1_kernel<16>, g1, b1, 0, stream, a, o, qws, qsc, Tk);
+      *variant = fr ? "layer1:gu1_decode_topk+down_combine1" : "ffn:gu1_decode+down_combine1";
       phase(2, stream);                                         // the down kernel also combines
       phase(3, stream);
       return hipGetLastError();

@@ -163,6 +163,15 @@ __device__ __forceinline__ float row16_max(float m) {
   return m;
 }
 
+// Maximum over each group of 8 lanes (lanes 8 r .. 8 r + 7), in registers:
+// quad butterflies, then the mirror within the half row.
+__device__ __forceinline__ float row8_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));   // quad [1,0,3,2]
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));   // quad [2,3,0,1]
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  return m;
+}
+
 // E4M3 codes of two elements of a block whose shared scale code is sc (the
 // requant of the intermediate), first element in bits 0..7, second in 8..15:
 // identical in every kernel that uses it.  The value is scaled by 2^(127 - sc)
