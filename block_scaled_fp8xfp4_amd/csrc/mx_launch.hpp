@@ -60,6 +60,12 @@ size_t router_logits_ws_bytes(int T, int H, int E);
 hipError_t launch_router_logits(const uint16_t* h, int T, int H, const uint16_t* wg, int E, float* logits, void* ws,
                                 hipStream_t stream, const char** variant);
 
+// shared expert of one row (I <= 1024): gate/up as canonical parts into pbuf
+// [H / 1024 rounded up][2I], then the down kernel with the part sum, SwiGLU and
+// requant in its prologue; h, q, q_sc receive the intermediate (diagnostics)
+hipError_t launch_shared_down1(const uint8_t* x, const uint8_t* x_sc, int H, const uint8_t* w13,
+                               const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,
+                               float* h, uint8_t* q, uint8_t* q_sc, float* pbuf, hipStream_t stream);
 size_t shared_ws_bytes(int T, int H, int I);
 hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H, const uint8_t* w13,
                                 const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,

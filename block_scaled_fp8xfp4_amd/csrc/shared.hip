@@ -38,11 +38,15 @@ __global__ __launch_bounds__(256) void swiglu_requant_kernel(const float* __rest
   if ((c & 31) == 0) q_sc[t * (I / 32) + c / 32] = (uint8_t)sc;
 }
 
+static size_t a256(size_t b) { return (b + 255) / 256 * 256; }
+
+// one row with I <= 1024 takes the two-launch path (gate/up parts + down with the requant prologue)
+static bool one_row_path(int T, int I) { return T == 1 && I <= KPART; }
+
+// [h: T x 2I fp32][q: T x I][q_sc: T x I/32][parts: one row's gate/up parts, one-row path only]
 size_t shared_ws_bytes(int T, int H, int I) {
-  (void)H;
-  const size_t hb = ((size_t)T * 2 * I * 4 + 255) / 256 * 256;
-  const size_t qb = ((size_t)T * I + 255) / 256 * 256;
-  return hb + qb + ((size_t)T * (I / 32) + 255) / 256 * 256;
+  const size_t base = a256((size_t)T * 2 * I * 4) + a256((size_t)T * I) + a256((size_t)T * (I / 32));
+  return base + (one_row_path(T, I) ? a256((size_t)((H + KPART - 1) / KPART) * 2 * I * 4) : 0);
 }
 
 hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H, const uint8_t* w13,
@@ -50,9 +54,14 @@ hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, in
                                 void* ws, hipStream_t stream, const char** variant) {
   uint8_t* base = static_cast<uint8_t*>(ws);
   float* h = reinterpret_cast<float*>(base);
-  uint8_t* q = base + ((size_t)T * 2 * I * 4 + 255) / 256 * 256;
-  uint8_t* q_sc = q + ((size_t)T * I + 255) / 256 * 256;
+  uint8_t* q = base + a256((size_t)T * 2 * I * 4);
+  uint8_t* q_sc = q + a256((size_t)T * I);
   const char* v = "";
+  if (one_row_path(T, I)) {
+    float* pbuf = reinterpret_cast<float*>(q_sc + a256((size_t)T * (I / 32)));
+    *variant = "shared:decode1_gemm_parts+down_requant";
+    return launch_shared_down1(x, x_sc, H, w13, w13_sc, w2, w2_sc, I, y, h, q, q_sc, pbuf, stream);
+  }
   hipError_t e = launch_block_gemm(x, x_sc, w13, w13_sc, T, 2 * I, H, h, false, stream, &v);
   if (e != hipSuccess) return e;
   const int64_t pairs = (int64_t)T * (I / 2);
