@@ -869,8 +869,17 @@ constexpr int GU_STAGES = 2;                      // LDS stages per workgroup
 constexpr int GU_NT = 2 * GU_BM;                  // threads: one wavefront per 64 rows x 64 columns
 constexpr int GU_WG_PER_CU = GU_BM == 128 ? 4 / GU_STAGES : 1;   // workgroups resident per CU (LDS-bound)
 
-__device__ __forceinline__ int a_phys(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }   // 16-byte chunk
-__device__ __forceinline__ int b_phys(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+// LDS slot (16-byte chunk) of chunk c of tile row r.  A 16-byte LDS read is
+// served eight lanes at a time, and the eight lanes of an operand read are
+// eight consecutive rows at one chunk: the swizzles put those eight chunks
+// at eight distinct 16-byte positions of a 128-byte bank sweep.  Activation
+// rows are 128 bytes (8 chunks): position c ^ (r mod 8).  Weight rows are 64
+// bytes (4 chunks, two rows per sweep): position 4 (r mod 2) + (c ^ (r / 2
+// mod 4)).
+__device__ __forceinline__ int a_swz(int r) { return r & 7; }
+__device__ __forceinline__ int b_swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int a_phys(int r, int c) { return r * 8 + (c ^ a_swz(r)); }
+__device__ __forceinline__ int b_phys(int r, int c) { return r * 4 + (c ^ b_swz(r)); }
 
 struct GuStage {
   u32x4 a[GU_BM * 8];                             // [row][8 chunks] swizzled
@@ -946,14 +955,14 @@ __global__ __launch_bounds__(GU_NT, GU_WG_PER_CU) void gu_prefill_kernel(FfnArgs
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int p = j * GU_NT + tid;
-      const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+      const int r = p >> 3, c = (p & 7) ^ a_swz(r);
       const int t = tok[r];
       aoff[j] = (uint32_t)(t < 0 ? 0 : t) * (uint32_t)H + c * 16;
     }
 #pragma unroll
     for (int j = 0; j < NBD; ++j) {
       const int p = j * GU_NT + tid;
-      const int rb = p >> 2, cb = (p & 3) ^ ((rb >> 2) & 3);
+      const int rb = p >> 2, cb = (p & 3) ^ b_swz(rb);
       const int icol = rb & 127;
       const int r13 = (rb < 128 ? 0 : I) + c0 + (icol < ncols ? icol : 0);
       boff[j] = (uint32_t)r13 * (uint32_t)(H / 2) + cb * 16;
