@@ -233,8 +233,8 @@ constexpr int DEC_SPITCH = DEC_MAX_STEPS + 1;     // LDS pitch (dwords) of the s
 // is requested before the weights, so waiting for it never waits for them
 // (vector-memory counters drain in issue order).
 
-// Gate/up + SwiGLU + requant: one workgroup per (expert, block of 32
-// intermediate columns), i.e. 64 W13 rows: wavefronts 0, 1 take gate rows
+// Gate/up + SwiGLU + requant (T > 1): one workgroup per (expert, block of
+// 32 intermediate columns), i.e. 64 W13 rows: wavefronts 0, 1 take gate rows
 // 32 b + [0, 16) and + [16, 32), wavefronts 2, 3 the matching up rows.  Per
 // pass of at most R = min(8, T) rows of the expert, the activation rows are
 // gathered into LDS; each wavefront's 16 weight rows (whole K, NS >= H / 128
@@ -242,24 +242,12 @@ constexpr int DEC_SPITCH = DEC_MAX_STEPS + 1;     // LDS pitch (dwords) of the s
 // in LDS (16 rows x H / 32 bytes, one coalesced span).  The four 16 x 16
 // results meet in LDS, where one pass turns each row's 32 gate/up pairs into
 // one requantized block.  Writes q, its scale, and the fp32 h = [gate | up]
-// of every pair when h is non-null (diagnostics).  ONE (T = 1): every pair
-// is row 0, whose activations are
-// requested before the route is read.  EXACT: H = 128 NS, so every address
-// offset is a constant.
-//
-// RPER > 0 (single row, fused with the gate): every wavefront ranks the
-// row's logits itself (the wavefront top-k with RPER logits per lane)
-// instead of reading a route.  Item i takes the expert of slot i / nb
-// (descending logit): the wavefront runs only the ranking rounds up to that
-// slot before issuing the expert's weight loads, and the remaining rounds
-// while they are in flight; the pair's bucket position, the rank of its
-// expert among the k in ascending order, is known by then.  Workgroup 0's
-// first wavefront writes the route outputs exactly as the single-row route
-// kernel does, for the down kernel and the caller.
-template <int NS, bool EXACT, bool ONE, int RPER>
+// of every pair when h is non-null (diagnostics).  EXACT: H = 128 NS, so
+// every address offset is a constant.
+template <int NS, bool EXACT>
 __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* __restrict__ qws,
                                                            uint8_t* __restrict__ qsc_ws, float* __restrict__ h,
-                                                           int Tk, int R, FusedRoute fr) {
+                                                           int Tk, int R) {
   __shared__ int tok[DEC_ROWS];
   __shared__ float hb[16 * DEC_HPITCH];
   __shared__ uint32_t bsc[4][16 * DEC_SPITCH];                 // per wavefront: [row][step] scale dwords
@@ -273,73 +261,58 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
   uint32_t* xslds = reinterpret_cast<uint32_t*>(dyn_lds + (size_t)R * pitch);   // [R][nsteps]
   u32x4 xv[DEC_ROWS];
   uint32_t xsv = 0x7F7F7F7Fu;
-  // the parts of the rows' activations and scales past what one thread per
-  // 16-byte chunk / scale dword covers (H > 4096): staged directly
-  auto stage_rest = [&](int nr) {
-    for (int idx = tid; idx < nr * chunks; idx += 256) {
-      const int r = idx / chunks, c = idx % chunks;
-      if (c < 256) continue;
-      const int t = ONE ? 0 : tok[r];
-      *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + c * 16) =
-          t >= 0 ? ldg16(a.x + (int64_t)t * H + c * 16) : u32x4{0u, 0u, 0u, 0u};
+  // the pass's rows (tok[0, nr)): their activations and scales requested into
+  // registers (one thread per 16-byte chunk / scale dword), then staged in
+  // LDS; the parts past what one thread covers (H > 4096) are staged directly
+  auto request_rows = [&](int nr) {
+#pragma unroll
+    for (int r = 0; r < DEC_ROWS; ++r) {
+      const int t = r < nr ? tok[r] : -1;
+      xv[r] = (t >= 0 && tid < chunks) ? ldg16(a.x + (int64_t)t * H + tid * 16) : u32x4{0u, 0u, 0u, 0u};
     }
-    for (int idx = tid + 256; idx < nr * nsteps; idx += 256) {
-      const int r = idx / nsteps, c = idx % nsteps;
-      const int t = ONE ? 0 : tok[r];
-      xslds[idx] = t >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)t * (H / 32))[c] : 0x7F7F7F7Fu;
+    const int rs = tid / nsteps, ss = tid % nsteps;
+    const int ts = (tid < nr * nsteps) ? tok[rs] : -1;
+    xsv = ts >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)ts * (H / 32))[ss] : 0x7F7F7F7Fu;
+  };
+  auto stage_rows = [&](int nr) {
+#pragma unroll
+    for (int r = 0; r < DEC_ROWS; ++r)
+      if (r < nr && tid < chunks) *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + tid * 16) = xv[r];
+    if (tid < nr * nsteps) xslds[tid] = xsv;
+    if (chunks > 256 || nr * nsteps > 256) {                    // H > 4096
+      for (int idx = tid; idx < nr * chunks; idx += 256) {
+        const int r = idx / chunks, c = idx % chunks;
+        if (c < 256) continue;
+        const int t = tok[r];
+        *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + c * 16) =
+            t >= 0 ? ldg16(a.x + (int64_t)t * H + c * 16) : u32x4{0u, 0u, 0u, 0u};
+      }
+      for (int idx = tid + 256; idx < nr * nsteps; idx += 256) {
+        const int t = tok[idx / nsteps];
+        xslds[idx] = t >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)t * (H / 32))[idx % nsteps]
+                            : 0x7F7F7F7Fu;
+      }
     }
   };
-  if (ONE) {
-    xv[0] = tid < chunks ? ldg16(a.x + tid * 16) : u32x4{0u, 0u, 0u, 0u};
-    if (tid < nsteps) xsv = reinterpret_cast<const uint32_t*>(a.x_sc)[tid];
-  }
+  auto gather_tok = [&](int p, int nr) {                       // tokens of bucket positions [p, p + nr)
+    if (tid < nr) {
+      const int pr = a.perm[p + tid];
+      tok[tid] = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
+    }
+  };
   WaveExperts we;                                               // every wavefront reads the expert list itself
-  constexpr int RP = RPER > 0 ? RPER : 1;
-  TopkState<RP> st;
-  bool live = true;
-  int nitems;
-  if (RPER > 0) {
-    const float sv = fr.survival != nullptr ? fr.survival[0] : 1.0f;   // in flight with the logits
-    topk_begin<RP>(st, fr.logits, a.E);
-    live = fr.survival == nullptr || !(sv < fr.skip_below);
-    nitems = live ? a.k * nb : 0;
-  } else {
-    wave_experts_load(a.offsets, a.E, we);
-    nitems = wave_experts_scan(a.E, we) * nb;
-  }
+  wave_experts_load(a.offsets, a.E, we);
+  const int nitems = wave_experts_scan(a.E, we) * nb;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int blk = item % nb;
     int e, p0, cnt;
-    if (RPER > 0) {                                             // the expert of slot item / nb
-      const int j = item / nb;
-      topk_rounds<RP>(st, j + 1);
-      e = __builtin_amdgcn_readlane(st.idx, j);
-      p0 = 0;                                                   // its bucket position: after the weight loads
-      cnt = 1;
-    } else {
-      wave_tile(we, a.E, item / nb, e, p0, cnt);
-    }
+    wave_tile(we, a.E, item / nb, e, p0, cnt);
     if (p0 < 0 || p0 + cnt > Tk) cnt = 0;                       // malformed route: skip
     const int n0 = min(R, cnt);
     lds_barrier();                                              // the previous item's LDS reads are done
-    if (!ONE) {
-      if (tid < n0) {
-        const int pr = a.perm[p0 + tid];
-        tok[tid] = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
-      }
-      lds_barrier();
-      // first pass's rows: requested before the weights
-#pragma unroll
-      for (int r = 0; r < DEC_ROWS; ++r) {
-        const int t = r < n0 ? tok[r] : -1;
-        xv[r] = (t >= 0 && tid < chunks) ? ldg16(a.x + (int64_t)t * H + tid * 16) : u32x4{0u, 0u, 0u, 0u};
-      }
-      {
-        const int r = tid / nsteps, s = tid % nsteps;
-        const int t = (tid < n0 * nsteps) ? tok[r] : -1;
-        xsv = t >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)t * (H / 32))[s] : 0x7F7F7F7Fu;
-      }
-    }
+    gather_tok(p0, n0);
+    lds_barrier();
+    request_rows(n0);                                           // the first pass's rows: before the weights
     // this wavefront's 16 rows of scales: one contiguous span of 16 * nsteps dwords
     const int64_t wrow0 = (int64_t)e * 2 * I + (wave < 2 ? 0 : I) + blk * 32 + (wave & 1) * 16;
     const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.w13_sc + wrow0 * (H / 32));
@@ -354,26 +327,13 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
     u32x4 bw[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (EXACT || s < nsteps ? s : nsteps - 1) * 64);
-    if (RPER > 0) {                                             // the other slots, while the weights stream in
-      topk_rounds<RP>(st, a.k);
-      for (int i = 0; i < a.k; ++i) p0 += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
-    }
     // stage what the first pass needs (its loads were issued before the weights)
 #pragma unroll
     for (int i = 0; i < NBSV; ++i) {
       const int idx = lane + 64 * i;
       if (idx < 16 * nsteps) bsc[wave][(idx / nsteps) * spitch + idx % nsteps] = bsv[i];
     }
-    if (ONE) {
-      if (tid < chunks) *reinterpret_cast<u32x4*>(xlds + tid * 16) = xv[0];
-      if (tid < nsteps) xslds[tid] = xsv;
-    } else {
-#pragma unroll
-      for (int r = 0; r < DEC_ROWS; ++r)
-        if (r < n0 && tid < chunks) *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + tid * 16) = xv[r];
-      if (tid < n0 * nsteps) xslds[tid] = xsv;
-    }
-    if (chunks > 256 || (ONE ? 1 : n0) * nsteps > 256) stage_rest(ONE ? 1 : n0);   // H > 4096
+    stage_rows(n0);
     lds_barrier();
     const uint32_t* bsrow = &bsc[wave][col * spitch];
     // One pass over rows [r0, r0 + nrows) whose activations are in LDS.  Every
@@ -418,52 +378,17 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
         }
       }
     };
-    if (ONE) {
-      if (cnt > 0) run_pass(0, 1);                              // T = 1: at most one pair per expert
-      continue;
-    }
     for (int r0 = 0; r0 < cnt; r0 += R) {
       const int nrows = min(R, cnt - r0);
       if (r0 > 0) {                                             // later passes: gather their rows
         lds_barrier();
-        if (tid < nrows) {
-          const int pr = a.perm[p0 + r0 + tid];
-          tok[tid] = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
-        }
+        gather_tok(p0 + r0, nrows);
         lds_barrier();
-#pragma unroll
-        for (int r = 0; r < DEC_ROWS; ++r) {
-          const int t = r < nrows ? tok[r] : -1;
-          xv[r] = (t >= 0 && tid < chunks) ? ldg16(a.x + (int64_t)t * H + tid * 16) : u32x4{0u, 0u, 0u, 0u};
-        }
-        const int rs = tid / nsteps, ss = tid % nsteps;
-        const int ts = (tid < nrows * nsteps) ? tok[rs] : -1;
-        xsv = ts >= 0 ? reinterpret_cast<const uint32_t*>(a.x_sc + (int64_t)ts * (H / 32))[ss] : 0x7F7F7F7Fu;
-#pragma unroll
-        for (int r = 0; r < DEC_ROWS; ++r)
-          if (r < nrows && tid < chunks) *reinterpret_cast<u32x4*>(xlds + (size_t)r * pitch + tid * 16) = xv[r];
-        if (tid < nrows * nsteps) xslds[tid] = xsv;
-        if (chunks > 256 || nrows * nsteps > 256) stage_rest(nrows);   // H > 4096
+        request_rows(nrows);
+        stage_rows(nrows);
         lds_barrier();
       }
       run_pass(r0, nrows);
-    }
-  }
-  if (RPER > 0 && blockIdx.x == 0 && wave == 0) {              // the route outputs, as the single-row route kernel
-    topk_rounds<RP>(st, a.k);
-    int rrank = 0;                                              // lane j: position of slot j's expert in ascending order
-    for (int i = 0; i < a.k; ++i) rrank += __builtin_amdgcn_readlane(st.idx, i) < st.idx ? 1 : 0;
-    const float wt = slot_weight(st.val, a.k);
-    if (lane < a.k) {
-      fr.ids[lane] = st.idx;
-      fr.w[lane] = wt;
-      fr.slot_pos[lane] = live ? rrank : -1;
-      fr.perm[live ? rrank : lane] = live ? lane : -1;
-    }
-    for (int e = lane; e <= a.E; e += 64) {
-      int below = 0;
-      for (int i = 0; i < a.k; ++i) below += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
-      fr.offsets[e] = live ? below : 0;
     }
   }
 }
@@ -479,9 +404,15 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
 // wavefronts).
 // One-wavefront workgroups spread the 18.9 MB of a decode step's gate/up
 // weights over every CU, whose outstanding-miss capacity, not HBM, bounds a
-// stream this short.  RPER > 0: the gate runs here, as in gu_decode_kernel
-// (item i takes the expert of slot i / (I / 8); the ranking rounds past that
-// slot run while its weights are in flight); otherwise the pairs come from
+// stream this short.  RPER > 0 (single row, fused with the gate): every
+// wavefront ranks the row's logits itself (the wavefront top-k with RPER
+// logits per lane) instead of reading a route; item i takes the expert of
+// slot i / (I / 8) (descending logit), the wavefront runs only the ranking
+// rounds up to that slot before issuing the expert's weight loads and the
+// remaining rounds while they are in flight, when the pair's bucket position
+// (the rank of its expert among the k in ascending order) is known.
+// Workgroup 0 writes the route outputs exactly as the single-row route kernel
+// does, for the down kernel and the caller.  RPER = 0: the pairs come from
 // the route's offsets.
 template <int NS, bool EXACT, int RPER>
 __global__ __launch_bounds__(64) void gu1_kernel(FfnArgs a, float* __restrict__ abuf, float* __restrict__ h, int Tk,
@@ -1122,7 +1053,6 @@ constexpr int DN_QPITCH = 5 * KSTEP + 16;         // LDS pitch of an intermediat
 constexpr int DN_TPITCH = 36;                     // transpose rows: 32 floats + 4 (bank spread)
 constexpr int DN_W2_DMA = 10;                     // W2 row DMAs per wavefront per item (256 rows x <= 20 chunks)
 constexpr int DN_W2S_DMA = 3;                     // W2 scale dword DMAs per wavefront per item
-constexpr int DN_TILE_DMA = DN_ROWS_T / DN_WAVES + 1;   // per tile: 4 rows + 1 scale dword DMA
 constexpr int DN_TILE_ST = 4;                     // per tile: stores (2 subtiles x 2 halves)
 struct DnLds {
   uint8_t q[2][DN_ROWS_T][DN_QPITCH];             // intermediate rows, two buffers
@@ -1448,8 +1378,8 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     const int hs = a.H / KSTEP, is = (a.I + KSTEP - 1) / KSTEP;
     if (hs > DEC_MAX_STEPS || is > DOWN_MAX_STEPS) return hipErrorInvalidValue;   // the kernels' register arrays hold every step
     const dim3 g0(gu_grid), b0(256);
-#define MX_GU(NS_, EX_, ONE_) \
-  hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_, ONE_, 0>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R, FusedRoute{})
+#define MX_GU(NS_, EX_) \
+  hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R)
     if (a.T == 1) {
       // one wavefront per (pair, 8 intermediate columns); the SwiGLU rows go to the o region
       const int items = a.k * (a.I / 8);
@@ -1458,15 +1388,15 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       else if (a.E <= 256) launch_gu1<4>(hs, g1, stream, a, o, h, Tk, *fr);
       else launch_gu1<16>(hs, g1, stream, a, o, h, Tk, *fr);
     } else {
-      if (hs == 32) MX_GU(32, true, false);
-      else if (hs == 40) MX_GU(40, true, false);
-      else if (hs == 16) MX_GU(16, true, false);
-      else if (hs == 8) MX_GU(8, true, false);
-      else if (hs <= 4) MX_GU(4, false, false);
-      else if (hs <= 8) MX_GU(8, false, false);
-      else if (hs <= 16) MX_GU(16, false, false);
-      else if (hs <= 32) MX_GU(32, false, false);
-      else MX_GU(40, false, false);
+      if (hs == 32) MX_GU(32, true);
+      else if (hs == 40) MX_GU(40, true);
+      else if (hs == 16) MX_GU(16, true);
+      else if (hs == 8) MX_GU(8, true);
+      else if (hs <= 4) MX_GU(4, false);
+      else if (hs <= 8) MX_GU(8, false);
+      else if (hs <= 16) MX_GU(16, false);
+      else if (hs <= 32) MX_GU(32, false);
+      else MX_GU(40, false);
     }
 #undef MX_GU
     phase(1, stream);

@@ -145,7 +145,6 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint8_t* __restr
 // block's 8 activation panels and 8 weight panels are shared in that XCD's
 // L2 while its 64 workgroups move through K together.
 constexpr int GP_BM = 128, GP_BN = 128;
-constexpr int GP_DMA = 9;                         // per wavefront per step: 4 A + 4 B chunk DMAs + 1 scale DMA
 __device__ __forceinline__ int gp_phys(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }   // 16-byte chunk
 struct GpStage {
   u32x4 a[GP_BM * 8];                             // [row][8 chunks] swizzled
