@@ -237,7 +237,7 @@ def main():
         ffn_bytes = touched * EXPERT_BYTES(H, I) + T * (H + H // 32) + T * H * 4 + (T * E * 4 if fused else 0)
         achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
         if fused:
-            ffn_variant = mxmoe.last_variant() if False else "layer1:gu1_decode_topk+down_combine1"
+            ffn_variant = mxmoe.last_variant()          # the last host call was moe_layer_decode1
         if cfg.streams:
             # the same step with router-live verification rows: rows below the
             # confidence threshold take their anchor's experts instead of skipping

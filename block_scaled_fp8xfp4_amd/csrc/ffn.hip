@@ -15,7 +15,7 @@
 // they give the same bits; they differ only in how rows and weights reach the
 // matrix cores.
 //
-// Decode path (few rows per expert, weight streaming):
+// Decode path (few rows per expert, weight streaming), T > 1:
 //   gu_decode_kernel    one workgroup per (expert, block of 32 intermediate
 //                       columns) = 64 W13 rows, 16 per wavefront: the whole K
 //                       of the weight rows is loaded into registers at once,
@@ -24,9 +24,16 @@
 //                       intermediate block in the same workgroup.
 //   down_decode_kernel  one workgroup per (expert, 128 W2 rows); intermediate
 //                       rows from the workspace through LDS; writes o.
-//   down_combine1_kernel  one row (T = 1): one workgroup per 16 output
-//                       columns runs the down chains of all k slots and the
-//                       combine, so o never leaves the chip.
+// One row (T = 1):
+//   gu1_kernel          one wavefront per (slot, 8 intermediate columns): the
+//                       MFMA's 16 output columns are 8 gate rows and the
+//                       matching 8 up rows, so each tile yields 8 SwiGLU
+//                       values (fp32, in slot order in the workspace); may
+//                       rank the row's logits itself (the fused gate).
+//   down_combine1_kernel  one workgroup per 16 output columns: requantizes the
+//                       k SwiGLU rows to FP8 blocks in LDS while its W2 rows
+//                       stream in, runs the down chains of all k slots and
+//                       the combine, so o never leaves the chip.
 // Prefill path (hundreds of rows per expert, matrix-core bound):
 //   gu_prefill_kernel   expert tile of up to 128 rows x 128 intermediate
 //                       columns (256 W13 rows) per workgroup, 2 x 2

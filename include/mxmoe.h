@@ -182,7 +182,9 @@ mx_status moe_route(const float* logits, int T, int E, int k,
  *     bytes (256-byte aligned).  Its layout is documented for diagnostics
  *     and filled in by moe_ws_layout(): the FP8 intermediate q [T*k][I] and
  *     its scales SC [T*k][I/32] (row p = bucket position, written by every
- *     path) and the fp32 per-slot outputs o [T*k][H] (T > 1).
+ *     path) and the o region: the fp32 per-slot outputs o [T*k][H] when
+ *     T > 1; for one row (T = 1) its first k*I floats hold the SwiGLU rows
+ *     a [k][I] in slot order, which the down kernel requantizes.
  */
 size_t    moe_expert_ffn_workspace_bytes(int T, int H, int E, int I, int k);
 mx_status moe_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_o);
