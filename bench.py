@@ -74,7 +74,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="decode line without the verification-batch object")
+    ap.add_argument("--no-layer-shared", action="store_true",
+                    help="decode line without the routed + shared expert layer object")
     ap.add_argument("--graph", action="store_true", help="replay one HIP graph per step instead of eager launches")
+    ap.add_argument("--graph-steps", type=int, default=1,
+                    help="with --graph: decode steps captured per graph (a multi-layer decode graph)")
     ap.add_argument("--unfused", action="store_true",
                     help="decode step at T=1: moe_route + moe_expert_ffn instead of moe_layer_decode1")
     ap.add_argument("--prefetch", action="store_true",
@@ -187,16 +191,25 @@ def main():
         if not args.graph:
             run_step = step
         else:
-            # one HIP graph per step (and weight copy), as a serving loop
-            # replays its decode step; the library allocates and syncs nothing
+            # HIP graphs of G consecutive steps (each on its own weight copy),
+            # as a serving loop replays its decode step (G > 1: several layers
+            # in one graph); the library allocates and syncs nothing
+            G = max(1, args.graph_steps)
+            if args.steps % G or args.warmup % G:
+                sys.exit("--steps and --warmup must be multiples of --graph-steps")
+            ng = max(1, R // G)
             graphs = []
-            for i in range(R):
+            for gi in range(ng):
                 gr = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(gr):
-                    step(i)
+                    for u in range(G):
+                        step(gi * G + u)
                 graphs.append(gr)
             torch.cuda.synchronize()
-            run_step = lambda i: graphs[i % R].replay()
+
+            def run_step(i):
+                if i % G == 0:
+                    graphs[(i // G) % ng].replay()
         for i in range(args.warmup):
             run_step(i)
         torch.cuda.synchronize()
@@ -288,12 +301,65 @@ def main():
                        "touched_experts": touched, "experts_of_all_rows": len(all_ids),
                        "weight_bytes_skipped": (len(all_ids) - touched) * EXPERT_BYTES(H, I),
                        "bytes_per_step": step_bytes, "weight_copies": R,
-                       "launch": "hip_graph_per_step" if args.graph else "eager", "step_calls": step_variant,
+                       "launch": (f"hip_graph_{args.graph_steps}_steps" if args.graph else "eager"), "step_calls": step_variant,
                        "prefetch": bool(args.prefetch)},
         }
         if cfg.streams:
             out["router_live"] = live_obj
+        if fused and not args.graph and not args.no_layer_shared:
+            out["layer_with_shared"] = run_layer_with_shared(cfg, xq, xsc, logits, surv, copies, route, ffn,
+                                                             ffn_bytes)
         return inp, touched, out
+
+    def run_layer_with_shared(cfg, xq, xsc, logits, surv, copies, route, ffn, routed_bytes):
+        """The row's whole MoE layer, routed + shared experts: moe_layer_decode1_shared
+        (two launches) against moe_layer_decode1 + moe_shared_expert (four), each
+        over the same rotated routed weight copies and as many shared copies."""
+        H, E, k, I = cfg.H, cfg.E, cfg.k, cfg.I
+        w13, w2 = synth.shared_expert_weights(cfg)
+        S = quantize(torch.from_numpy(w13).to(dev), mxmoe.MX_FMT_E4M3) + \
+            quantize(torch.from_numpy(w2).to(dev), mxmoe.MX_FMT_E4M3)
+        sbytes = sum(t.numel() for t in S)
+        R = len(copies)
+        scopies = [S] + [tuple(t.clone() for t in S) for _ in range(R - 1)]
+        ys = torch.empty((1, H), dtype=torch.float32, device=dev)
+        ws_s = torch.empty(mxmoe.moe_shared_expert_workspace_bytes(1, H, I), dtype=torch.uint8, device=dev)
+        ws_f = torch.empty(mxmoe.moe_layer_decode1_shared_workspace_bytes(H, E, I, k, I), dtype=torch.uint8,
+                           device=dev)
+        r = route
+
+        def separate(i):
+            mxmoe.moe_layer_decode1(logits, k, surv, 0.2, xq, xsc, *copies[i % R], E, I, r.ids, r.w, r.offsets,
+                                    r.perm, r.slot_pos, ffn.y, ffn.ws)
+            mxmoe.moe_shared_expert(xq, xsc, *scopies[i % R], ys, ws_s)
+
+        def fused_call(i):
+            mxmoe.moe_layer_decode1_shared(logits, k, surv, 0.2, xq, xsc, *copies[i % R], E, I, *scopies[i % R],
+                                           r.ids, r.w, r.offsets, r.perm, r.slot_pos, ffn.y, ys, ws_f)
+
+        def timed(fn):
+            for i in range(R):
+                fn(i)
+            torch.cuda.synchronize()
+            reps = max(1, args.steps // R)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                for i in range(R):
+                    fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / (reps * R)
+
+        sep_ms = timed(separate)
+        fus_ms = timed(fused_call)
+        variant = mxmoe.last_variant()
+        nbytes = routed_bytes + sbytes + H * 4                 # + the shared weights and y_shared
+        return {"shared_I": I, "shared_weight_bytes": sbytes, "bytes": nbytes, "ms": round(fus_ms, 5),
+                "gbs": round(nbytes / (fus_ms * 1e-3) / 1e9, 2),
+                "pct_hbm_peak": round(100 * nbytes / (fus_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "separate_calls_ms": round(sep_ms, 5), "variant": variant,
+                "separate_calls": "moe_layer_decode1 + moe_shared_expert"}
 
     # ------------------------------------------------------------ dense FP8 GEMM at decode sizes (M = 1, 16)
     def run_dense_decode(steps, warmup):

@@ -246,6 +246,46 @@ mx_status moe_layer_decode1(const float* logits, int E, int k, const float* surv
   return from_hip(e);
 }
 
+static size_t layer1_routed_ws(int H, int E, int I, int k) { return (mx::ffn_ws_bytes(1, H, E, I, k) + 255) / 256 * 256; }
+
+size_t moe_layer_decode1_shared_workspace_bytes(int H, int E, int I, int k, int Is) {
+  if (H < 128 || E < 1 || k < 1 || k > E || I < 32 || Is < 32 || H % 32 || I % 32 || Is % 32) return 0;
+  return layer1_routed_ws(H, E, I, k) + mx::shared_ws_bytes(1, H, Is);
+}
+
+mx_status moe_layer_decode1_shared(const float* logits, int E, int k, const float* survival, float skip_below,
+                                   const uint8_t* x, const uint8_t* x_sc, int H, const uint8_t* w13,
+                                   const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I,
+                                   const uint8_t* sw13, const uint8_t* sw13_sc, const uint8_t* sw2,
+                                   const uint8_t* sw2_sc, int Is, int32_t* topk_ids, float* topk_w,
+                                   int32_t* expert_offsets, int32_t* perm, int32_t* slot_pos, float* y,
+                                   float* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  if (E < 1 || E > mx::MAX_E || k < 1 || k > E || k > mx::MAX_K || H < 128 || I < 32 || Is < 32) return MX_EINVAL;
+  if (H % 32 != 0 || I % 32 != 0 || Is % 32 != 0) return MX_EINVAL;
+  if (H % 128 != 0 || H > 128 * 8 * mx::MAX_PARTS || I > mx::MAX_I || mx::ffn_resolve_path(1, k, H, I) != 1 ||
+      Is > mx::KPART_MAX_SHARED1)
+    return MX_EUNSUPPORTED;
+  if (!logits || !x || !x_sc || !w13 || !w13_sc || !w2 || !w2_sc || !sw13 || !sw13_sc || !sw2 || !sw2_sc ||
+      !topk_ids || !topk_w || !expert_offsets || !perm || !slot_pos || !y || !y_shared)
+    return MX_EINVAL;
+  if (!aligned(logits, 4) || !aligned(survival, 4) || !aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
+      !aligned(y, 16) || !aligned(x_sc, 4) || !aligned(w13_sc, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      !aligned(expert_offsets, 4) || !aligned(perm, 4) || !aligned(slot_pos, 4) || !aligned(sw13, 16) ||
+      !aligned(sw2, 16) || !aligned(sw13_sc, 4) || !aligned(sw2_sc, 4) || !aligned(y_shared, 4))
+    return MX_EINVAL;
+  const size_t rws = layer1_routed_ws(H, E, I, k);
+  if (!ws || ws_bytes < rws + mx::shared_ws_bytes(1, H, Is) || !diag_h_fits(k, I)) return MX_EWORKSPACE;
+  if (!aligned(ws, 256)) return MX_EINVAL;
+  const mx::FfnArgs a{x, x_sc, 1, H, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y};
+  const mx::FusedRoute fr{logits, survival, skip_below, topk_ids, topk_w, expert_offsets, perm, slot_pos};
+  const mx::Shared1Args sh =
+      mx::shared1_args(x, x_sc, H, sw13, sw13_sc, sw2, sw2_sc, Is, y_shared, static_cast<uint8_t*>(ws) + rws);
+  const char* v = "";
+  const hipError_t e = mx::launch_ffn(a, ws, 1, static_cast<hipStream_t>(stream), &v, &fr, g_diag_h, &sh);
+  if (e == hipSuccess) g_variant = v;
+  return from_hip(e);
+}
+
 mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc, const uint8_t* w, const uint8_t* w_sc, int M, int N,
                          int K, void* y, int y_dtype, void* stream) {
   if (!a || !a_sc || !w || !w_sc || !y) return MX_EINVAL;

@@ -52,6 +52,7 @@
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 #include "route_device.hpp"
+#include "shared1_device.hpp"
 
 namespace mx {
 
@@ -421,9 +422,14 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
 // Workgroup 0 writes the route outputs exactly as the single-row route kernel
 // does, for the down kernel and the caller.  RPER = 0: the pairs come from
 // the route's offsets.
-template <int NS, bool EXACT, int RPER>
+template <int NS, bool EXACT, int RPER, bool SH>
 __global__ __launch_bounds__(64) void gu1_kernel(FfnArgs a, float* __restrict__ abuf, float* __restrict__ h, int Tk,
-                                                 FusedRoute fr) {
+                                                 FusedRoute fr, Shared1Args sh, int groute) {
+  if (SH && (int)blockIdx.x >= groute) {                        // the shared expert's gate/up parts (H % 128 == 0)
+    const int idx = (int)blockIdx.x - groute, nc = 2 * sh.I / 16;
+    shared1_part<false>(sh, idx % nc, idx / nc);
+    return;
+  }
   __shared__ __attribute__((aligned(16))) uint8_t xl[NS * KSTEP];
   __shared__ uint32_t xs[NS];
   __shared__ uint32_t bsc[16 * (NS + 1)];                       // [row][step] scale dwords, odd pitch
@@ -460,7 +466,7 @@ __global__ __launch_bounds__(64) void gu1_kernel(FfnArgs a, float* __restrict__ 
     if (EXACT || c < chunks) *reinterpret_cast<u32x4*>(xl + c * 16) = xv[i];
   }
   if (lane < nsteps) xs[lane] = xsv;
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  for (int item = blockIdx.x; item < nitems; item += SH ? groute : (int)gridDim.x) {
     const int j = item / ncg, c0 = (item % ncg) * 8;
     int e, p0 = 0, cnt = 1, slot = j;
     if (RPER > 0) {
@@ -655,10 +661,16 @@ __global__ __launch_bounds__(256, DN_WG_PER_CU(NS)) void down_decode_kernel(FfnA
 // w and w + 4 (then w + 8 and w + 12 when k > 8) with their W2 rows in
 // registers, and the 16 columns are combined in slot order exactly as the
 // combine kernel does.
-template <int NS>
+template <int NS, bool SH>
 __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const float* __restrict__ abuf,
                                                                uint8_t* __restrict__ qws,
-                                                               uint8_t* __restrict__ qsc_ws, int Tk) {
+                                                               uint8_t* __restrict__ qsc_ws, int Tk, Shared1Args sh) {
+  if (SH && (int)blockIdx.x >= a.H / 16) {                      // the shared expert's down tiles
+    const int tile = (int)blockIdx.x - a.H / 16;
+    if (sh.I % KSTEP) shared1_down<true>(sh, tile);
+    else shared1_down<false>(sh, tile);
+    return;
+  }
   constexpr int QP = NS * KSTEP + 16;                           // LDS pitch of an intermediate row
   constexpr int RQP = 8;                                        // 16-byte SwiGLU chunks per thread in flight
   __shared__ int pslot[MAX_K];
@@ -1343,10 +1355,12 @@ static inline void phase(int i, hipStream_t stream) {
 }
 
 // gate/up of one row: the NS / EXACT variant for H = 128 hs
-template <int RP>
-static void launch_gu1(int hs, dim3 grid, hipStream_t stream, const FfnArgs& a, float* abuf, float* h, int Tk,
-                       const FusedRoute& fr) {
-#define MX_GU1(NS_, EX_) hipLaunchKernelGGL((gu1_kernel<NS_, EX_, RP>), grid, dim3(64), 0, stream, a, abuf, h, Tk, fr)
+template <int RP, bool SH>
+static void launch_gu1(int hs, int groute, int gshared, hipStream_t stream, const FfnArgs& a, float* abuf, float* h,
+                       int Tk, const FusedRoute& fr, const Shared1Args& sh) {
+  const dim3 grid(groute + gshared);
+#define MX_GU1(NS_, EX_) \
+  hipLaunchKernelGGL((gu1_kernel<NS_, EX_, RP, SH>), grid, dim3(64), 0, stream, a, abuf, h, Tk, fr, sh, groute)
   if (hs == 32) MX_GU1(32, true);
   else if (hs == 40) MX_GU1(40, true);
   else if (hs == 16) MX_GU1(16, true);
@@ -1360,7 +1374,7 @@ static void launch_gu1(int hs, dim3 grid, hipStream_t stream, const FfnArgs& a, 
 }
 
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
-                      const FusedRoute* fr, float* h) {
+                      const FusedRoute* fr, float* h, const Shared1Args* sh) {
   const int Tk = a.T * a.k;
   // the caller validated the shape; a path that cannot run it is never launched
   path = ffn_resolve_path(path, Tk, a.H, a.I);
@@ -1387,13 +1401,18 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     const dim3 g0(gu_grid), b0(256);
 #define MX_GU(NS_, EX_) \
   hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R)
+    const Shared1Args shv = sh ? *sh : Shared1Args{};
     if (a.T == 1) {
-      // one wavefront per (pair, 8 intermediate columns); the SwiGLU rows go to the o region
+      // one wavefront per (pair, 8 intermediate columns); the SwiGLU rows go
+      // to the o region; then the shared expert's gate/up parts, if any
       const int items = a.k * (a.I / 8);
-      const dim3 g1(items < cus * 8 ? items : cus * 8);
-      if (!fr) launch_gu1<0>(hs, g1, stream, a, o, h, Tk, FusedRoute{});
-      else if (a.E <= 256) launch_gu1<4>(hs, g1, stream, a, o, h, Tk, *fr);
-      else launch_gu1<16>(hs, g1, stream, a, o, h, Tk, *fr);
+      const int gr = items < cus * 8 ? items : cus * 8;
+      const int gs = sh ? 2 * sh->I / 16 * shared1_nparts(a.H) : 0;
+      if (!fr) launch_gu1<0, false>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
+      else if (sh && a.E <= 256) launch_gu1<4, true>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);
+      else if (sh) launch_gu1<16, true>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);
+      else if (a.E <= 256) launch_gu1<4, false>(hs, gr, 0, stream, a, o, h, Tk, *fr, shv);
+      else launch_gu1<16, false>(hs, gr, 0, stream, a, o, h, Tk, *fr, shv);
     } else {
       if (hs == 32) MX_GU(32, true);
       else if (hs == 40) MX_GU(40, true);
@@ -1408,12 +1427,17 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
 #undef MX_GU
     phase(1, stream);
     if (a.T == 1) {
-      const dim3 g1(a.H / 16), b1(256);
-      if (is <= 2) hipLaunchKernelGGL(down_combine1_kernel<2>, g1, b1, 0, stream, a, o, qws, qsc, Tk);
-      else if (is <= 5) hipLaunchKernelGGL(down_combine1_kernel<5>, g1, b1, 0, stream, a, o, qws, qsc, Tk);
-      else if (is <= 8) hipLaunchKernelGGL(down_combine1_kernel<8>, g1, b1, 0, stream, a, o, qws, qsc, Tk);
-      else hipLaunchKernelGGL(down_combine1_kernel<16>, g1, b1, 0, stream, a, o, qws, qsc, Tk);
-      *variant = fr ? "layer1:gu1_decode_topk+down_combine1" : "ffn:gu1_decode+down_combine1";
+      const dim3 g1(a.H / 16 * (sh ? 2 : 1)), b1(256);        // the shared expert's down tiles after the routed ones
+#define MX_DC1(NS_)                                                                                    \
+  if (sh) hipLaunchKernelGGL((down_combine1_kernel<NS_, true>), g1, b1, 0, stream, a, o, qws, qsc, Tk, shv); \
+  else hipLaunchKernelGGL((down_combine1_kernel<NS_, false>), g1, b1, 0, stream, a, o, qws, qsc, Tk, shv)
+      if (is <= 2) { MX_DC1(2); }
+      else if (is <= 5) { MX_DC1(5); }
+      else if (is <= 8) { MX_DC1(8); }
+      else { MX_DC1(16); }
+#undef MX_DC1
+      *variant = sh ? "layer1_shared:gu1_decode_topk+shared_parts+down_combine1+shared_down"
+                    : fr ? "layer1:gu1_decode_topk+down_combine1" : "ffn:gu1_decode+down_combine1";
       phase(2, stream);                                         // the down kernel also combines
       phase(3, stream);
       return hipGetLastError();

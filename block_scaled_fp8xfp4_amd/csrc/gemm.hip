@@ -17,31 +17,11 @@
 // element's result does not depend on M.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
+#include "shared1_device.hpp"
 
 namespace mx {
 
 constexpr int XCDS_GEMM = 8;                      // XCDs of an MI355X (block scheduling)
-
-__device__ __forceinline__ v8i fp8_pair(const u32x4& lo, const u32x4& hi) {
-  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
-// K tail (TAIL: K % 128 != 0, e.g. the shared expert's K = 576): the last
-// step's 16-byte chunks past K are zero in registers and its scale blocks
-// past K are 127 (1.0), on both operands, in every kernel; scale rows are
-// then not dword-aligned and are read a byte at a time.
-template <bool TAIL>
-__device__ __forceinline__ u32x4 ld_chunk(const uint8_t* p, int kpos, int K) {   // p: 16 bytes at K position kpos
-  if (TAIL && kpos >= K) return u32x4{0u, 0u, 0u, 0u};
-  return ldg16(p);
-}
-// lane group g's scale of step s, in byte g (the MFMA is passed dword >> 8 g)
-template <bool TAIL>
-__device__ __forceinline__ uint32_t ld_scale(const uint8_t* row_sc, int s, int g, int nblk) {
-  if (!TAIL) return reinterpret_cast<const uint32_t*>(row_sc)[s];
-  const int b = 4 * s + g;
-  return (uint32_t)(b < nblk ? row_sc[b] : 127) << (8 * g);
-}
 
 template <bool BF16_OUT, bool WHOLE, bool TAIL>                 // WHOLE: K = 4 parts of 1024 exactly
 __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
@@ -327,140 +307,28 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(const uint8_t* __r
 }
 
 // ---------------------------------------------- shared expert, one row (T = 1)
-// Gate/up of one row as canonical parts: one wavefront per (16 output
-// columns, part q of 8 steps), the part's chain from zero written to
-// pbuf[q][N]; the shared expert's down kernel adds the parts in part order,
-// exactly as the decode kernel's LDS reduction, so the sum is the dense
-// projection's canonical result.  (The decode GEMM would run 4 wavefronts per
-// 16 columns on N / 16 = 2I / 16 CUs; this spreads the row's gate/up weights
-// over every CU.)
+// (the tile bodies are in shared1_device.hpp, shared with the fused
+// single-row layer's kernels)
 template <bool TAIL>
-__global__ __launch_bounds__(64) void gemm1_parts_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
-                                                         const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_sc,
-                                                         int N, int K, float* __restrict__ pbuf) {
-  const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
-  const int q = blockIdx.y, s0 = q * KPART_STEPS;
-  const int nsteps = (K + KSTEP - 1) / KSTEP, nblk = K / 32;
-  const int64_t n = blockIdx.x * 16 + col;
-  const uint8_t* ap = a + g * 16;
-  const uint8_t* wp = w + n * K + g * 16;
-  const uint8_t* wsp = w_sc + n * (K / 32);
-  u32x4 alo[KPART_STEPS], ahi[KPART_STEPS], blo[KPART_STEPS], bhi[KPART_STEPS];
-  uint32_t as[KPART_STEPS], bs[KPART_STEPS];
-#pragma unroll
-  for (int m = 0; m < KPART_STEPS; ++m) {                       // the row first, then the weights
-    const int s = min(s0 + m, nsteps - 1);
-    alo[m] = ld_chunk<TAIL>(ap + s * KSTEP, s * KSTEP + 16 * g, K);
-    ahi[m] = ld_chunk<TAIL>(ap + s * KSTEP + 64, s * KSTEP + 64 + 16 * g, K);
-    as[m] = ld_scale<TAIL>(a_sc, s, g, nblk);
-  }
-#pragma unroll
-  for (int m = 0; m < KPART_STEPS; ++m) {
-    const int s = min(s0 + m, nsteps - 1);
-    blo[m] = ld_chunk<TAIL>(wp + s * KSTEP, s * KSTEP + 16 * g, K);
-    bhi[m] = ld_chunk<TAIL>(wp + s * KSTEP + 64, s * KSTEP + 64 + 16 * g, K);
-    bs[m] = ld_scale<TAIL>(wsp, s, g, nblk);
-  }
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < KPART_STEPS; ++m)
-    if (s0 + m < nsteps)
-      acc = mfma_fp8_fp8(fp8_pair(alo[m], ahi[m]), fp8_pair(blo[m], bhi[m]), acc, as[m] >> (8 * g), bs[m] >> (8 * g));
-  if (g == 0) pbuf[(int64_t)q * N + n] = acc[0];                // output row 0 (every A row is the row)
+__global__ __launch_bounds__(64) void gemm1_parts_kernel(Shared1Args sh) {
+  shared1_part<TAIL>(sh, blockIdx.x, blockIdx.y);
 }
 
-// Down projection of the shared expert for one row, with the SwiGLU and the
-// requant in its prologue: h = the gate/up parts added in part order (left
-// to right, fp32), a = swiglu(gate, up), block-32 E4M3 requant (the routed
-// experts' routine) into LDS; then the 16 output columns of the workgroup as
-// the decode GEMM computes them (K = I in one part: a chain from zero over
-// the steps; past K zero elements and unit scales on both operands).
-// Workgroup 0 also writes h, q and q_sc to the workspace.  I <= 1024.
 template <bool TAIL>
-__global__ __launch_bounds__(256) void shared_down1_kernel(const float* __restrict__ pbuf, int nparts, int I,
-                                                           const uint8_t* __restrict__ w2,
-                                                           const uint8_t* __restrict__ w2_sc, float* __restrict__ y,
-                                                           float* __restrict__ h_out, uint8_t* __restrict__ q_out,
-                                                           uint8_t* __restrict__ qsc_out) {
-  constexpr int NSD = KPART_STEPS;                              // steps of K = I <= 1024
-  __shared__ __attribute__((aligned(16))) float hs[2 * NSD * KSTEP];
-  __shared__ __attribute__((aligned(16))) uint8_t q1[NSD * KSTEP];
-  __shared__ uint8_t s1[NSD * 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int nsteps = (I + KSTEP - 1) / KSTEP, nblk = I / 32;
-  const int64_t n = blockIdx.x * 16 + col;
-  // wavefront 0: the 16 W2 rows, requested first
-  u32x4 blo[NSD], bhi[NSD];
-  uint32_t bs[NSD];
-  if (wave == 0) {
-    const uint8_t* wp = w2 + n * I + g * 16;
-    const uint8_t* wsp = w2_sc + n * (I / 32);
-#pragma unroll
-    for (int s = 0; s < NSD; ++s) {
-      const int ss = min(s, nsteps - 1);
-      blo[s] = ld_chunk<TAIL>(wp + ss * KSTEP, ss * KSTEP + 16 * g, I);
-      bhi[s] = ld_chunk<TAIL>(wp + ss * KSTEP + 64, ss * KSTEP + 64 + 16 * g, I);
-      bs[s] = ld_scale<TAIL>(wsp, ss, g, nblk);
-    }
-  }
-  // h = ((p0 + p1) + p2) + ... per column, 4 columns per thread
-  const int c4n = 2 * I / 4;
-  for (int c4 = tid; c4 < c4n; c4 += 256) {
-    v4f v = *reinterpret_cast<const v4f*>(pbuf + 4 * c4);
-    for (int q = 1; q < nparts; ++q) {
-      const v4f p = *reinterpret_cast<const v4f*>(pbuf + (int64_t)q * 2 * I + 4 * c4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = v[i] + p[i];
-    }
-    *reinterpret_cast<v4f*>(&hs[4 * c4]) = v;
-    if (blockIdx.x == 0) *reinterpret_cast<v4f*>(h_out + 4 * c4) = v;
-  }
-  for (int idx = tid; idx < NSD * KSTEP - I; idx += 256) q1[I + idx] = 0;   // K past I: zero elements
-  for (int idx = tid; idx < NSD * 4 - nblk; idx += 256) s1[nblk + idx] = 127;   // and unit scales
-  lds_barrier();
-  // SwiGLU + requant: 16 lanes per block of 32, columns c and c + 16
-  for (int b0 = 0; b0 < nblk; b0 += 16) {
-    const int b = b0 + (tid >> 4), c = tid & 15;
-    const bool ok = b < nblk;
-    const int cb = ok ? b * 32 : 0;
-    uint32_t sc;
-    const uint32_t d = swiglu_requant2(hs[cb + c], hs[I + cb + c], hs[cb + 16 + c], hs[I + cb + 16 + c], &sc);
-    if (ok) {
-      q1[cb + c] = (uint8_t)d;
-      q1[cb + 16 + c] = (uint8_t)(d >> 8);
-      if (c == 0) s1[b] = (uint8_t)sc;
-      if (blockIdx.x == 0) {
-        q_out[cb + c] = (uint8_t)d;
-        q_out[cb + 16 + c] = (uint8_t)(d >> 8);
-        if (c == 0) qsc_out[b] = (uint8_t)sc;
-      }
-    }
-  }
-  lds_barrier();
-  if (wave != 0) return;
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < NSD; ++s)
-    if (s < nsteps) {
-      const u32x4 alo = *reinterpret_cast<const u32x4*>(&q1[s * KSTEP + g * 16]);
-      const u32x4 ahi = *reinterpret_cast<const u32x4*>(&q1[s * KSTEP + 64 + g * 16]);
-      const uint32_t sa = (uint32_t)s1[4 * s + g] << (8 * g);
-      acc = mfma_fp8_fp8(fp8_pair(alo, ahi), fp8_pair(blo[s], bhi[s]), acc, sa >> (8 * g), bs[s] >> (8 * g));
-    }
-  if (g == 0) y[n] = acc[0];
+__global__ __launch_bounds__(256) void shared_down1_kernel(Shared1Args sh) {
+  shared1_down<TAIL>(sh, blockIdx.x);
 }
 
 hipError_t launch_shared_down1(const uint8_t* x, const uint8_t* x_sc, int H, const uint8_t* w13,
                                const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,
                                float* h, uint8_t* q, uint8_t* q_sc, float* pbuf, hipStream_t stream) {
-  const int nparts = (H + KPART - 1) / KPART;
-  const dim3 g1(2 * I / 16, nparts);
-  if (H % KSTEP) hipLaunchKernelGGL(gemm1_parts_kernel<true>, g1, dim3(64), 0, stream, x, x_sc, w13, w13_sc, 2 * I, H, pbuf);
-  else hipLaunchKernelGGL(gemm1_parts_kernel<false>, g1, dim3(64), 0, stream, x, x_sc, w13, w13_sc, 2 * I, H, pbuf);
+  const Shared1Args sh{x, x_sc, w13, w13_sc, w2, w2_sc, H, I, pbuf, y, h, q, q_sc};
+  const dim3 g1(2 * I / 16, shared1_nparts(H));
+  if (H % KSTEP) hipLaunchKernelGGL(gemm1_parts_kernel<true>, g1, dim3(64), 0, stream, sh);
+  else hipLaunchKernelGGL(gemm1_parts_kernel<false>, g1, dim3(64), 0, stream, sh);
   const dim3 g2(H / 16);
-  if (I % KSTEP) hipLaunchKernelGGL(shared_down1_kernel<true>, g2, dim3(256), 0, stream, pbuf, nparts, I, w2, w2_sc, y, h, q, q_sc);
-  else hipLaunchKernelGGL(shared_down1_kernel<false>, g2, dim3(256), 0, stream, pbuf, nparts, I, w2, w2_sc, y, h, q, q_sc);
+  if (I % KSTEP) hipLaunchKernelGGL(shared_down1_kernel<true>, g2, dim3(256), 0, stream, sh);
+  else hipLaunchKernelGGL(shared_down1_kernel<false>, g2, dim3(256), 0, stream, sh);
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ constexpr int ROUTE_CHUNK = 256; // rows per bucketing chunk
 constexpr int ROUTE_FUSED_MAX_T = 32;  // rows ranked inside the single-workgroup route (more: a top-k launch first)
 constexpr int LG_MAX_H = 16384;     // router logits: hidden width
 constexpr int LG_PREFILL_MIN_T = 1024; // router logits: rows from which the tiled kernel runs (measured crossover)
+constexpr int KPART_MAX_SHARED1 = 1024; // one-row shared expert: its down projection is one K part
 
 hipError_t launch_quantize(const void* src, bool bf16, int64_t rows, int64_t cols, bool fp4,
                            uint8_t* q, uint8_t* sc, hipStream_t stream);
@@ -36,6 +37,14 @@ struct FusedRoute {
   const float* logits; const float* survival; float skip_below;
   int32_t* ids; float* w; int32_t* offsets; int32_t* perm; int32_t* slot_pos;
 };
+// one row's shared expert (T = 1, I <= 1024): x FP8 [H] + SC; W13 FP8 [2I][H]
+// + SC; W2 FP8 [H][I] + SC; pbuf the gate/up parts [ceil(H / 1024)][2I]; y
+// [H]; h [2I], q [I], q_sc [I/32] receive the intermediate (diagnostics)
+struct Shared1Args {
+  const uint8_t* x; const uint8_t* x_sc; const uint8_t* w13; const uint8_t* w13_sc;
+  const uint8_t* w2; const uint8_t* w2_sc; int H, I;
+  float* pbuf; float* y; float* h; uint8_t* q; uint8_t* q_sc;
+};
 size_t ffn_ws_bytes(int T, int H, int E, int I, int k);
 void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_o);
 // path: 0 automatic, 1 decode kernels, 2 prefill kernels.  Returns the path
@@ -43,8 +52,10 @@ void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, 
 // when no kernel supports the shape (then nothing may be launched).
 int ffn_resolve_path(int path, int64_t Tk, int H, int I);
 // h: NULL, or fp32 [T*k][2I] that receives the gate/up values (diagnostics)
+// sh (single-row fused layer only): the shared expert's tiles run in the same
+// two launches as the routed experts'
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
-                      const FusedRoute* fr = nullptr, float* h = nullptr);
+                      const FusedRoute* fr = nullptr, float* h = nullptr, const Shared1Args* sh = nullptr);
 void set_ffn_phase_events(const hipEvent_t* ev, int n);
 // moe_expert_ffn_noalloc: the library's own device scratch array (per GPU,
 // NOALLOC_SCRATCH_BYTES) in place of a caller workspace; *ptr receives its
@@ -67,6 +78,9 @@ hipError_t launch_shared_down1(const uint8_t* x, const uint8_t* x_sc, int H, con
                                const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,
                                float* h, uint8_t* q, uint8_t* q_sc, float* pbuf, hipStream_t stream);
 size_t shared_ws_bytes(int T, int H, int I);
+// the pointers of the one-row shared expert inside a moe_shared_expert workspace
+Shared1Args shared1_args(const uint8_t* x, const uint8_t* x_sc, int H, const uint8_t* w13, const uint8_t* w13_sc,
+                         const uint8_t* w2, const uint8_t* w2_sc, int I, float* y, void* ws);
 hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H, const uint8_t* w13,
                                 const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,
                                 void* ws, hipStream_t stream, const char** variant);

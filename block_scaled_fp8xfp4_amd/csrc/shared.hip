@@ -49,6 +49,15 @@ size_t shared_ws_bytes(int T, int H, int I) {
   return base + (one_row_path(T, I) ? a256((size_t)((H + KPART - 1) / KPART) * 2 * I * 4) : 0);
 }
 
+Shared1Args shared1_args(const uint8_t* x, const uint8_t* x_sc, int H, const uint8_t* w13, const uint8_t* w13_sc,
+                         const uint8_t* w2, const uint8_t* w2_sc, int I, float* y, void* ws) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* h = reinterpret_cast<float*>(base);
+  uint8_t* q = base + a256((size_t)2 * I * 4);
+  uint8_t* q_sc = q + a256((size_t)I);
+  float* pbuf = reinterpret_cast<float*>(q_sc + a256((size_t)(I / 32)));
+  return Shared1Args{x, x_sc, w13, w13_sc, w2, w2_sc, H, I, pbuf, y, h, q, q_sc};
+}
 hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H, const uint8_t* w13,
                                 const uint8_t* w13_sc, const uint8_t* w2, const uint8_t* w2_sc, int I, float* y,
                                 void* ws, hipStream_t stream, const char** variant) {
@@ -58,9 +67,9 @@ hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, in
   uint8_t* q_sc = q + a256((size_t)T * I);
   const char* v = "";
   if (one_row_path(T, I)) {
-    float* pbuf = reinterpret_cast<float*>(q_sc + a256((size_t)T * (I / 32)));
+    const Shared1Args sh = shared1_args(x, x_sc, H, w13, w13_sc, w2, w2_sc, I, y, ws);
     *variant = "shared:decode1_gemm_parts+down_requant";
-    return launch_shared_down1(x, x_sc, H, w13, w13_sc, w2, w2_sc, I, y, h, q, q_sc, pbuf, stream);
+    return launch_shared_down1(x, x_sc, H, w13, w13_sc, w2, w2_sc, I, y, sh.h, sh.q, sh.q_sc, sh.pbuf, stream);
   }
   hipError_t e = launch_block_gemm(x, x_sc, w13, w13_sc, T, 2 * I, H, h, false, stream, &v);
   if (e != hipSuccess) return e;

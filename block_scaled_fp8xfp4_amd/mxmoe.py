@@ -20,7 +20,8 @@ EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logit
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
            "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events",
            "moe_shared_expert_workspace_bytes", "moe_shared_expert", "mx_prefetch",
-           "moe_layer_decode1", "mx_set_ffn_diag", "moe_expert_ffn_noalloc", "moe_expert_ffn_noalloc_max_bytes")
+           "moe_layer_decode1", "mx_set_ffn_diag", "moe_expert_ffn_noalloc", "moe_expert_ffn_noalloc_max_bytes",
+           "moe_layer_decode1_shared_workspace_bytes", "moe_layer_decode1_shared")
 
 _lib = None
 
@@ -72,6 +73,11 @@ def load():
     lib.moe_shared_expert.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, SZ, P]
     lib.moe_layer_decode1.restype = I32
     lib.moe_layer_decode1.argtypes = [P, I32, I32, P, F32, P, P, I32, P, P, P, P, I32, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_layer_decode1_shared_workspace_bytes.restype = SZ
+    lib.moe_layer_decode1_shared_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.moe_layer_decode1_shared.restype = I32
+    lib.moe_layer_decode1_shared.argtypes = [P, I32, I32, P, F32, P, P, I32, P, P, P, P, I32, P, P, P, P, I32,
+                                             P, P, P, P, P, P, P, P, SZ, P]
     lib.mx_prefetch.restype = I32
     lib.mx_prefetch.argtypes = [P, ctypes.c_uint64, ctypes.c_uint64, P]
     lib.mx_status_string.restype = ctypes.c_char_p
@@ -208,6 +214,25 @@ def moe_layer_decode1(logits, k, survival, skip_below, x, x_sc, w13, w13_sc, w2,
                                     _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I, _ptr(topk_ids), _ptr(topk_w),
                                     _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(y), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_decode1")
+
+
+def moe_layer_decode1_shared_workspace_bytes(H, E, I, k, Is):
+    return load().moe_layer_decode1_shared_workspace_bytes(H, E, I, k, Is)
+
+
+def moe_layer_decode1_shared(logits, k, survival, skip_below, x, x_sc, w13, w13_sc, w2, w2_sc, E, I,
+                             sw13, sw13_sc, sw2, sw2_sc, topk_ids, topk_w, expert_offsets, perm, slot_pos, y,
+                             y_shared, ws, stream=None):
+    """moe_layer_decode1 plus the row's shared expert (sw13 FP8 [2Is, H], sw2 FP8 [H, Is] + scales) in the
+    same two launches; y_shared [H] fp32 as moe_shared_expert."""
+    H = x.shape[-1]
+    Is = sw2.shape[-1]
+    _check(load().moe_layer_decode1_shared(_ptr(logits), E, k, _ptr(survival), float(skip_below), _ptr(x), _ptr(x_sc),
+                                           H, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I, _ptr(sw13),
+                                           _ptr(sw13_sc), _ptr(sw2), _ptr(sw2_sc), Is, _ptr(topk_ids), _ptr(topk_w),
+                                           _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(y), _ptr(y_shared),
+                                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_layer_decode1_shared")
 
 
 def fp8_block_gemm(a, a_sc, w, w_sc, y, y_dtype, stream=None):

@@ -243,6 +243,40 @@ mx_status moe_layer_decode1(const float* logits, int E, int k, const float* surv
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The whole MoE layer of ONE row, routed and shared experts, in the same two
+ * launches: moe_layer_decode1 with the shared expert's tiles carried by its
+ * kernels (the shared expert's gate/up parts beside the routed gate/up, its
+ * down projection beside the routed down projection and combine), instead of
+ * a separate moe_shared_expert call of two more launches (forum thread post
+ * #6, "Kernel by kernel against B12X": the shared expert runs beside the
+ * routed experts on a side stream; TP4 README, settings table, row
+ * "Kernels").  Results, bit for bit: topk_ids, topk_w, expert_offsets, perm,
+ * slot_pos and y as moe_layer_decode1; y_shared [H] fp32 as
+ * moe_shared_expert(x, x_sc, T = 1, H, sw13, sw13_sc, sw2, sw2_sc, Is).  The
+ * skip mask applies to the routed experts only (a dead row still gets its
+ * shared expert).  The caller adds y and y_shared.  sw13 FP8 [2Is][H] + SC
+ * [2Is][H/32]; sw2 FP8 [H][Is] + SC [H][Is/32]; sw13, sw2 16-byte aligned,
+ * their scales and y_shared 4-byte aligned.  Supported: the
+ * moe_layer_decode1 shapes and Is % 32 == 0, Is <= 1024 (else
+ * MX_EUNSUPPORTED).  ws: moe_layer_decode1_shared_workspace_bytes(H, E, I,
+ * k, Is) bytes, 256-byte aligned: the routed part (the moe_expert_ffn
+ * layout, moe_ws_layout(1, H, I, k)) padded to 256 bytes, then the shared
+ * part (the moe_shared_expert layout at T = 1).  Other arguments and errors
+ * as moe_layer_decode1; the workspace size function returns 0 for invalid
+ * shapes.
+ */
+size_t    moe_layer_decode1_shared_workspace_bytes(int H, int E, int I, int k, int Is);
+mx_status moe_layer_decode1_shared(const float* logits, int E, int k, const float* survival, float skip_below,
+                                   const uint8_t* x, const uint8_t* x_sc, int H,
+                                   const uint8_t* w13, const uint8_t* w13_sc,
+                                   const uint8_t* w2, const uint8_t* w2_sc, int I,
+                                   const uint8_t* sw13, const uint8_t* sw13_sc,
+                                   const uint8_t* sw2, const uint8_t* sw2_sc, int Is,
+                                   int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                                   int32_t* perm, int32_t* slot_pos, float* y, float* y_shared,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dense block-32 FP8 GEMM (post #2 "Known issues and next steps": dense FP8
  * GEMMs are the largest remaining decode lever; post #6 "How it works":
  * MXFP8 projections, decode rows on small row tiles).

@@ -167,6 +167,34 @@ def test_layer_decode1_rejects_bad_arguments(lib):
     assert layer1(lib, ws=None) == mxmoe.MX_EWORKSPACE
 
 
+def layer1s(lib, H=256, I=64, E=8, k=2, Is=64, ws=FAKE_WS, ws_bytes=1 << 30, sw2=FAKE, ys=FAKE):
+    return lib.moe_layer_decode1_shared(FAKE, E, k, None, 0.2, FAKE, FAKE, H, FAKE, FAKE, FAKE, FAKE, I,
+                                        FAKE, FAKE, sw2, FAKE, Is, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ys,
+                                        ws, ws_bytes, None)
+
+
+def test_layer_decode1_shared_rejects_bad_arguments(lib):
+    """The routed part's checks as moe_layer_decode1, and the shared expert's:
+    Is a multiple of 32 up to 1024 (its down projection is one K part), every
+    pointer, the combined workspace; all before any launch."""
+    assert layer1s(lib, k=0) == mxmoe.MX_EINVAL
+    assert layer1s(lib, H=320) == mxmoe.MX_EUNSUPPORTED
+    assert layer1s(lib, Is=48) == mxmoe.MX_EINVAL
+    assert layer1s(lib, Is=16) == mxmoe.MX_EINVAL
+    assert layer1s(lib, Is=1056) == mxmoe.MX_EUNSUPPORTED
+    assert layer1s(lib, sw2=None) == mxmoe.MX_EINVAL
+    assert layer1s(lib, ys=None) == mxmoe.MX_EINVAL
+    assert layer1s(lib, ys=ctypes.c_void_p((1 << 20) + 2)) == mxmoe.MX_EINVAL
+    assert layer1s(lib, ws=None) == mxmoe.MX_EWORKSPACE
+    need = lib.moe_layer_decode1_shared_workspace_bytes(256, 8, 64, 2, 64)
+    routed = lib.moe_expert_ffn_workspace_bytes(1, 256, 8, 64, 2)
+    shared = lib.moe_shared_expert_workspace_bytes(1, 256, 64)
+    assert need == (routed + 255) // 256 * 256 + shared
+    assert layer1s(lib, ws_bytes=need - 1) == mxmoe.MX_EWORKSPACE
+    assert lib.moe_layer_decode1_shared_workspace_bytes(256, 8, 64, 2, 48) == 0
+    assert lib.moe_layer_decode1_shared_workspace_bytes(256, 8, 64, 9, 64) == 0
+
+
 def test_ffn_diagnostic_buffer(lib):
     """mx_set_ffn_diag: misaligned buffers are refused; a call whose gate/up
     values do not fit the buffer fails with MX_EWORKSPACE before any launch."""

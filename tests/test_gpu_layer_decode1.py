@@ -66,3 +66,86 @@ def test_dead_row_and_ties():
     ties = np.zeros((1, 32), np.float32)                       # all equal: experts 0..k-1
     y, route = run_both(layer, ties, np.array([0.9], np.float32), 0.2)
     assert np.array_equal(host(route.ids)[0], np.arange(4))
+
+
+# ------------------------------------------- routed + shared experts, one row
+def shared_operands(cfg, H, Is):
+    """The shared expert's FP8 weights (quantized by the oracle) on the device."""
+    w13, w2 = synth.shared_expert_weights(cfg, H, Is)
+    q13, s13 = oracle.quantize_e4m3(w13)
+    q2, s2 = oracle.quantize_e4m3(w2)
+    return tuple(dev(t) for t in (q13, s13, q2, s2))
+
+
+def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
+    """moe_layer_decode1_shared against moe_layer_decode1 followed by
+    moe_shared_expert (T = 1): route outputs, y, y_shared and both workspace
+    parts (the routed intermediate and SwiGLU rows; the shared h, q, q_sc and
+    gate/up parts) bit for bit."""
+    c = layer.cfg
+    E, k, H, I = c.E, c.k, c.H, c.I
+    sw13, sw13s, sw2, sw2s = sw
+    Is = sw2.shape[1]
+    d = layer.d
+    x, xs = d["x"][:1].contiguous(), d["x_sc"][:1].contiguous()
+    lg = dev(np.ascontiguousarray(logits[:1], np.float32))
+    sv = None if survival is None else dev(np.ascontiguousarray(survival[:1], np.float32))
+    rws = mxmoe.moe_expert_ffn_workspace_bytes(1, H, E, I, k)
+    sws = mxmoe.moe_shared_expert_workspace_bytes(1, H, Is)
+    # the two calls
+    ref = Route(1, E, k)
+    y_ref = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws_r = torch.full((rws,), 0xFF, dtype=torch.uint8, device="cuda")
+    mxmoe.moe_layer_decode1(lg, k, sv, skip, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], E, I, ref.ids, ref.w,
+                            ref.offsets, ref.perm, ref.slot_pos, y_ref, ws_r)
+    ys_ref = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws_s = torch.full((sws,), 0xFF, dtype=torch.uint8, device="cuda")
+    mxmoe.moe_shared_expert(x, xs, sw13, sw13s, sw2, sw2s, ys_ref, ws_s)
+    assert mxmoe.last_variant() == "shared:decode1_gemm_parts+down_requant"
+    # the fused call
+    fz = Route(1, E, k)
+    for key in ("ids", "offsets", "perm", "slot_pos"):
+        getattr(fz, key).fill_(-7)
+    y = torch.full((1, H), 7.0, device="cuda")
+    ys = torch.full((1, H), 7.0, device="cuda")
+    need = mxmoe.moe_layer_decode1_shared_workspace_bytes(H, E, I, k, Is)
+    assert need == (rws + 255) // 256 * 256 + sws
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    mxmoe.moe_layer_decode1_shared(lg, k, sv, skip, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], E, I,
+                                   sw13, sw13s, sw2, sw2s, fz.ids, fz.w, fz.offsets, fz.perm, fz.slot_pos, y, ys, ws)
+    assert mxmoe.last_variant().startswith("layer1_shared:")
+    for key in ("ids", "w", "offsets", "perm", "slot_pos"):
+        assert torch.equal(getattr(fz, key), getattr(ref, key)), key
+    assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
+    assert torch.equal(ys.view(torch.int32), ys_ref.view(torch.int32))
+    off = (rws + 255) // 256 * 256
+    assert torch.equal(ws[:rws], ws_r), "routed workspace"
+    assert torch.equal(ws[off:off + sws], ws_s), "shared workspace"
+    return host(y), host(ys)
+
+
+def test_decode_workload_with_shared_expert_bitwise():
+    from gpu_common import moe_workload
+    inp, r, layer = moe_workload("decode")
+    c = inp.cfg
+    y, ys = run_with_shared(layer, inp.logits, shared_operands(c, c.H, c.I))
+    assert np.any(ys) and np.any(y)
+    say("layer_decode1_shared: routed and shared outputs bitwise equal to the two separate calls")
+
+
+@pytest.mark.parametrize("shape,Is", [
+    (dict(seed=41, T=1, H=256, E=8, k=2, I=64), 64),
+    (dict(seed=42, T=1, H=1152, E=384, k=8, I=96), 160),          # K tail in the shared down projection
+    (dict(seed=43, T=1, H=512, E=64, k=16, I=160), 1024),         # the largest shared intermediate
+    (dict(seed=45, T=1, H=2048, E=32, k=4, I=128), 128),          # two K parts of the shared gate/up
+])
+def test_small_shapes_with_shared_expert(shape, Is):
+    inp, r, layer = small_workload(**shape)
+    run_with_shared(layer, inp.logits, shared_operands(layer.cfg, shape["H"], Is))
+
+
+def test_dead_row_still_gets_its_shared_expert():
+    inp, r, layer = small_workload(seed=44, T=1, H=256, E=32, k=4, I=64)
+    y, ys = run_with_shared(layer, inp.logits, shared_operands(layer.cfg, 256, 96), np.array([0.1], np.float32), 0.2)
+    assert not np.any(y) and not np.any(np.signbit(y))
+    assert np.any(ys)
