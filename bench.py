@@ -582,7 +582,9 @@ def main():
         result["shared_expert"] = run_shared_expert(cfg, inp, args.steps, args.warmup)
         cpu_cfg = cfg
         if not args.no_prefill:
-            pre, _ = run_prefill(5, 2)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()                           # the decode weight copies go back to the device
+            pre, _ = run_prefill(20, 5)
             result["prefill"] = pre
 
     result.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
