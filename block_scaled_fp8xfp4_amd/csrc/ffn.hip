@@ -494,7 +494,7 @@ __global__ __launch_bounds__(64) void gu1_kernel(FfnArgs a, float* __restrict__ 
     u32x4 bw[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (EXACT || s < nsteps ? s : nsteps - 1) * 64);
-    if (RPER > 0 && h != nullptr) {                             // the pair's bucket position, for the diagnostic h
+    if (RPER > 0) {                                             // the other slots, while the weights stream in
       topk_rounds<RP>(st, a.k);
       for (int i = 0; i < a.k; ++i) p0 += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
     }
