@@ -43,3 +43,27 @@ def test_gemm_largest_k(M, prefix):
     rows = None if M < 16 else np.array([0, 1, 159, 318, 319], np.int32)
     check_gemm(a, w, rows=rows)
     assert mxmoe.last_variant().startswith(prefix)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_ffn_all_rows_dead(path):
+    """A batch whose rows all skip the routed experts: no pair is bucketed, no
+    expert item runs, and y is +0 everywhere (no sign bit), on both paths; the
+    output buffer starts as garbage."""
+    import torch
+    from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route
+    from gpu_common import dev, host
+    inp, r, layer = small_workload(seed=77, T=40, H=256, E=16, k=4, I=64)
+    c = layer.cfg
+    route = Route(c.T, c.E, c.k)
+    route(dev(inp.logits), dev(np.full(c.T, 0.1, np.float32)))
+    assert not host(route.offsets).any() and np.all(host(route.slot_pos) == -1)
+    ffn = ExpertFFN(c.T, c.H, c.E, c.I, c.k)
+    ffn.y.fill_(float("nan"))
+    old = mxmoe.set_ffn_path(path)
+    try:
+        y = ffn(layer.d["x"], layer.d["x_sc"], route, layer.d["w13"], layer.d["w13_sc"], layer.d["w2"], layer.d["w2_sc"])
+    finally:
+        mxmoe.set_ffn_path(old)
+    yh = host(y)
+    assert not np.any(yh) and not np.any(np.signbit(yh)), "dead rows must give +0"
