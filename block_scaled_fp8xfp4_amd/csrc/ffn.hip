@@ -421,7 +421,8 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
 // (the rank of its expert among the k in ascending order) is known.
 // Workgroup 0 writes the route outputs exactly as the single-row route kernel
 // does, for the down kernel and the caller.  RPER = 0: the pairs come from
-// the route's offsets.
+// the route's offsets.  SH (the routed + shared layer): the workgroups from
+// groute on each run one of the shared expert's gate/up parts instead.
 template <int NS, bool EXACT, int RPER, bool SH>
 __global__ __launch_bounds__(64) void gu1_kernel(FfnArgs a, float* __restrict__ abuf, float* __restrict__ h, int Tk,
                                                  FusedRoute fr, Shared1Args sh, int groute) {
@@ -660,7 +661,8 @@ __global__ __launch_bounds__(256, DN_WG_PER_CU(NS)) void down_decode_kernel(FfnA
 // intermediate to the workspace).  Wavefront w runs the down chains of slots
 // w and w + 4 (then w + 8 and w + 12 when k > 8) with their W2 rows in
 // registers, and the 16 columns are combined in slot order exactly as the
-// combine kernel does.
+// combine kernel does.  SH (the routed + shared layer): workgroups H / 16 and
+// on each run one of the shared expert's down tiles instead.
 template <int NS, bool SH>
 __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const float* __restrict__ abuf,
                                                                uint8_t* __restrict__ qws,
