@@ -120,29 +120,40 @@ __device__ __forceinline__ int tile_expert(const int* tile_start, int E, int til
 }
 
 // The expert list seen by one wavefront, from its own registers (no LDS, no
-// barrier): lane l holds offsets[l * per + i], i = 0..per (per = ceil(E / 64)).
-// A "tile" here is an expert with at least one live pair, in expert order.
+// barrier): lane l holds offsets[l * per + i], i = 0..per (per = ceil(E / 64)
+// <= EPL).  A "tile" here is an expert with at least one live pair, in expert
+// order.  EPL = 4 serves E <= 256 and EPL = 16 every E up to MAX_E: the loops
+// over a lane's entries are unrolled to EPL, and at E = 256 the four-entry
+// form takes 3.8 us off the verification batch's FFN call (two kernels, and
+// one list lookup per item).
+template <int EPL>
 struct WaveExperts {
-  int o[17];
+  int o[EPL + 1];
   int per, cnt, incl;                             // this lane's tiles and their inclusive prefix
 };
 
-__device__ __forceinline__ void wave_experts_load(const int32_t* __restrict__ offsets, int E, WaveExperts& w) {
+// Entries per lane of the expert list for E experts.
+constexpr int epl_for(int E) { return E <= 256 ? 4 : 16; }
+
+template <int EPL>
+__device__ __forceinline__ void wave_experts_load(const int32_t* __restrict__ offsets, int E, WaveExperts<EPL>& w) {
+  static_assert(EPL == 4 || EPL == 16, "expert-list capacity");
   const int lane = threadIdx.x & 63;
-  w.per = (E + 63) / 64;                          // <= MAX_E / 64 = 16
+  w.per = (E + 63) / 64;                          // <= EPL (the launcher picks EPL from E)
 #pragma unroll
-  for (int i = 0; i < 17; ++i) {                  // branch-free: entries past per are never used
+  for (int i = 0; i < EPL + 1; ++i) {             // branch-free: entries past per are never used
     const int e = lane * w.per + i;
     w.o[i] = offsets[e < E ? e : E];
   }
 }
 
 // Count this lane's tiles and scan them over the wavefront; returns the total.
-__device__ __forceinline__ int wave_experts_scan(int E, WaveExperts& w) {
+template <int EPL>
+__device__ __forceinline__ int wave_experts_scan(int E, WaveExperts<EPL>& w) {
   const int lane = threadIdx.x & 63;
   int c = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < EPL; ++i)
     if (i < w.per && lane * w.per + i < E && w.o[i + 1] > w.o[i]) ++c;
   w.cnt = c;
   w.incl = c + wave_excl_scan(c, lane);
@@ -150,13 +161,14 @@ __device__ __forceinline__ int wave_experts_scan(int E, WaveExperts& w) {
 }
 
 // Tile t (< total): its expert, first bucket position and pair count.
-__device__ __forceinline__ void wave_tile(const WaveExperts& w, int E, int t, int& e, int& p0, int& cnt) {
+template <int EPL>
+__device__ __forceinline__ void wave_tile(const WaveExperts<EPL>& w, int E, int t, int& e, int& p0, int& cnt) {
   const int lane = threadIdx.x & 63;
   const unsigned long long past = __ballot(w.incl > t);
   const int L = __builtin_ctzll(past);            // lowest lane whose tiles reach past t
   int k = t - (w.incl - w.cnt), ei = 0, pe = 0, ce = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     const bool live = i < w.per && lane * w.per + i < E && w.o[i + 1] > w.o[i];
     if (live && k == 0) { ei = lane * w.per + i; pe = w.o[i]; ce = w.o[i + 1] - w.o[i]; }
     if (live) --k;
@@ -167,11 +179,12 @@ __device__ __forceinline__ void wave_tile(const WaveExperts& w, int E, int t, in
 }
 
 // The expert whose bucket holds position p (offsets[e] <= p < offsets[e + 1]), or -1.
-__device__ __forceinline__ int wave_owner(const WaveExperts& w, int E, int p) {
+template <int EPL>
+__device__ __forceinline__ int wave_owner(const WaveExperts<EPL>& w, int E, int p) {
   const int lane = threadIdx.x & 63;
   int ei = -1;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < EPL; ++i)
     if (i < w.per && lane * w.per + i < E && w.o[i] <= p && p < w.o[i + 1]) ei = lane * w.per + i;
   const unsigned long long has = __ballot(ei >= 0);
   return has ? __builtin_amdgcn_readlane(ei, __builtin_ctzll(has)) : -1;
@@ -252,7 +265,7 @@ constexpr int DEC_SPITCH = DEC_MAX_STEPS + 1;     // LDS pitch (dwords) of the s
 // one requantized block.  Writes q, its scale, and the fp32 h = [gate | up]
 // of every pair when h is non-null (diagnostics).  EXACT: H = 128 NS, so
 // every address offset is a constant.
-template <int NS, bool EXACT>
+template <int NS, bool EXACT, int EPL>
 __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* __restrict__ qws,
                                                            uint8_t* __restrict__ qsc_ws, float* __restrict__ h,
                                                            int Tk, int R) {
@@ -308,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
       tok[tid] = (pr >= 0 && pr < Tk) ? pr / a.k : -1;
     }
   };
-  WaveExperts we;                                               // every wavefront reads the expert list itself
+  WaveExperts<EPL> we;                                          // every wavefront reads the expert list itself
   wave_experts_load(a.offsets, a.E, we);
   const int nitems = wave_experts_scan(a.E, we) * nb;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void gu_decode_kernel(FfnArgs a, uint8_t* _
 // does, for the down kernel and the caller.  RPER = 0: the pairs come from
 // the route's offsets.  SH (the routed + shared layer): the workgroups from
 // groute on each run one of the shared expert's gate/up parts instead.
-template <int NS, bool EXACT, int RPER, bool SH>
+template <int NS, bool EXACT, int RPER, bool SH, int EPL>
 __global__ __launch_bounds__(64) void gu1_kernel(FfnArgs a, float* __restrict__ abuf, float* __restrict__ h, int Tk,
                                                  FusedRoute fr, Shared1Args sh, int groute) {
   if (SH && (int)blockIdx.x >= groute) {                        // the shared expert's gate/up parts (H % 128 == 0)
@@ -446,7 +459,7 @@ __global__ __launch_bounds__(64) void gu1_kernel(FfnArgs a, float* __restrict__ 
     xv[i] = (EXACT || c < chunks) ? ldg16(a.x + c * 16) : u32x4{0u, 0u, 0u, 0u};
   }
   uint32_t xsv = lane < nsteps ? reinterpret_cast<const uint32_t*>(a.x_sc)[lane] : 0x7F7F7F7Fu;
-  WaveExperts we;
+  WaveExperts<EPL> we;
   constexpr int RP = RPER > 0 ? RPER : 1;
   TopkState<RP> st;
   bool live = true;
@@ -589,13 +602,13 @@ __device__ void stage_q_rows(const uint8_t* __restrict__ qws, const uint8_t* __r
 // per wavefront.  W2 first (NS >= I / 128 steps in registers), then the
 // expert's intermediate rows, 16 per pass, from the workspace into LDS;
 // writes o.
-template <int NS>
+template <int NS, int EPL>
 __global__ __launch_bounds__(256, DN_WG_PER_CU(NS)) void down_decode_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
                                                              const uint8_t* __restrict__ qsc_ws,
                                                              float* __restrict__ o, int Tk) {
   __shared__ __attribute__((aligned(16))) uint8_t qlds[DN_ROWS][MAX_I + 16];
   __shared__ uint8_t slds[DN_ROWS][MAX_I / 32];
-  WaveExperts we;
+  WaveExperts<EPL> we;
   wave_experts_load(a.offsets, a.E, we);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -663,7 +676,7 @@ __global__ __launch_bounds__(256, DN_WG_PER_CU(NS)) void down_decode_kernel(FfnA
 // registers, and the 16 columns are combined in slot order exactly as the
 // combine kernel does.  SH (the routed + shared layer): workgroups H / 16 and
 // on each run one of the shared expert's down tiles instead.
-template <int NS, bool SH>
+template <int NS, bool SH, int EPL>
 __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const float* __restrict__ abuf,
                                                                uint8_t* __restrict__ qws,
                                                                uint8_t* __restrict__ qsc_ws, int Tk, Shared1Args sh) {
@@ -691,7 +704,7 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
     my_p = a.slot_pos[tid];
     my_w = a.topk_w[tid];
   }
-  WaveExperts we;
+  WaveExperts<EPL> we;
   wave_experts_load(a.offsets, a.E, we);
   // the k SwiGLU rows (row j = slot j), requested before any weight, as
   // 16-byte chunks: chunk ch = tid + 256 i of a round holds floats [4 c, 4 c +
@@ -1357,12 +1370,12 @@ static inline void phase(int i, hipStream_t stream) {
 }
 
 // gate/up of one row: the NS / EXACT variant for H = 128 hs
-template <int RP, bool SH>
+template <int RP, bool SH, int EPL>
 static void launch_gu1(int hs, int groute, int gshared, hipStream_t stream, const FfnArgs& a, float* abuf, float* h,
                        int Tk, const FusedRoute& fr, const Shared1Args& sh) {
   const dim3 grid(groute + gshared);
 #define MX_GU1(NS_, EX_) \
-  hipLaunchKernelGGL((gu1_kernel<NS_, EX_, RP, SH>), grid, dim3(64), 0, stream, a, abuf, h, Tk, fr, sh, groute)
+  hipLaunchKernelGGL((gu1_kernel<NS_, EX_, RP, SH, EPL>), grid, dim3(64), 0, stream, a, abuf, h, Tk, fr, sh, groute)
   if (hs == 32) MX_GU1(32, true);
   else if (hs == 40) MX_GU1(40, true);
   else if (hs == 16) MX_GU1(16, true);
@@ -1373,6 +1386,32 @@ static void launch_gu1(int hs, int groute, int gshared, hipStream_t stream, cons
   else if (hs <= 32) MX_GU1(32, false);
   else MX_GU1(40, false);
 #undef MX_GU1
+}
+
+// gate/up for T > 1 and the down projection for T > 1 and T = 1, with the
+// expert list's capacity chosen from E
+template <int NS, bool EX>
+static void launch_gu_decode(dim3 grid, size_t lds, hipStream_t stream, const FfnArgs& a, uint8_t* qws, uint8_t* qsc,
+                             float* h, int Tk, int R) {
+  if (a.E <= 256) hipLaunchKernelGGL((gu_decode_kernel<NS, EX, 4>), grid, dim3(256), lds, stream, a, qws, qsc, h, Tk, R);
+  else hipLaunchKernelGGL((gu_decode_kernel<NS, EX, 16>), grid, dim3(256), lds, stream, a, qws, qsc, h, Tk, R);
+}
+template <int NS>
+static void launch_down_decode(dim3 grid, hipStream_t stream, const FfnArgs& a, const uint8_t* qws,
+                               const uint8_t* qsc, float* o, int Tk) {
+  if (a.E <= 256) hipLaunchKernelGGL((down_decode_kernel<NS, 4>), grid, dim3(256), 0, stream, a, qws, qsc, o, Tk);
+  else hipLaunchKernelGGL((down_decode_kernel<NS, 16>), grid, dim3(256), 0, stream, a, qws, qsc, o, Tk);
+}
+template <int NS>
+static void launch_down_combine1(dim3 grid, hipStream_t stream, const FfnArgs& a, const float* abuf, uint8_t* qws,
+                                 uint8_t* qsc, int Tk, const Shared1Args& sh, bool with_shared) {
+  if (with_shared) {
+    if (a.E <= 256) hipLaunchKernelGGL((down_combine1_kernel<NS, true, 4>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
+    else hipLaunchKernelGGL((down_combine1_kernel<NS, true, 16>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
+  } else {
+    if (a.E <= 256) hipLaunchKernelGGL((down_combine1_kernel<NS, false, 4>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
+    else hipLaunchKernelGGL((down_combine1_kernel<NS, false, 16>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
+  }
 }
 
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
@@ -1400,9 +1439,8 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     const int gu_grid = gu_items < cus * 2 ? gu_items : cus * 2;
     const int hs = a.H / KSTEP, is = (a.I + KSTEP - 1) / KSTEP;
     if (hs > DEC_MAX_STEPS || is > DOWN_MAX_STEPS) return hipErrorInvalidValue;   // the kernels' register arrays hold every step
-    const dim3 g0(gu_grid), b0(256);
-#define MX_GU(NS_, EX_) \
-  hipLaunchKernelGGL((gu_decode_kernel<NS_, EX_>), g0, b0, lds, stream, a, qws, qsc, h, Tk, R)
+    const dim3 g0(gu_grid);
+#define MX_GU(NS_, EX_) launch_gu_decode<NS_, EX_>(g0, lds, stream, a, qws, qsc, h, Tk, R)
     const Shared1Args shv = sh ? *sh : Shared1Args{};
     if (a.T == 1) {
       // one wavefront per (pair, 8 intermediate columns); the SwiGLU rows go
@@ -1410,11 +1448,13 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       const int items = a.k * (a.I / 8);
       const int gr = items < cus * 8 ? items : cus * 8;
       const int gs = sh ? 2 * sh->I / 16 * shared1_nparts(a.H) : 0;
-      if (!fr) launch_gu1<0, false>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
-      else if (sh && a.E <= 256) launch_gu1<4, true>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);
-      else if (sh) launch_gu1<16, true>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);
-      else if (a.E <= 256) launch_gu1<4, false>(hs, gr, 0, stream, a, o, h, Tk, *fr, shv);
-      else launch_gu1<16, false>(hs, gr, 0, stream, a, o, h, Tk, *fr, shv);
+      // (the fused gate ranks the logits itself: the expert list is unused there)
+      if (!fr && a.E <= 256) launch_gu1<0, false, 4>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
+      else if (!fr) launch_gu1<0, false, 16>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
+      else if (sh && a.E <= 256) launch_gu1<4, true, 4>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);
+      else if (sh) launch_gu1<16, true, 4>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);
+      else if (a.E <= 256) launch_gu1<4, false, 4>(hs, gr, 0, stream, a, o, h, Tk, *fr, shv);
+      else launch_gu1<16, false, 4>(hs, gr, 0, stream, a, o, h, Tk, *fr, shv);
     } else {
       if (hs == 32) MX_GU(32, true);
       else if (hs == 40) MX_GU(40, true);
@@ -1429,10 +1469,8 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
 #undef MX_GU
     phase(1, stream);
     if (a.T == 1) {
-      const dim3 g1(a.H / 16 * (sh ? 2 : 1)), b1(256);        // the shared expert's down tiles after the routed ones
-#define MX_DC1(NS_)                                                                                    \
-  if (sh) hipLaunchKernelGGL((down_combine1_kernel<NS_, true>), g1, b1, 0, stream, a, o, qws, qsc, Tk, shv); \
-  else hipLaunchKernelGGL((down_combine1_kernel<NS_, false>), g1, b1, 0, stream, a, o, qws, qsc, Tk, shv)
+      const dim3 g1(a.H / 16 * (sh ? 2 : 1));                   // the shared expert's down tiles after the routed ones
+#define MX_DC1(NS_) launch_down_combine1<NS_>(g1, stream, a, o, qws, qsc, Tk, shv, sh != nullptr)
       if (is <= 2) { MX_DC1(2); }
       else if (is <= 5) { MX_DC1(5); }
       else if (is <= 8) { MX_DC1(8); }
@@ -1446,11 +1484,11 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
     }
     const int dn_items = max_active * (a.H / 128);
     const int dn_occ = DN_WG_PER_CU(is <= 2 ? 2 : is <= 5 ? 5 : is <= 8 ? 8 : 16);
-    const dim3 g2(dn_items < cus * dn_occ ? dn_items : cus * dn_occ), b2(256);
-    if (is <= 2) hipLaunchKernelGGL(down_decode_kernel<2>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
-    else if (is <= 5) hipLaunchKernelGGL(down_decode_kernel<5>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
-    else if (is <= 8) hipLaunchKernelGGL(down_decode_kernel<8>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
-    else hipLaunchKernelGGL(down_decode_kernel<16>, g2, b2, 0, stream, a, qws, qsc, o, Tk);
+    const dim3 g2(dn_items < cus * dn_occ ? dn_items : cus * dn_occ);
+    if (is <= 2) launch_down_decode<2>(g2, stream, a, qws, qsc, o, Tk);
+    else if (is <= 5) launch_down_decode<5>(g2, stream, a, qws, qsc, o, Tk);
+    else if (is <= 8) launch_down_decode<8>(g2, stream, a, qws, qsc, o, Tk);
+    else launch_down_decode<16>(g2, stream, a, qws, qsc, o, Tk);
     *variant = "ffn:gu_decode+down_decode+combine";
     phase(2, stream);
   } else {
