@@ -593,17 +593,20 @@ __device__ void stage_q_rows(const uint8_t* __restrict__ qws, const uint8_t* __r
   }
 }
 
-// Workgroups per CU of the persistent down kernel: three while its registers
-// allow (measured at the verification batch: 39 us against 43 us with two;
-// one workgroup per item instead of a persistent grid: 70 us)
-#define DN_WG_PER_CU(NS) ((NS) <= 5 ? 3 : 2)
+// Workgroups per CU of the persistent down kernel: as many as its registers
+// allow, four at I <= 640 with the four-entry expert list (128 VGPRs), else
+// three, or two at I > 640 (measured at the verification batch: with the
+// 16-entry list three took 39 us against 43 us with two; with the four-entry
+// list four took 97.2 us per FFN call against 98.4 us with three; one
+// workgroup per item instead of a persistent grid: 70 us)
+#define DN_WG_PER_CU(NS, EPL) ((NS) <= 5 ? ((EPL) == 4 ? 4 : 3) : 2)
 
 // Down: one workgroup per (expert, 128 W2 rows), 32 rows (two 16-row tiles)
 // per wavefront.  W2 first (NS >= I / 128 steps in registers), then the
 // expert's intermediate rows, 16 per pass, from the workspace into LDS;
 // writes o.
 template <int NS, int EPL>
-__global__ __launch_bounds__(256, DN_WG_PER_CU(NS)) void down_decode_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
+__global__ __launch_bounds__(256, DN_WG_PER_CU(NS, EPL)) void down_decode_kernel(FfnArgs a, const uint8_t* __restrict__ qws,
                                                              const uint8_t* __restrict__ qsc_ws,
                                                              float* __restrict__ o, int Tk) {
   __shared__ __attribute__((aligned(16))) uint8_t qlds[DN_ROWS][MAX_I + 16];
@@ -1393,23 +1396,23 @@ static void launch_gu1(int hs, int groute, int gshared, hipStream_t stream, cons
 template <int NS, bool EX>
 static void launch_gu_decode(dim3 grid, size_t lds, hipStream_t stream, const FfnArgs& a, uint8_t* qws, uint8_t* qsc,
                              float* h, int Tk, int R) {
-  if (a.E <= 256) hipLaunchKernelGGL((gu_decode_kernel<NS, EX, 4>), grid, dim3(256), lds, stream, a, qws, qsc, h, Tk, R);
+  if (epl_for(a.E) == 4) hipLaunchKernelGGL((gu_decode_kernel<NS, EX, 4>), grid, dim3(256), lds, stream, a, qws, qsc, h, Tk, R);
   else hipLaunchKernelGGL((gu_decode_kernel<NS, EX, 16>), grid, dim3(256), lds, stream, a, qws, qsc, h, Tk, R);
 }
 template <int NS>
 static void launch_down_decode(dim3 grid, hipStream_t stream, const FfnArgs& a, const uint8_t* qws,
                                const uint8_t* qsc, float* o, int Tk) {
-  if (a.E <= 256) hipLaunchKernelGGL((down_decode_kernel<NS, 4>), grid, dim3(256), 0, stream, a, qws, qsc, o, Tk);
+  if (epl_for(a.E) == 4) hipLaunchKernelGGL((down_decode_kernel<NS, 4>), grid, dim3(256), 0, stream, a, qws, qsc, o, Tk);
   else hipLaunchKernelGGL((down_decode_kernel<NS, 16>), grid, dim3(256), 0, stream, a, qws, qsc, o, Tk);
 }
 template <int NS>
 static void launch_down_combine1(dim3 grid, hipStream_t stream, const FfnArgs& a, const float* abuf, uint8_t* qws,
                                  uint8_t* qsc, int Tk, const Shared1Args& sh, bool with_shared) {
   if (with_shared) {
-    if (a.E <= 256) hipLaunchKernelGGL((down_combine1_kernel<NS, true, 4>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
+    if (epl_for(a.E) == 4) hipLaunchKernelGGL((down_combine1_kernel<NS, true, 4>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
     else hipLaunchKernelGGL((down_combine1_kernel<NS, true, 16>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
   } else {
-    if (a.E <= 256) hipLaunchKernelGGL((down_combine1_kernel<NS, false, 4>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
+    if (epl_for(a.E) == 4) hipLaunchKernelGGL((down_combine1_kernel<NS, false, 4>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
     else hipLaunchKernelGGL((down_combine1_kernel<NS, false, 16>), grid, dim3(256), 0, stream, a, abuf, qws, qsc, Tk, sh);
   }
 }
@@ -1449,7 +1452,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       const int gr = items < cus * 8 ? items : cus * 8;
       const int gs = sh ? 2 * sh->I / 16 * shared1_nparts(a.H) : 0;
       // (the fused gate ranks the logits itself: the expert list is unused there)
-      if (!fr && a.E <= 256) launch_gu1<0, false, 4>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
+      if (!fr && epl_for(a.E) == 4) launch_gu1<0, false, 4>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
       else if (!fr) launch_gu1<0, false, 16>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
       else if (sh && a.E <= 256) launch_gu1<4, true, 4>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);
       else if (sh) launch_gu1<16, true, 4>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);
@@ -1483,7 +1486,7 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       return hipGetLastError();
     }
     const int dn_items = max_active * (a.H / 128);
-    const int dn_occ = DN_WG_PER_CU(is <= 2 ? 2 : is <= 5 ? 5 : is <= 8 ? 8 : 16);
+    const int dn_occ = DN_WG_PER_CU(is <= 2 ? 2 : is <= 5 ? 5 : is <= 8 ? 8 : 16, epl_for(a.E));
     const dim3 g2(dn_items < cus * dn_occ ? dn_items : cus * dn_occ);
     if (is <= 2) launch_down_decode<2>(g2, stream, a, qws, qsc, o, Tk);
     else if (is <= 5) launch_down_decode<5>(g2, stream, a, qws, qsc, o, Tk);
