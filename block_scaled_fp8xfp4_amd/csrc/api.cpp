@@ -171,8 +171,8 @@ mx_status moe_expert_ffn(const uint8_t* x, const uint8_t* x_sc, int T, int H, co
   if (!x || !x_sc || !topk_w || !expert_offsets || !perm || !slot_pos || !w13 || !w13_sc || !w2 || !w2_sc || !y)
     return MX_EINVAL;
   if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(x_sc, 4) ||
-      !aligned(w13_sc, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) || !aligned(perm, 4) ||
-      !aligned(slot_pos, 4))
+      !aligned(w13_sc, 4) || !aligned(w2_sc, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(perm, 4) || !aligned(slot_pos, 4))
     return MX_EINVAL;
   // the kernels of the requested path (automatic: either path) must support (H, I): never a silent fallback
   const int path = mx::ffn_resolve_path(g_ffn_path.load(), (int64_t)T * k, H, I);
@@ -201,8 +201,8 @@ mx_status moe_expert_ffn_noalloc(const uint8_t* x, const uint8_t* x_sc, int T, i
   if (!x || !x_sc || !topk_w || !expert_offsets || !perm || !slot_pos || !w13 || !w13_sc || !w2 || !w2_sc || !y)
     return MX_EINVAL;
   if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(y, 16) || !aligned(x_sc, 4) ||
-      !aligned(w13_sc, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) || !aligned(perm, 4) ||
-      !aligned(slot_pos, 4))
+      !aligned(w13_sc, 4) || !aligned(w2_sc, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(perm, 4) || !aligned(slot_pos, 4))
     return MX_EINVAL;
   const int path = mx::ffn_resolve_path(g_ffn_path.load(), (int64_t)T * k, H, I);
   if (path == 0) return MX_EUNSUPPORTED;
@@ -233,8 +233,8 @@ mx_status moe_layer_decode1(const float* logits, int E, int k, const float* surv
       !perm || !slot_pos || !y)
     return MX_EINVAL;
   if (!aligned(logits, 4) || !aligned(survival, 4) || !aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
-      !aligned(y, 16) || !aligned(x_sc, 4) || !aligned(w13_sc, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
-      !aligned(expert_offsets, 4) || !aligned(perm, 4) || !aligned(slot_pos, 4))
+      !aligned(y, 16) || !aligned(x_sc, 4) || !aligned(w13_sc, 4) || !aligned(w2_sc, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(expert_offsets, 4) || !aligned(perm, 4) || !aligned(slot_pos, 4))
     return MX_EINVAL;
   if (!ws || ws_bytes < mx::ffn_ws_bytes(1, H, E, I, k) || !diag_h_fits(k, I)) return MX_EWORKSPACE;
   if (!aligned(ws, 256)) return MX_EINVAL;
@@ -269,9 +269,9 @@ mx_status moe_layer_decode1_shared(const float* logits, int E, int k, const floa
       !topk_ids || !topk_w || !expert_offsets || !perm || !slot_pos || !y || !y_shared)
     return MX_EINVAL;
   if (!aligned(logits, 4) || !aligned(survival, 4) || !aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
-      !aligned(y, 16) || !aligned(x_sc, 4) || !aligned(w13_sc, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
-      !aligned(expert_offsets, 4) || !aligned(perm, 4) || !aligned(slot_pos, 4) || !aligned(sw13, 16) ||
-      !aligned(sw2, 16) || !aligned(sw13_sc, 4) || !aligned(sw2_sc, 4) || !aligned(y_shared, 4))
+      !aligned(y, 16) || !aligned(x_sc, 4) || !aligned(w13_sc, 4) || !aligned(w2_sc, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(expert_offsets, 4) || !aligned(perm, 4) || !aligned(slot_pos, 4) ||
+      !aligned(sw13, 16) || !aligned(sw2, 16) || !aligned(sw13_sc, 4) || !aligned(sw2_sc, 4) || !aligned(y_shared, 4))
     return MX_EINVAL;
   const size_t rws = layer1_routed_ws(H, E, I, k);
   if (!ws || ws_bytes < rws + mx::shared_ws_bytes(1, H, Is) || !diag_h_fits(k, I)) return MX_EWORKSPACE;

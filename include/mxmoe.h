@@ -165,6 +165,7 @@ mx_status moe_route(const float* logits, int T, int E, int k,
  * x      FP8 [T][H],  x_sc  SC [T][H/32]          activations
  * w13    FP4 [E][2I][H/2], w13_sc SC [E][2I][H/32] rows [0, I) gate, [I, 2I) up
  * w2     FP4 [E][H][I/2],  w2_sc  SC [E][H][I/32]  down projection
+ *        (x, w13, w2 and y 16-byte aligned; x_sc, w13_sc, w2_sc 4-byte)
  * topk_w, expert_offsets, perm, slot_pos: as written by moe_route (k slots).
  * y      fp32 [T][H]: y_t = sum_{j=0..k-1} w_tj * o_tj, added in slot order,
  *        where o_tj = down(requant_fp8(silu(gate) * up)) of pair (t, j);

@@ -103,8 +103,8 @@ def test_route_live_rejects_bad_arguments(lib):
     assert route_live(lib, T=8192, E=256, k=8, ws_bytes=100) == mxmoe.MX_EWORKSPACE
 
 
-def ffn(lib, T=4, H=256, E=8, I=64, k=2, ws=FAKE_WS, ws_bytes=1 << 34, x=FAKE, w13=FAKE):
-    return lib.moe_expert_ffn(x, FAKE, T, H, FAKE, FAKE, FAKE, FAKE, k, w13, FAKE, FAKE, FAKE, E, I, FAKE,
+def ffn(lib, T=4, H=256, E=8, I=64, k=2, ws=FAKE_WS, ws_bytes=1 << 34, x=FAKE, w13=FAKE, w2_sc=FAKE):
+    return lib.moe_expert_ffn(x, FAKE, T, H, FAKE, FAKE, FAKE, FAKE, k, w13, FAKE, FAKE, w2_sc, E, I, FAKE,
                               ws, ws_bytes, None)
 
 
@@ -118,6 +118,7 @@ def test_ffn_rejects_bad_arguments(lib):
     assert ffn(lib, I=4096) == mxmoe.MX_EUNSUPPORTED                            # I > 2048
     assert ffn(lib, x=None) == mxmoe.MX_EINVAL
     assert ffn(lib, w13=ctypes.c_void_p((1 << 20) + 8)) == mxmoe.MX_EINVAL      # alignment
+    assert ffn(lib, w2_sc=ctypes.c_void_p((1 << 20) + 2)) == mxmoe.MX_EINVAL    # scale rows are read as dwords
     assert ffn(lib, ws=None) == mxmoe.MX_EWORKSPACE
     assert ffn(lib, ws_bytes=1000) == mxmoe.MX_EWORKSPACE
     assert ffn(lib, E=0) == mxmoe.MX_EINVAL
@@ -155,8 +156,8 @@ def test_ffn_forced_path_rejects_what_that_path_lacks(lib):
         mxmoe.set_ffn_path(old)
 
 
-def layer1(lib, H=256, I=64, E=8, k=2, ws=FAKE_WS, ws_bytes=1 << 30):
-    return lib.moe_layer_decode1(FAKE, E, k, None, 0.2, FAKE, FAKE, H, FAKE, FAKE, FAKE, FAKE, I, FAKE, FAKE, FAKE,
+def layer1(lib, H=256, I=64, E=8, k=2, ws=FAKE_WS, ws_bytes=1 << 30, w2_sc=FAKE):
+    return lib.moe_layer_decode1(FAKE, E, k, None, 0.2, FAKE, FAKE, H, FAKE, FAKE, FAKE, w2_sc, I, FAKE, FAKE, FAKE,
                                  FAKE, FAKE, FAKE, ws, ws_bytes, None)
 
 
@@ -164,6 +165,7 @@ def test_layer_decode1_rejects_bad_arguments(lib):
     assert layer1(lib, k=0) == mxmoe.MX_EINVAL
     assert layer1(lib, k=9, E=8) == mxmoe.MX_EINVAL
     assert layer1(lib, H=320) == mxmoe.MX_EUNSUPPORTED
+    assert layer1(lib, w2_sc=ctypes.c_void_p((1 << 20) + 1)) == mxmoe.MX_EINVAL
     assert layer1(lib, ws=None) == mxmoe.MX_EWORKSPACE
 
 
