@@ -60,6 +60,13 @@ int mx_set_ffn_path(int path) {
   return g_ffn_path.exchange(path);
 }
 
+int mx_set_layer1_single_launch(int on) {
+  if (on != 0 && on != 1) return MX_EINVAL;
+  static std::atomic<int> cur{1};
+  mx::set_layer1_onepass(on == 1);
+  return cur.exchange(on);
+}
+
 mx_status mx_quantize(const void* src, int src_dtype, int64_t rows, int64_t cols, int fmt, uint8_t* q, uint8_t* sc,
                       void* stream) {
   if (!src || !q || !sc) return MX_EINVAL;

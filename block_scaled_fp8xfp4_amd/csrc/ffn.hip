@@ -48,6 +48,7 @@
 //   shares weights and activations in its own L2.
 // combine_kernel adds w_tj * o_tj over the slots in order j = 0..k-1.
 #include <atomic>
+#include <chrono>
 
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
@@ -827,6 +828,290 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
   }
 }
 
+// ------------------------------------------------ single-launch layer (T = 1) ==
+// moe_layer_decode1 in one launch: gate/up workgroups (one per slot and block
+// of 32 intermediate columns, four wavefronts of 8 columns each: the
+// gu1_kernel tile per wavefront) and down + combine workgroups (32 output
+// columns each, two slots per wavefront) in one grid.  A gate/up workgroup
+// requantizes its block itself (the block is whole in the workgroup) and
+// hands the 32 E4M3 codes and the E8M0 code to every down workgroup through
+// the workspace: nine 8-byte words, each four payload bytes and the call's
+// 32-bit tag, written by 64-bit system-scope stores (they reach memory whole).
+// A down wavefront reads a slot's words with system-scope loads (which read
+// memory, never a stale cached copy) until every word carries the tag.  Tags are unique per call in the process, so
+// words of earlier calls, or garbage in a fresh workspace, never match and
+// nothing has to be cleared.  Gate/up workgroups have lower indices than down
+// workgroups and never wait, so they are dispatched first; every wait is
+// bounded in wall-clock time (a down workgroup whose time runs out sets bit 0
+// of *status, and that call's result is undefined).
+struct Handoff {
+  uint64_t* words;                                              // [k][I/32][9] (payload, tag) words
+  uint32_t* status;                                             // bit 0: a wait ran past its limit
+  uint32_t tag;                                                 // this call's tag
+  long long limit;                                              // wall-clock ticks one down workgroup may wait
+  int nprod;                                                    // gate/up workgroups: k * I / 32
+};
+constexpr int L1_HWORDS = 9;                                    // words per block: 8 x four codes, 1 x scale code
+// words per slot: I / 32 blocks of nine, padded to an even count (whole 16-byte reads)
+__host__ __device__ constexpr int l1_slot_words(int I) { return ((I / 32) * L1_HWORDS + 1) & ~1; }
+
+// Gate/up of one block of 32 intermediate columns of slot j: wavefront w
+// computes columns [32 b + 8 w, +8) exactly as gu1_kernel's item does (the
+// fused gate's top-k in every wavefront; 8 gate + 8 up weight rows per
+// MFMA tile), then wavefront 0 requantizes the 32 SwiGLU values (block
+// maximum, E8M0 code, E4M3 codes: the requant routine of every path) and
+// publishes them; it also writes q, its scale, the fp32 SwiGLU row values
+// and (workgroup 0) the route outputs, as the two-launch path does.
+template <int NS, bool EXACT, int RP>
+__device__ void layer1_gate_up(const FfnArgs& a, float* __restrict__ abuf, float* __restrict__ h,
+                               uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws, const FusedRoute& fr,
+                               const Handoff& ho) {
+  __shared__ __attribute__((aligned(16))) uint8_t xl[NS * KSTEP];
+  __shared__ uint32_t xs[NS];
+  __shared__ uint32_t bsc[4][16 * (NS + 1)];                    // per wavefront: [row][step] scale dwords
+  __shared__ float sw[32];
+  __shared__ __attribute__((aligned(16))) uint8_t qb[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int H = EXACT ? NS * KSTEP : a.H, I = a.I, nb = I / 32;
+  const int nsteps = H / KSTEP, chunks = H / 16, spitch = nsteps | 1;
+  constexpr int XPT = (NS * 8 + 63) / 64;                       // 16-byte activation chunks per lane
+  u32x4 xv[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = lane + 64 * i;
+    xv[i] = (EXACT || c < chunks) ? ldg16(a.x + c * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const uint32_t xsv = lane < nsteps ? reinterpret_cast<const uint32_t*>(a.x_sc)[lane] : 0x7F7F7F7Fu;
+  const float sv = fr.survival != nullptr ? fr.survival[0] : 1.0f;   // in flight with the logits
+  TopkState<RP> st;
+  topk_begin<RP>(st, fr.logits, a.E);
+  const bool live = fr.survival == nullptr || !(sv < fr.skip_below);
+  const int j = (int)blockIdx.x / nb, b = (int)blockIdx.x % nb;
+  const int c0 = 32 * b + 8 * wave;                             // this wavefront's first intermediate column
+  int p0 = 0;                                                   // the pair's bucket position
+  if (live) {                                                   // workgroup-uniform
+    // every wavefront stages the whole activation row itself (the same bytes)
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = lane + 64 * i;
+      if (EXACT || c < chunks) *reinterpret_cast<u32x4*>(xl + c * 16) = xv[i];
+    }
+    if (lane < nsteps) xs[lane] = xsv;
+    topk_rounds<RP>(st, j + 1);
+    const int e = __builtin_amdgcn_readlane(st.idx, j);
+    const int64_t ebase = (int64_t)e * 2 * I;
+    const int64_t wrow = ebase + (col < 8 ? c0 + col : I + c0 + col - 8);
+    constexpr int NBSV = (16 * NS + 63) / 64;
+    uint32_t bsv[NBSV];
+#pragma unroll
+    for (int i = 0; i < NBSV; ++i) {
+      const int idx = lane + 64 * i, r = idx / nsteps, sidx = idx % nsteps;
+      const int64_t sr = ebase + (r < 8 ? c0 + r : I + c0 + r - 8);
+      bsv[i] = idx < 16 * nsteps ? reinterpret_cast<const uint32_t*>(a.w13_sc + sr * (H / 32))[sidx] : 0u;
+    }
+    const uint8_t* wp = a.w13 + wrow * (H / 2) + g * 16;
+    u32x4 bw[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) bw[s] = ldg16(wp + (EXACT || s < nsteps ? s : nsteps - 1) * 64);
+    topk_rounds<RP>(st, a.k);                                   // the other slots, while the weights stream in
+    for (int i = 0; i < a.k; ++i) p0 += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
+    uint32_t* bscw = bsc[wave];
+#pragma unroll
+    for (int i = 0; i < NBSV; ++i) {
+      const int idx = lane + 64 * i;
+      if (idx < 16 * nsteps) bscw[(idx / nsteps) * spitch + idx % nsteps] = bsv[i];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                         // lgkmcnt(0): this wavefront's LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    const uint8_t* arow = xl + g * 16;
+    const uint32_t* bsrow = &bscw[col * spitch];
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (EXACT || s < nsteps) {
+        const u32x4 alo = *reinterpret_cast<const u32x4*>(arow + s * KSTEP);
+        const u32x4 ahi = *reinterpret_cast<const u32x4*>(arow + s * KSTEP + 64);
+        acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand(bw[s]), acc, xs[s] >> (8 * g), bsrow[s] >> (8 * g));
+      }
+    }
+    const float up = __shfl_down(acc[0], 8, 16);                // gate values in lanes 0..7, up values in 8..15
+    if (h != nullptr && lane < 16)                              // diagnostics only
+      h[(int64_t)p0 * 2 * I + (col < 8 ? c0 + col : I + c0 + col - 8)] = acc[0];
+    if (lane < 8) {
+      const float av = swiglu(acc[0], up);
+      abuf[(int64_t)j * I + c0 + lane] = av;                    // the SwiGLU rows of the workspace's layout
+      sw[8 * wave + lane] = av;
+    }
+    lds_barrier();
+    if (wave == 0) {
+      const float v = lane < 32 ? sw[lane] : 0.f;
+      float m = row16_max(__builtin_fabsf(v));
+      m = fmaxf(m, __shfl_xor(m, 16));                          // lanes 0..31: the block maximum
+      const uint32_t sc = e8m0_code_for_amax(m, 8);
+      if (lane < 32) qb[lane] = (uint8_t)(requant2_e4m3(v, 0.f, sc) & 0xFFu);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+      if (lane < L1_HWORDS) {
+        const uint32_t pay = lane < 8 ? reinterpret_cast<const uint32_t*>(qb)[lane] : sc;
+        __hip_atomic_store(ho.words + (int64_t)j * l1_slot_words(I) + b * L1_HWORDS + lane, (uint64_t)pay | ((uint64_t)ho.tag << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (lane < 8) reinterpret_cast<uint32_t*>(qws + (int64_t)p0 * I + 32 * b)[lane] = pay;
+        else qsc_ws[(int64_t)p0 * nb + b] = (uint8_t)sc;
+      }
+    }
+  }
+  if (blockIdx.x == 0 && wave == 0) {                           // the route outputs, as the single-row route kernel
+    topk_rounds<RP>(st, a.k);
+    int rrank = 0;
+    for (int i = 0; i < a.k; ++i) rrank += __builtin_amdgcn_readlane(st.idx, i) < st.idx ? 1 : 0;
+    const float wt = slot_weight(st.val, a.k);
+    if (lane < a.k) {
+      fr.ids[lane] = st.idx;
+      fr.w[lane] = wt;
+      fr.slot_pos[lane] = live ? rrank : -1;
+      fr.perm[live ? rrank : lane] = live ? lane : -1;
+    }
+    for (int e = lane; e <= a.E; e += 64) {
+      int below = 0;
+      for (int i = 0; i < a.k; ++i) below += __builtin_amdgcn_readlane(st.idx, i) < e ? 1 : 0;
+      fr.offsets[e] = live ? below : 0;
+    }
+  }
+}
+
+// Down projection + combine of L1_COLS output columns (L1_COLS / 16 tiles):
+// wavefront w takes slots w and w + 4.  It ranks the logits itself, issues
+// each slot's W2 rows as soon as the slot's round has named the expert, then
+// waits for the slots' codes (both slots' words in one round of reads),
+// copies them into LDS and runs the slot's chains (down_combine1_kernel's
+// chain: K past I zero, blocks past I / 32 scale 127).  Wavefront 0 adds the
+// k products in slot order.  k <= 8, I <= NSD * 128.  (Measured at the
+// decode shape: one 16-column tile per workgroup, 12.6 us per call; two
+// tiles, half as many workgroups, 14.4-14.9 us.)
+constexpr int L1_COLS = 16;
+template <int NSD, int RP>
+__device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handoff& ho, int tile) {
+  constexpr int QP = NSD * KSTEP + 16;
+  constexpr int CT = L1_COLS / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t q1[8][QP];
+  __shared__ uint8_t s1[8][NSD * 4];
+  __shared__ float olds[8][L1_COLS];
+  const uint64_t t0 = wall_clock64();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int H = a.H, I = a.I, nb = I / 32, k = a.k;
+  const int nsteps = (I + KSTEP - 1) / KSTEP;
+  const float sv = fr.survival != nullptr ? fr.survival[0] : 1.0f;
+  TopkState<RP> st;
+  topk_begin<RP>(st, fr.logits, a.E);
+  const bool live = fr.survival == nullptr || !(sv < fr.skip_below);
+  if (!live) {                                                  // no bucket: +0 (workgroup-uniform exit)
+    if (tid < L1_COLS) a.y[tile * L1_COLS + tid] = 0.f;
+    return;
+  }
+  u32x4 bw[2][CT][NSD];
+  uint32_t bs[2][CT][NSD];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {                                 // branch-free: a slot past k reloads slot k - 1's rows
+    const int jj = min(wave + 4 * u, k - 1);
+    topk_rounds<RP>(st, jj + 1);
+    const int64_t r0 = (int64_t)__builtin_amdgcn_readlane(st.idx, jj) * H + tile * L1_COLS + col;
+#pragma unroll
+    for (int t = 0; t < CT; ++t) load_w2_tile<NSD>(a.w2, a.w2_sc, r0 + 16 * t, I, g, bw[u][t], bs[u][t]);
+  }
+  topk_rounds<RP>(st, k);
+  const float wt = slot_weight(st.val, k);                      // lane j: the weight of slot j
+  for (int idx = lane; idx < 2 * (QP - I); idx += 64) {         // this wavefront's rows: K past I reads zeros
+    const int jj = wave + 4 * (idx / (QP - I));
+    q1[jj][I + idx % (QP - I)] = 0;
+  }
+  for (int idx = lane; idx < 2 * (NSD * 4 - nb); idx += 64)
+    s1[wave + 4 * (idx / (NSD * 4 - nb))][nb + idx % (NSD * 4 - nb)] = 127;
+  // the slots' words, coalesced: a slot's I / 32 * 9 words (<= 180, padded
+  // to an even count so that no 16-byte read straddles the end of the range)
+  // are read as 16-byte chunks, lane l holding words 2 l, 2 l + 1 and
+  // 128 + 2 l, 129 + 2 l; word i is part i % 9 of block i / 9 (parts 0..7:
+  // four codes, part 8: the scale code)
+  const int nwords = nb * L1_HWORDS, nwp = l1_slot_words(I);
+  uint32_t pending = (wave < k ? 1u : 0u) | (wave + 4 < k ? 2u : 0u);
+  while (pending) {
+    u32x4 v[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t bytes = (pending >> u) & 1u ? (uint32_t)nwp * 8u : 0u;   // 0: reads nothing
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(ho.words + (int64_t)(wave + 4 * u) * nwp), (short)0, bytes, 0x00020000);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) v[u][h] = __builtin_amdgcn_raw_buffer_load_b128(r, (128 * h + 2 * lane) * 8, 0, 17);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if ((pending >> u) & 1u) {                                // wavefront-uniform
+        bool ok = true;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            ok = ok && (128 * h + 2 * lane + e >= nwords || v[u][h][2 * e + 1] == ho.tag);
+        if (__ballot(ok) == ~0ull) {
+          const int jj = wave + 4 * u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int wi = 128 * h + 2 * lane + e, blk = wi / L1_HWORDS, part = wi % L1_HWORDS;
+              if (wi < nwords) {
+                if (part < 8) *reinterpret_cast<uint32_t*>(&q1[jj][32 * blk + 4 * part]) = v[u][h][2 * e];
+                else s1[jj][blk] = (uint8_t)v[u][h][2 * e];
+              }
+            }
+          __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0): the row is in LDS
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int t = 0; t < CT; ++t) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NSD; ++s) {
+              if (s < nsteps) {
+                const int klo = s * KSTEP + g * 16;
+                const bool bv = 4 * s + g < nb;
+                const u32x4 alo = *reinterpret_cast<const u32x4*>(&q1[jj][klo]);
+                const u32x4 ahi = *reinterpret_cast<const u32x4*>(&q1[jj][klo + 64]);
+                acc = mfma_fp8_fp4(fp8_operand(alo, ahi), fp4_operand_masked(bw[u][t][s], bv), acc,
+                                   s1[jj][4 * s + g], bs[u][t][s]);
+              }
+            }
+            if (g == 0) olds[jj][16 * t + col] = acc[0];        // row 0 of the tile
+          }
+          pending &= ~(1u << u);
+        }
+      }
+    }
+    if (pending == 0) break;
+    if ((long long)(wall_clock64() - t0) > ho.limit) {
+      if (lane == 0) __hip_atomic_fetch_or(ho.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  lds_barrier();
+  if (wave == 0) {
+    float acc = 0.f;
+    for (int jj = 0; jj < k; ++jj)
+      acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), jj)), olds[jj][lane & (L1_COLS - 1)], acc);
+    if (lane < L1_COLS) a.y[tile * L1_COLS + lane] = acc;
+  }
+}
+
+template <int NS, bool EXACT, int RP, int NSD>
+__global__ __launch_bounds__(256) void layer1_kernel(FfnArgs a, float* __restrict__ abuf, float* __restrict__ h,
+                                                     uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws,
+                                                     FusedRoute fr, Handoff ho) {
+  if ((int)blockIdx.x >= ho.nprod) layer1_down<NSD, RP>(a, fr, ho, (int)blockIdx.x - ho.nprod);
+  else layer1_gate_up<NS, EXACT, RP>(a, abuf, h, qws, qsc_ws, fr, ho);
+}
+
 // ========================================================== prefill path ==
 // (measured: 256-row tiles, eight wavefronts and one workgroup per CU, which
 // halve the weight re-reads, ran at 505-539 us against 474 us, bitwise equal)
@@ -1330,7 +1615,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // ================================================================= host ===
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-// workspace: [q: Tk*I][q_sc: Tk*I/32][o: Tk*H fp32][queue counters][scratch row], each 256-byte aligned
+// workspace: [q: Tk*I][q_sc: Tk*I/32][o: Tk*H fp32][queue counters][scratch row][T = 1: handoff words],
+// each 256-byte aligned
 void ffn_ws_layout(int T, int H, int I, int k, size_t* off_q, size_t* off_q_sc, size_t* off_o) {
   const size_t Tk = (size_t)T * k;
   *off_q = 0;
@@ -1343,8 +1629,11 @@ size_t ffn_ws_bytes(int T, int H, int E, int I, int k) {
   (void)E;
   size_t q, qs, o;
   ffn_ws_layout(T, H, I, k, &q, &qs, &o);
-  // o holds T*k rows of H floats (per-slot outputs) or, at T = 1, of I floats (the SwiGLU rows)
-  return o + align256((size_t)T * k * (H > I ? H : I) * 4) + 256 + 256;   // + work-queue counters + a scratch row
+  // o holds T*k rows of H floats (per-slot outputs) or, at T = 1, of I floats (the SwiGLU rows);
+  // then the work-queue counters (at T = 1: the handoff status word), a scratch row and, at T = 1,
+  // the single-launch layer's handoff words (nine 8-byte words per block of 32 intermediate values)
+  return o + align256((size_t)T * k * (H > I ? H : I) * 4) + 256 + 256 +
+         (T == 1 ? align256((size_t)k * l1_slot_words(I) * 8) : 0);
 }
 
 // Row pairs at or below which the decode kernels are chosen.
@@ -1389,6 +1678,56 @@ static void launch_gu1(int hs, int groute, int gshared, hipStream_t stream, cons
   else if (hs <= 32) MX_GU1(32, false);
   else MX_GU1(40, false);
 #undef MX_GU1
+}
+
+// The single-launch layer of one row: k * I / 32 gate/up workgroups and
+// H / 32 down + combine workgroups in one grid.
+template <int RP, int NSD>
+static void launch_layer1(int hs, hipStream_t stream, const FfnArgs& a, float* abuf, float* h, uint8_t* qws,
+                          uint8_t* qsc, const FusedRoute& fr, const Handoff& ho) {
+  const dim3 grid(ho.nprod + a.H / L1_COLS);
+#define MX_L1(NS_, EX_) \
+  hipLaunchKernelGGL((layer1_kernel<NS_, EX_, RP, NSD>), grid, dim3(256), 0, stream, a, abuf, h, qws, qsc, fr, ho)
+  if (hs == 32) MX_L1(32, true);
+  else if (hs == 40) MX_L1(40, true);
+  else if (hs == 16) MX_L1(16, true);
+  else if (hs == 8) MX_L1(8, true);
+  else if (hs <= 4) MX_L1(4, false);
+  else if (hs <= 8) MX_L1(8, false);
+  else if (hs <= 16) MX_L1(16, false);
+  else if (hs <= 32) MX_L1(32, false);
+  else MX_L1(40, false);
+#undef MX_L1
+}
+
+static std::atomic<bool> g_layer1_onepass{true};
+void set_layer1_onepass(bool on) { g_layer1_onepass.store(on); }
+
+// A tag no earlier call of this process used (a random start, then +1 per
+// call; unique over 2^32 calls).
+static uint32_t next_call_tag() {
+  static std::atomic<uint32_t> next{[] {
+    uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^ (uint64_t)(uintptr_t)&next;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;               // splitmix64 finalizer
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return (uint32_t)(z ^ (z >> 31));
+  }()};
+  return next.fetch_add(1);
+}
+
+// Wall-clock ticks in 20 ms on the current device (the limit of one consumer's waits).
+static long long handoff_limit_ticks() {
+  static std::atomic<long long> ticks_per_ms[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  long long t = ticks_per_ms[dev].load();
+  if (t == 0) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
+    t = khz;
+    ticks_per_ms[dev].store(t);
+  }
+  return 20 * t;
 }
 
 // gate/up for T > 1 and the down projection for T > 1 and T = 1, with the
@@ -1452,6 +1791,27 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       const int gr = items < cus * 8 ? items : cus * 8;
       const int gs = sh ? 2 * sh->I / 16 * shared1_nparts(a.H) : 0;
       // (the fused gate ranks the logits itself: the expert list is unused there)
+      // One launch when the down projection fits a consumer wavefront (k <= 8,
+      // I <= 640) and the stream is not being captured (a graph would replay
+      // one tag; the two-launch path below has no tags).
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (fr && !sh && a.k <= 8 && is <= 5 && g_layer1_onepass.load() &&
+          hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+        const Handoff ho{reinterpret_cast<uint64_t*>(base + oo + obytes + 512), reinterpret_cast<uint32_t*>(queue),
+                         next_call_tag(), handoff_limit_ticks(), a.k * (a.I / 32)};
+        if (is <= 2) {
+          if (a.E <= 256) launch_layer1<4, 2>(hs, stream, a, o, h, qws, qsc, *fr, ho);
+          else launch_layer1<16, 2>(hs, stream, a, o, h, qws, qsc, *fr, ho);
+        } else {
+          if (a.E <= 256) launch_layer1<4, 5>(hs, stream, a, o, h, qws, qsc, *fr, ho);
+          else launch_layer1<16, 5>(hs, stream, a, o, h, qws, qsc, *fr, ho);
+        }
+        *variant = "layer1:gate_up_topk+down_combine (one launch)";
+        phase(1, stream);
+        phase(2, stream);
+        phase(3, stream);
+        return hipGetLastError();
+      }
       if (!fr && epl_for(a.E) == 4) launch_gu1<0, false, 4>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
       else if (!fr) launch_gu1<0, false, 16>(hs, gr, 0, stream, a, o, h, Tk, FusedRoute{}, shv);
       else if (sh && a.E <= 256) launch_gu1<4, true, 4>(hs, gr, gs, stream, a, o, h, Tk, *fr, shv);

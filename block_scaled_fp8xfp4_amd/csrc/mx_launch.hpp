@@ -57,6 +57,7 @@ int ffn_resolve_path(int path, int64_t Tk, int H, int I);
 hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, const char** variant,
                       const FusedRoute* fr = nullptr, float* h = nullptr, const Shared1Args* sh = nullptr);
 void set_ffn_phase_events(const hipEvent_t* ev, int n);
+void set_layer1_onepass(bool on);
 // moe_expert_ffn_noalloc: the library's own device scratch array (per GPU,
 // NOALLOC_SCRATCH_BYTES) in place of a caller workspace; *ptr receives its
 // address on the current device.

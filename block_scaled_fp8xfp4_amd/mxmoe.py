@@ -18,7 +18,7 @@ MX_OUT_BF16, MX_OUT_F32 = 0, 1
 # every entry point declared in include/mxmoe.h
 EXPORTS = ("mx_quantize", "moe_router_logits_workspace_bytes", "moe_router_logits", "moe_route_workspace_bytes", "moe_route", "moe_route_live", "moe_expert_ffn_workspace_bytes",
            "moe_ws_layout", "moe_expert_ffn", "fp8_block_gemm", "mx_status_string",
-           "mx_last_variant", "mx_set_ffn_path", "mx_check_requant", "mx_set_phase_events",
+           "mx_last_variant", "mx_set_ffn_path", "mx_set_layer1_single_launch", "mx_check_requant", "mx_set_phase_events",
            "moe_shared_expert_workspace_bytes", "moe_shared_expert", "mx_prefetch",
            "moe_layer_decode1", "mx_set_ffn_diag", "moe_expert_ffn_noalloc", "moe_expert_ffn_noalloc_max_bytes",
            "moe_layer_decode1_shared_workspace_bytes", "moe_layer_decode1_shared")
@@ -86,6 +86,8 @@ def load():
     lib.mx_last_variant.argtypes = []
     lib.mx_set_ffn_path.restype = I32
     lib.mx_set_ffn_path.argtypes = [I32]
+    lib.mx_set_layer1_single_launch.restype = I32
+    lib.mx_set_layer1_single_launch.argtypes = [I32]
     lib.mx_check_requant.restype = I32
     lib.mx_check_requant.argtypes = [ctypes.c_uint32, ctypes.c_uint32, P, P]
     lib.mx_set_phase_events.restype = I32
@@ -100,6 +102,14 @@ def status_string(status):
 
 def last_variant():
     return load().mx_last_variant().decode()
+
+
+def set_layer1_single_launch(on):
+    """1 = moe_layer_decode1 in one launch where it applies, 0 = two launches; returns the previous setting."""
+    r = load().mx_set_layer1_single_launch(int(on))
+    if r < 0:
+        raise MXError(r, "mx_set_layer1_single_launch")
+    return r
 
 
 def set_ffn_path(path):
@@ -208,7 +218,7 @@ def moe_expert_ffn_noalloc_max_bytes():
 
 def moe_layer_decode1(logits, k, survival, skip_below, x, x_sc, w13, w13_sc, w2, w2_sc, E, I, topk_ids, topk_w,
                       expert_offsets, perm, slot_pos, y, ws, stream=None):
-    """Route + routed-expert FFN of one row (logits [1, E] or [E]) in two launches."""
+    """Route + routed-expert FFN of one row (logits [1, E] or [E]) in one launch (or two)."""
     H = x.shape[-1]
     _check(load().moe_layer_decode1(_ptr(logits), E, k, _ptr(survival), float(skip_below), _ptr(x), _ptr(x_sc), H,
                                     _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I, _ptr(topk_ids), _ptr(topk_w),

@@ -222,10 +222,21 @@ mx_status moe_expert_ffn_noalloc(const uint8_t* x, const uint8_t* x_sc, int T, i
                                  float* y, void* stream);
 
 /*
- * The routed-expert layer of ONE row in two launches: moe_route and
+ * The routed-expert layer of ONE row in one launch (or two): moe_route and
  * moe_expert_ffn for T = 1 fused, the top-k gate running inside the gate/up
  * kernel (every workgroup ranks the row's E logits itself, so the experts'
- * weight loads start without waiting for a route kernel).  Same arguments
+ * weight loads start without waiting for a route kernel).  With k <= 8,
+ * I <= 640 and a stream that is not being captured into a graph,
+ * gate/up and the down projection + combine run in ONE launch: the down
+ * workgroups stream their W2 rows while the gate/up workgroups run and take
+ * each slot's SwiGLU row from them through the workspace (the gate/up side
+ * stores a per-call tag beside it once it has reached memory; nothing in the
+ * workspace needs to be cleared first).  Every wait in that handoff is
+ * bounded (20 ms); one that runs out sets bit 0 of the 32-bit status word at
+ * byte offset off_o + k * max(H, I) * 4 rounded up to 256 of ws (off_o from
+ * moe_ws_layout(1, H, I, k); never expected, and that call's y is then
+ * undefined); callers may check that word.  Otherwise (and under graph
+ * capture) the layer runs as two launches.  Both forms give the same bits.  Same arguments
  * and results as moe_route (T = 1, skip mode) followed by moe_expert_ffn
  * (T = 1), bit for bit: topk_ids, topk_w, expert_offsets, perm, slot_pos
  * are written as moe_route writes them, y as moe_expert_ffn.  ws:
@@ -352,6 +363,14 @@ const char* mx_last_variant(void);
  * Process-wide; returns the previous setting, or MX_EINVAL for other values.
  */
 int mx_set_ffn_path(int path);
+
+/*
+ * Single-launch form of moe_layer_decode1 (see there): 1 = used wherever it
+ * applies (the default), 0 = always two launches.  Both give bitwise the same
+ * results; this exists so tests can prove it and benchmarks compare them.
+ * Process-wide; returns the previous setting, or MX_EINVAL for other values.
+ */
+int mx_set_layer1_single_launch(int on);
 
 /*
  * Diagnostic gate/up output (for parity tests of the gate/up GEMM: the

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from block_scaled_fp8xfp4_amd import mxmoe, synth
-from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route
+from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route, quantize
 from gpu_common import Layer, assert_close, dev, host, say, small_workload
 
 pytestmark = pytest.mark.gpu
@@ -119,7 +119,8 @@ def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
     assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
     assert torch.equal(ys.view(torch.int32), ys_ref.view(torch.int32))
     off = (rws + 255) // 256 * 256
-    assert torch.equal(ws[:rws], ws_r), "routed workspace"
+    flags = rws - (k * (((I // 32) * 9 + 1) & ~1) * 8 + 255) // 256 * 256   # the handoff words end the region
+    assert torch.equal(ws[:flags], ws_r[:flags]), "routed workspace"
     assert torch.equal(ws[off:off + sws], ws_s), "shared workspace"
     return host(y), host(ys)
 
@@ -149,3 +150,116 @@ def test_dead_row_still_gets_its_shared_expert():
     y, ys = run_with_shared(layer, inp.logits, shared_operands(layer.cfg, 256, 96), np.array([0.1], np.float32), 0.2)
     assert not np.any(y) and not np.any(np.signbit(y))
     assert np.any(ys)
+
+
+# ---------------------------------------- one launch against two launches
+def status_offset(H, I, k):
+    """Byte offset of the single-launch handoff status word in the workspace."""
+    off_o = mxmoe.moe_ws_layout(1, H, I, k)[2]
+    return off_o + (k * max(H, I) * 4 + 255) // 256 * 256
+
+
+def layer1_call(layer, lg, sv, skip, x, xs, ws, single):
+    c = layer.cfg
+    d = layer.d
+    prev = mxmoe.set_layer1_single_launch(1 if single else 0)
+    try:
+        r = Route(1, c.E, c.k)
+        for key in ("ids", "offsets", "perm", "slot_pos"):
+            getattr(r, key).fill_(-7)
+        y = torch.full((1, c.H), 7.0, device="cuda")
+        mxmoe.moe_layer_decode1(lg, c.k, sv, skip, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], c.E, c.I,
+                                r.ids, r.w, r.offsets, r.perm, r.slot_pos, y, ws)
+        v = mxmoe.last_variant()
+    finally:
+        mxmoe.set_layer1_single_launch(prev)
+    return r, y, v
+
+
+def single_vs_two(layer, logits, survival=None, skip=0.2):
+    """moe_layer_decode1 in one launch and in two launches: every route
+    output, y and the workspace's intermediate (q, its scales and the SwiGLU
+    rows) bit for bit; the handoff status word stays clear."""
+    c = layer.cfg
+    E, k, H, I = c.E, c.k, c.H, c.I
+    d = layer.d
+    x, xs = d["x"][:1].contiguous(), d["x_sc"][:1].contiguous()
+    lg = dev(np.ascontiguousarray(logits[:1], np.float32))
+    sv = None if survival is None else dev(np.ascontiguousarray(survival[:1], np.float32))
+    n = mxmoe.moe_expert_ffn_workspace_bytes(1, H, E, I, k)
+    ws2 = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    r2, y2, v2 = layer1_call(layer, lg, sv, skip, x, xs, ws2, False)
+    assert v2 == "layer1:gu1_decode_topk+down_combine1", v2
+    ws1 = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")   # garbage: nothing needs clearing
+    so = status_offset(H, I, k)
+    ws1[so:so + 4] = 0
+    r1, y1, v1 = layer1_call(layer, lg, sv, skip, x, xs, ws1, True)
+    assert "one launch" in v1, v1
+    assert int(ws1[so:so + 4].view(torch.int32).item()) == 0, "a handoff wait ran out of time"
+    for key in ("ids", "w", "offsets", "perm", "slot_pos"):
+        assert torch.equal(getattr(r1, key), getattr(r2, key)), key
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    live = survival is None or not survival[0] < skip
+    if live:
+        oq, oqs, oo = mxmoe.moe_ws_layout(1, H, I, k)
+        assert torch.equal(ws1[oq:oq + k * I], ws2[oq:oq + k * I]), "q"
+        assert torch.equal(ws1[oqs:oqs + k * I // 32], ws2[oqs:oqs + k * I // 32]), "q scales"
+        assert torch.equal(ws1[oo:oo + k * I * 4], ws2[oo:oo + k * I * 4]), "SwiGLU rows"
+    return host(y1)
+
+
+def test_single_launch_decode_workload():
+    from gpu_common import moe_workload
+    inp, r, layer = moe_workload("decode")
+    y = single_vs_two(layer, inp.logits)
+    err, cos = assert_close(y, layer.oracle_y(r), "layer_decode1 single launch end to end")
+    say(f"layer_decode1 single launch: bitwise equal to two launches; end-to-end {err:.2e}, cosine {cos:.8f}")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(seed=51, T=1, H=256, E=8, k=2, I=64),                  # one down step
+    dict(seed=52, T=1, H=1152, E=384, k=8, I=96),               # 16 logits per lane, a non-exact gate/up step count
+    dict(seed=53, T=1, H=512, E=64, k=1, I=640),                # the largest intermediate of the single launch
+    dict(seed=54, T=1, H=5120, E=384, k=8, I=576),              # the pages' layer shape
+    dict(seed=55, T=1, H=2048, E=256, k=6, I=288),              # k below 8, I not a multiple of 128
+])
+def test_single_launch_shapes(shape):
+    inp, r, layer = small_workload(**shape)
+    single_vs_two(layer, inp.logits)
+
+
+def test_single_launch_dead_row_and_ties():
+    inp, r, layer = small_workload(seed=56, T=1, H=256, E=32, k=4, I=64)
+    y = single_vs_two(layer, inp.logits, np.array([0.1], np.float32), 0.2)
+    assert not np.any(y) and not np.any(np.signbit(y))
+    single_vs_two(layer, np.zeros((1, 32), np.float32), np.array([0.9], np.float32), 0.2)
+
+
+def test_single_launch_alternating_inputs_share_one_workspace():
+    """Calls with different rows on one workspace, one after another: each
+    call waits for its own gate/up results (the tags of the call before never
+    match), so every y equals its own two-launch result bit for bit."""
+    from gpu_common import moe_workload
+    inp, r, layer = moe_workload("decode")
+    c = layer.cfg
+    d = layer.d
+    rng = np.random.default_rng(57)
+    cases = []
+    for i in range(3):
+        lg = dev(rng.standard_normal((1, c.E)).astype(np.float32))
+        xb = torch.from_numpy(rng.standard_normal((1, c.H)).astype(np.float32)).to("cuda").to(torch.bfloat16)
+        xq, xsc = quantize(xb, mxmoe.MX_FMT_E4M3)
+        ws = torch.zeros(mxmoe.moe_expert_ffn_workspace_bytes(1, c.H, c.E, c.I, c.k), dtype=torch.uint8,
+                         device="cuda")
+        _, y, _ = layer1_call(layer, lg, None, 0.2, xq, xsc, ws, False)
+        cases.append((lg, xq, xsc, y))
+    n = mxmoe.moe_expert_ffn_workspace_bytes(1, c.H, c.E, c.I, c.k)
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    so = status_offset(c.H, c.I, c.k)
+    ws[so:so + 4] = 0
+    for it in range(24):
+        lg, xq, xsc, yref = cases[it % 3 if it < 12 else (it * 7) % 3]
+        _, y, v = layer1_call(layer, lg, None, 0.2, xq, xsc, ws, True)
+        assert "one launch" in v
+        assert torch.equal(y.view(torch.int32), yref.view(torch.int32)), f"call {it}"
+    assert int(ws[so:so + 4].view(torch.int32).item()) == 0
