@@ -121,3 +121,33 @@ def test_prefill_router_logits_are_deterministic():
     call()
     assert mxmoe.last_variant().startswith("logits:prefill")
     repeat_bitwise(call, [logits], "prefill router logits", copies=1)
+
+
+def test_single_launch_layer_is_deterministic_beside_other_work():
+    """moe_layer_decode1 in one launch, whose down workgroups wait for the
+    gate/up workgroups' requantized blocks: y, the route outputs and the
+    intermediate bit for bit over every repeat, alone and while the copy
+    stream shares the GPU (its workgroups can delay the gate/up side), and the
+    handoff status word stays clear (no wait ran out of time)."""
+    from block_scaled_fp8xfp4_amd.layer import Route
+    inp, r, layer = moe_workload("decode")
+    c = inp.cfg
+    d = layer.d
+    x, xs = d["x"][:1].contiguous(), d["x_sc"][:1].contiguous()
+    lg = dev(np.ascontiguousarray(inp.logits[:1], np.float32))
+    route = Route(1, c.E, c.k)
+    y = torch.empty((1, c.H), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(mxmoe.moe_expert_ffn_workspace_bytes(1, c.H, c.E, c.I, c.k), dtype=torch.uint8, device="cuda")
+    oq, oqs, oo = mxmoe.moe_ws_layout(1, c.H, c.I, c.k)
+    so = oo + (c.k * max(c.H, c.I) * 4 + 255) // 256 * 256
+
+    def call():
+        mxmoe.moe_layer_decode1(lg, c.k, None, 0.2, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], c.E, c.I,
+                                route.ids, route.w, route.offsets, route.perm, route.slot_pos, y, ws)
+
+    call()
+    assert "one launch" in mxmoe.last_variant()
+    outs = [y, route.ids, route.w, route.offsets, route.perm, route.slot_pos, ws[oq:oq + c.k * c.I],
+            ws[oqs:oqs + c.k * c.I // 32]]
+    repeat_bitwise(call, outs, "single-launch decode layer", copies=1)
+    assert int(ws[so:so + 4].view(torch.int32).item()) == 0, "a handoff wait ran out of time"
