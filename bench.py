@@ -20,6 +20,7 @@ Prints ONE JSON line.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -43,11 +44,17 @@ def log(msg):
 
 
 def kernel_sources_hash():
+    """Hash of the library's code: every file under csrc/ with its comments
+    removed and its whitespace collapsed, so that a comment-only edit keeps
+    the profiles taken on the same code valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp8xfp4_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,6 +34,12 @@
 //                       k SwiGLU rows to FP8 blocks in LDS while its W2 rows
 //                       stream in, runs the down chains of all k slots and
 //                       the combine, so o never leaves the chip.
+//   layer1_kernel       the same layer in ONE launch (moe_layer_decode1, k <=
+//                       8): gate/up workgroups of one requant block each
+//                       (four wavefronts = the gu1 tile four times) hand the
+//                       block's FP8 codes to down + combine workgroups (16
+//                       output columns, two slots per wavefront) through
+//                       tagged words in the workspace; every wait is bounded.
 // Prefill path (hundreds of rows per expert, matrix-core bound):
 //   gu_prefill_kernel   expert tile of up to 128 rows x 128 intermediate
 //                       columns (256 W13 rows) per workgroup, 2 x 2
