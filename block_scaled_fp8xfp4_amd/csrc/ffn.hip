@@ -837,21 +837,22 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
 // ------------------------------------------------ single-launch layer (T = 1) ==
 // moe_layer_decode1 in one launch: gate/up workgroups (one per slot and block
 // of 32 intermediate columns, four wavefronts of 8 columns each: the
-// gu1_kernel tile per wavefront) and down + combine workgroups (32 output
-// columns each, two slots per wavefront) in one grid.  A gate/up workgroup
+// gu1_kernel tile per wavefront) and down + combine workgroups (L1_COLS = 16
+// output columns each, two slots per wavefront) in one grid.  A gate/up workgroup
 // requantizes its block itself (the block is whole in the workgroup) and
 // hands the 32 E4M3 codes and the E8M0 code to every down workgroup through
 // the workspace: nine 8-byte words, each four payload bytes and the call's
 // 32-bit tag, written by 64-bit system-scope stores (they reach memory whole).
 // A down wavefront reads a slot's words with system-scope loads (which read
-// memory, never a stale cached copy) until every word carries the tag.  Tags are unique per call in the process, so
-// words of earlier calls, or garbage in a fresh workspace, never match and
+// memory, never a stale cached copy) until every word carries the tag.  Tags
+// are unique per call in the process, so words of earlier calls, or garbage
+// in a fresh workspace, never match and
 // nothing has to be cleared.  Gate/up workgroups have lower indices than down
 // workgroups and never wait, so they are dispatched first; every wait is
 // bounded in wall-clock time (a down workgroup whose time runs out sets bit 0
 // of *status, and that call's result is undefined).
 struct Handoff {
-  uint64_t* words;                                              // [k][I/32][9] (payload, tag) words
+  uint64_t* words;                                              // [k][l1_slot_words(I)]: (payload, tag) words
   uint32_t* status;                                             // bit 0: a wait ran past its limit
   uint32_t tag;                                                 // this call's tag
   long long limit;                                              // wall-clock ticks one down workgroup may wait
