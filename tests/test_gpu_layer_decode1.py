@@ -263,3 +263,35 @@ def test_single_launch_alternating_inputs_share_one_workspace():
         assert "one launch" in v
         assert torch.equal(y.view(torch.int32), yref.view(torch.int32)), f"call {it}"
     assert int(ws[so:so + 4].view(torch.int32).item()) == 0
+
+
+# ------------------------------------------- seeded sweep of the single launch
+def sweep_shapes(n=12, seed=71):
+    """Single-row layer shapes drawn once from a fixed seed, inside the single
+    launch's domain (k <= 8, I <= 640): H a multiple of 128 up to 5120, E up
+    to 1024, I a multiple of 32, some rows dead."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([8, 33, 128, 256, 300, 512, 1024]))
+        out.append(dict(seed=seed + 1 + i, T=1, H=128 * int(rng.integers(1, 41)), E=E,
+                        k=int(rng.integers(1, min(8, E) + 1)), I=32 * int(rng.integers(1, 21)),
+                        dead=bool(rng.random() < 0.2)))
+    return out
+
+
+@pytest.mark.parametrize("shape", sweep_shapes(), ids=lambda s: f"H{s['H']}_E{s['E']}_k{s['k']}_I{s['I']}")
+def test_single_launch_sweep(shape):
+    """One launch against two, bit for bit, and end to end against the oracle."""
+    s = dict(shape)
+    dead = s.pop("dead")
+    inp = synth.small_moe(s["seed"], s["T"], s["H"], s["E"], s["k"], s["I"])
+    r = oracle.route(inp.logits, s["k"], inp.survival)
+    layer = Layer(inp, np.unique(r["ids"]))                     # the row's experts alone get weights
+    surv = np.array([0.1 if dead else 0.9], np.float32)
+    y = single_vs_two(layer, inp.logits, surv, 0.2)
+    if dead:
+        assert not np.any(y) and not np.any(np.signbit(y))
+    else:
+        err, cos = assert_close(y, layer.oracle_y(r), f"single launch {shape}")
+        say(f"single launch {shape}: end to end {err:.2e}, cosine {cos:.8f}")
