@@ -223,25 +223,30 @@ mx_status moe_expert_ffn_noalloc(const uint8_t* x, const uint8_t* x_sc, int T, i
 
 /*
  * The routed-expert layer of ONE row in one launch (or two): moe_route and
- * moe_expert_ffn for T = 1 fused, the top-k gate running inside the gate/up
- * kernel (every workgroup ranks the row's E logits itself, so the experts'
- * weight loads start without waiting for a route kernel).  With k <= 8,
- * I <= 640 and a stream that is not being captured into a graph,
- * gate/up and the down projection + combine run in ONE launch: the down
- * workgroups stream their W2 rows while the gate/up workgroups run and take
- * each slot's SwiGLU row from them through the workspace (the gate/up side
- * stores a per-call tag beside it once it has reached memory; nothing in the
- * workspace needs to be cleared first).  Every wait in that handoff is
- * bounded (20 ms); one that runs out sets bit 0 of the 32-bit status word at
- * byte offset off_o + k * max(H, I) * 4 rounded up to 256 of ws (off_o from
- * moe_ws_layout(1, H, I, k); never expected, and that call's y is then
- * undefined); callers may check that word.  Otherwise (and under graph
- * capture) the layer runs as two launches.  Both forms give the same bits.  Same arguments
- * and results as moe_route (T = 1, skip mode) followed by moe_expert_ffn
- * (T = 1), bit for bit: topk_ids, topk_w, expert_offsets, perm, slot_pos
- * are written as moe_route writes them, y as moe_expert_ffn.  ws:
- * moe_expert_ffn_workspace_bytes(1, H, E, I, k) bytes.  Supported: the
- * moe_expert_ffn decode-path shapes (H % 128 == 0, H <= 5120, I <= 2048).
+ * moe_expert_ffn for T = 1 fused, the top-k gate running inside every
+ * workgroup (each ranks the row's E logits itself, so the experts' weight
+ * loads start without waiting for a route kernel).  With k <= 8, I <= 640
+ * and a stream that is not being captured into a graph, gate/up and the
+ * down projection + combine run in ONE launch: each gate/up workgroup
+ * requantizes one block of 32 intermediate values and hands the block's FP8
+ * and scale codes to the down workgroups through the workspace, every 8-byte
+ * word carrying a per-call tag beside its payload, while the down
+ * workgroups stream their W2 rows.  Nothing in the workspace needs to be
+ * cleared first (tags are a per-process 32-bit count, so a stale word could
+ * only pass for a fresh one after 2^32 calls that all left it unwritten).
+ * Every wait in that handoff is bounded (20 ms); one that runs out sets bit
+ * 0 of the 32-bit status word at byte offset off_o + k * max(H, I) * 4
+ * rounded up to 256 of ws (off_o from moe_ws_layout(1, H, I, k); never
+ * expected, and that call's y is then undefined); callers may clear and
+ * check that word.  Otherwise (and under graph capture) the layer runs as
+ * two launches.  Both forms give the same bits, and the same arguments and
+ * results as moe_route (T = 1, skip mode) followed by moe_expert_ffn (T = 1):
+ * topk_ids, topk_w, expert_offsets, perm, slot_pos are written as moe_route
+ * writes them, y as moe_expert_ffn, and the workspace's q, its scales and
+ * the SwiGLU rows as moe_expert_ffn at T = 1.  Calls that share a workspace
+ * must not overlap.  ws: moe_expert_ffn_workspace_bytes(1, H, E, I, k) bytes.
+ * Supported: the moe_expert_ffn decode-path shapes (H % 128 == 0, H <= 5120,
+ * I <= 2048).
  * (Forum thread post #6, "How it works": the MoE top-k gate and the routed
  * experts; "Kernel by kernel against B12X": router and routed experts are
  * the decode step's largest groups after the dense projections.)
