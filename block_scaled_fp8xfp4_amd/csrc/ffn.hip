@@ -851,13 +851,8 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
 // workgroups and never wait, so they are dispatched first; every wait is
 // bounded in wall-clock time (a down workgroup whose time runs out sets bit 0
 // of *status, and that call's result is undefined).
-struct Handoff {
-  uint64_t* words;                                              // [k][l1_slot_words(I)]: (payload, tag) words
-  uint32_t* status;                                             // bit 0: a wait ran past its limit
-  uint32_t tag;                                                 // this call's tag
-  long long limit;                                              // wall-clock ticks one down workgroup may wait
-  int nprod;                                                    // gate/up workgroups: k * I / 32
-};
+// (Handoff, next_call_tag and handoff_limit_ticks: mx_launch.hpp; here
+// words = [k][l1_slot_words(I)] (payload, tag) words, nprod = k * I / 32.)
 constexpr int L1_HWORDS = 9;                                    // words per block: 8 x four codes, 1 x scale code
 // words per slot: I / 32 blocks of nine, padded to an even count (whole 16-byte reads)
 __host__ __device__ constexpr int l1_slot_words(int I) { return ((I / 32) * L1_HWORDS + 1) & ~1; }
@@ -1709,10 +1704,11 @@ static void launch_layer1(int hs, hipStream_t stream, const FfnArgs& a, float* a
 
 static std::atomic<bool> g_layer1_onepass{true};
 void set_layer1_onepass(bool on) { g_layer1_onepass.store(on); }
+bool single_launch_on() { return g_layer1_onepass.load(); }
 
 // A tag no earlier call of this process used (a random start, then +1 per
 // call; unique over 2^32 calls).
-static uint32_t next_call_tag() {
+uint32_t next_call_tag() {
   static std::atomic<uint32_t> next{[] {
     uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^ (uint64_t)(uintptr_t)&next;
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;               // splitmix64 finalizer
@@ -1723,7 +1719,7 @@ static uint32_t next_call_tag() {
 }
 
 // Wall-clock ticks in 20 ms on the current device (the limit of one consumer's waits).
-static long long handoff_limit_ticks() {
+long long handoff_limit_ticks() {
   static std::atomic<long long> ticks_per_ms[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;

@@ -58,6 +58,21 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
                       const FusedRoute* fr = nullptr, float* h = nullptr, const Shared1Args* sh = nullptr);
 void set_ffn_phase_events(const hipEvent_t* ev, int n);
 void set_layer1_onepass(bool on);
+
+// Cross-workgroup handoff of the single-launch forms: producers store 8-byte
+// words (payload, then this call's 32-bit tag) with system-scope stores;
+// consumers read them with system-scope loads until every word carries the
+// tag, each wait bounded by `limit` wall-clock ticks (then bit 0 of *status).
+struct Handoff {
+  uint64_t* words;                 // the (payload, tag) words
+  uint32_t* status;                // bit 0: a wait ran past its limit
+  uint32_t tag;                    // this call's tag
+  long long limit;                 // wall-clock ticks one consumer may wait in all
+  int nprod;                       // producer workgroups (they come first in the grid)
+};
+bool single_launch_on();           // mx_set_layer1_single_launch
+uint32_t next_call_tag();          // unique per call in the process (a random start, then +1)
+long long handoff_limit_ticks();   // 20 ms of the current device's wall clock
 // moe_expert_ffn_noalloc: the library's own device scratch array (per GPU,
 // NOALLOC_SCRATCH_BYTES) in place of a caller workspace; *ptr receives its
 // address on the current device.

@@ -105,7 +105,8 @@ def last_variant():
 
 
 def set_layer1_single_launch(on):
-    """1 = moe_layer_decode1 in one launch where it applies, 0 = two launches; returns the previous setting."""
+    """1 = moe_layer_decode1 and moe_shared_expert (T = 1) in one launch where it applies, 0 = two launches;
+    returns the previous setting."""
     r = load().mx_set_layer1_single_launch(int(on))
     if r < 0:
         raise MXError(r, "mx_set_layer1_single_launch")
@@ -257,7 +258,8 @@ def moe_shared_expert_workspace_bytes(T, H, I):
 
 
 def moe_shared_expert(x, x_sc, w13, w13_sc, w2, w2_sc, y, ws, stream=None):
-    """y [T, H] fp32 = shared expert of x (FP8 [T, H] + scales); w13 [2I, H], w2 [H, I] FP8 + scales."""
+    """y [T, H] fp32 = shared expert of x (FP8 [T, H] + scales); w13 [2I, H], w2 [H, I] FP8 + scales.
+    One row (T = 1, H % 128 == 0, I <= 1024, not under graph capture) runs in one launch."""
     T, H = x.shape
     I = w2.shape[1]
     if tuple(w13.shape) != (2 * I, H) or tuple(y.shape) != (T, H):

@@ -327,6 +327,17 @@ mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc,
  * (256-byte aligned, contents ignored): the fp32 gate/up values
  * [T][2I], then the FP8 intermediate [T][I] and its scales [T][I/32], each
  * 256-byte aligned.  Asynchronous on stream.
+ * One row (T = 1, I <= 1024) has decode forms of its own: with H % 128 == 0
+ * and a stream that is not being captured, ONE launch, whose gate/up workgroups (8 intermediate columns
+ * each, all of K) hand their SwiGLU values to the down workgroups through
+ * the workspace as 8-byte words that carry a per-call tag (nothing needs
+ * clearing first); each wait is bounded (20 ms) and one that runs out sets
+ * bit 0 of the 32-bit status word in the workspace's last 256 bytes (offset
+ * moe_shared_expert_workspace_bytes(1, H, I) - 256; never expected, and that
+ * call's y is then undefined; callers may clear and check it).  Otherwise
+ * two launches (gate/up K parts, then the down projection with the SwiGLU
+ * and requant in its prologue).  Both give the same bits as the T > 1 path's
+ * rows.  Calls that share a workspace must not overlap.
  */
 size_t    moe_shared_expert_workspace_bytes(int T, int H, int I);
 mx_status moe_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, int H,
@@ -370,8 +381,9 @@ const char* mx_last_variant(void);
 int mx_set_ffn_path(int path);
 
 /*
- * Single-launch form of moe_layer_decode1 (see there): 1 = used wherever it
- * applies (the default), 0 = always two launches.  Both give bitwise the same
+ * Single-launch forms of moe_layer_decode1 and of moe_shared_expert at T = 1
+ * (see there): 1 = used wherever they apply (the default), 0 = always two
+ * launches.  Both give bitwise the same
  * results; this exists so tests can prove it and benchmarks compare them.
  * Process-wide; returns the previous setting, or MX_EINVAL for other values.
  */

@@ -269,6 +269,19 @@ def test_shared_expert_rejects_bad_arguments(lib):
     assert shared(lib, T=0, x=None, y=None, ws=None) == mxmoe.MX_OK       # nothing to do, nothing launched
 
 
+def test_shared_expert_one_row_workspace_layout(lib):
+    """One row: h, q, q_sc, then the gate/up parts (two-launch form) or the
+    I handoff words (one-launch form; they fit in the parts' room), then the
+    one-launch form's status word in the last 256 bytes."""
+    a = lambda b: (b + 255) // 256 * 256
+    for H, I in ((4096, 576), (256, 64), (5120, 1024), (128, 32)):
+        parts = (H + 1023) // 1024
+        assert I * 8 <= parts * 2 * I * 4
+        assert lib.moe_shared_expert_workspace_bytes(1, H, I) == \
+            a(2 * I * 4) + a(I) + a(I // 32) + a(parts * 2 * I * 4) + 256
+    assert lib.moe_shared_expert_workspace_bytes(1, 256, 1056) == a(2 * 1056 * 4) + a(1056) + a(33)
+
+
 def test_prefetch_rejects_bad_arguments(lib):
     assert lib.mx_prefetch(None, 64, 0, None) == mxmoe.MX_EINVAL
     assert lib.mx_prefetch(ctypes.c_void_p((1 << 20) + 4), 64, 0, None) == mxmoe.MX_EINVAL   # alignment

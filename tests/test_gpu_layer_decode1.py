@@ -81,7 +81,7 @@ def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
     """moe_layer_decode1_shared against moe_layer_decode1 followed by
     moe_shared_expert (T = 1): route outputs, y, y_shared and both workspace
     parts (the routed intermediate and SwiGLU rows; the shared h, q, q_sc and
-    gate/up parts) bit for bit."""
+    gate/up parts of the shared expert's two-launch form) bit for bit."""
     c = layer.cfg
     E, k, H, I = c.E, c.k, c.H, c.I
     sw13, sw13s, sw2, sw2s = sw
@@ -100,8 +100,12 @@ def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
                             ref.offsets, ref.perm, ref.slot_pos, y_ref, ws_r)
     ys_ref = torch.empty((1, H), dtype=torch.float32, device="cuda")
     ws_s = torch.full((sws,), 0xFF, dtype=torch.uint8, device="cuda")
-    mxmoe.moe_shared_expert(x, xs, sw13, sw13s, sw2, sw2s, ys_ref, ws_s)
-    assert mxmoe.last_variant() == "shared:decode1_gemm_parts+down_requant"
+    prev = mxmoe.set_layer1_single_launch(0)                   # the shared expert's two-launch form
+    try:
+        mxmoe.moe_shared_expert(x, xs, sw13, sw13s, sw2, sw2s, ys_ref, ws_s)
+        assert mxmoe.last_variant() == "shared:decode1_gemm_parts+down_requant"
+    finally:
+        mxmoe.set_layer1_single_launch(prev)
     # the fused call
     fz = Route(1, E, k)
     for key in ("ids", "offsets", "perm", "slot_pos"):
@@ -121,7 +125,7 @@ def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
     off = (rws + 255) // 256 * 256
     flags = rws - (k * (((I // 32) * 9 + 1) & ~1) * 8 + 255) // 256 * 256   # the handoff words end the region
     assert torch.equal(ws[:flags], ws_r[:flags]), "routed workspace"
-    assert torch.equal(ws[off:off + sws], ws_s), "shared workspace"
+    assert torch.equal(ws[off:off + sws - 256], ws_s[:sws - 256]), "shared workspace"   # then its status word
     return host(y), host(ys)
 
 
