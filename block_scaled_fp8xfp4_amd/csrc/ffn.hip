@@ -991,36 +991,56 @@ __device__ void layer1_gate_up(const FfnArgs& a, float* __restrict__ abuf, float
 // k products in slot order.  k <= 8, I <= NSD * 128.  (Measured at the
 // decode shape: one 16-column tile per workgroup, 12.6 us per call; two
 // tiles, half as many workgroups, 14.4-14.9 us.)
+// SH (the routed + shared layer): the workgroup also runs the shared
+// expert's down projection of the same 16 columns: wavefront 1 requests the
+// shared W2 rows before anything else, every wavefront polls its share of
+// the shared SwiGLU words in the same read rounds as its slots, and after
+// the rounds the four wavefronts requantize the shared row while wavefront 0
+// combines, then wavefront 1 runs the shared chain (shared1_down_wait's
+// arithmetic: the same bits as the shared expert alone).  A dead row skips
+// the routed work only.  Shared I <= NSD * 128.
 constexpr int L1_COLS = 16;
-template <int NSD, int RP>
-__device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handoff& ho, int tile) {
+template <int NSD, int RP, bool SH = false>
+__device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handoff& ho, int tile,
+                            const Shared1Args& sh = Shared1Args{}, const uint64_t* swords = nullptr) {
   constexpr int QP = NSD * KSTEP + 16;
   constexpr int CT = L1_COLS / 16;
+  constexpr int SN = SH ? NSD * KSTEP : 1;
   __shared__ __attribute__((aligned(16))) uint8_t q1[8][QP];
   __shared__ uint8_t s1[8][NSD * 4];
   __shared__ float olds[8][L1_COLS];
+  __shared__ __attribute__((aligned(16))) float sav[SN];      // SH: the shared SwiGLU row
+  __shared__ __attribute__((aligned(16))) uint8_t sq1[SN];    // SH: its E4M3 codes, K past I zero
+  __shared__ uint8_t ss1[SH ? NSD * 4 : 1];                     // SH: its scale codes
   const uint64_t t0 = wall_clock64();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int H = a.H, I = a.I, nb = I / 32, k = a.k;
   const int nsteps = (I + KSTEP - 1) / KSTEP;
+  u32x4 sblo[SH ? NSD : 1], sbhi[SH ? NSD : 1];
+  uint32_t sbs[SH ? NSD : 1];
+  if constexpr (SH) {
+    if (wave == 1) shared1_w2_rows<true, NSD>(sh, tile, sblo, sbhi, sbs);
+  }
   const float sv = fr.survival != nullptr ? fr.survival[0] : 1.0f;
   TopkState<RP> st;
   topk_begin<RP>(st, fr.logits, a.E);
   const bool live = fr.survival == nullptr || !(sv < fr.skip_below);
-  if (!live) {                                                  // no bucket: +0 (workgroup-uniform exit)
+  if (!live) {                                                  // no bucket: +0 (workgroup-uniform)
     if (tid < L1_COLS) a.y[tile * L1_COLS + tid] = 0.f;
-    return;
+    if constexpr (!SH) return;
   }
   u32x4 bw[2][CT][NSD];
   uint32_t bs[2][CT][NSD];
+  if (live) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {                                 // branch-free: a slot past k reloads slot k - 1's rows
-    const int jj = min(wave + 4 * u, k - 1);
-    topk_rounds<RP>(st, jj + 1);
-    const int64_t r0 = (int64_t)__builtin_amdgcn_readlane(st.idx, jj) * H + tile * L1_COLS + col;
+    for (int u = 0; u < 2; ++u) {                               // branch-free: a slot past k reloads slot k - 1's rows
+      const int jj = min(wave + 4 * u, k - 1);
+      topk_rounds<RP>(st, jj + 1);
+      const int64_t r0 = (int64_t)__builtin_amdgcn_readlane(st.idx, jj) * H + tile * L1_COLS + col;
 #pragma unroll
-    for (int t = 0; t < CT; ++t) load_w2_tile<NSD>(a.w2, a.w2_sc, r0 + 16 * t, I, g, bw[u][t], bs[u][t]);
+      for (int t = 0; t < CT; ++t) load_w2_tile<NSD>(a.w2, a.w2_sc, r0 + 16 * t, I, g, bw[u][t], bs[u][t]);
+    }
   }
   topk_rounds<RP>(st, k);
   const float wt = slot_weight(st.val, k);                      // lane j: the weight of slot j
@@ -1036,7 +1056,8 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
   // 128 + 2 l, 129 + 2 l; word i is part i % 9 of block i / 9 (parts 0..7:
   // four codes, part 8: the scale code)
   const int nwords = nb * L1_HWORDS, nwp = l1_slot_words(I);
-  uint32_t pending = (wave < k ? 1u : 0u) | (wave + 4 < k ? 2u : 0u);
+  uint32_t pending = live ? (wave < k ? 1u : 0u) | (wave + 4 < k ? 2u : 0u) : 0u;
+  if constexpr (SH) pending |= 4u;                              // this wavefront's share of the shared words
   while (pending) {
     u32x4 v[2][2];
 #pragma unroll
@@ -1047,6 +1068,8 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
 #pragma unroll
       for (int h = 0; h < 2; ++h) v[u][h] = __builtin_amdgcn_raw_buffer_load_b128(r, (128 * h + 2 * lane) * 8, 0, 17);
     }
+    u32x4 sv4[2];
+    if constexpr (SH) shared1_words_issue(swords, sh.I, (pending & 4u) != 0u, sv4);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if ((pending >> u) & 1u) {                                // wavefront-uniform
@@ -1090,6 +1113,9 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
         }
       }
     }
+    if constexpr (SH) {
+      if ((pending & 4u) && shared1_words_take(sv4, sh.I, ho.tag, sav)) pending &= ~4u;
+    }
     if (pending == 0) break;
     if ((long long)(wall_clock64() - t0) > ho.limit) {
       if (lane == 0) __hip_atomic_fetch_or(ho.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -1098,20 +1124,33 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
     __builtin_amdgcn_s_sleep(1);
   }
   lds_barrier();
-  if (wave == 0) {
+  if (wave == 0 && live) {
     float acc = 0.f;
     for (int jj = 0; jj < k; ++jj)
       acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), jj)), olds[jj][lane & (L1_COLS - 1)], acc);
     if (lane < L1_COLS) a.y[tile * L1_COLS + lane] = acc;
   }
+  if constexpr (SH) {
+    shared1_requant<NSD>(sh, sav, sq1, ss1, tile == 0);
+    lds_barrier();
+    if (wave == 1) shared1_chain<NSD>(sh, tile, sq1, ss1, sblo, sbhi, sbs);
+  }
 }
 
-template <int NS, bool EXACT, int RP, int NSD>
+// Workgroups [0, k I / 32): routed gate/up; SH: [k I / 32, ho.nprod) the
+// shared expert's gate/up (8 intermediate columns each, its words in the
+// shared workspace's parts region); then H / 16 down workgroups.
+template <int NS, bool EXACT, int RP, int NSD, bool SH>
 __global__ __launch_bounds__(256) void layer1_kernel(FfnArgs a, float* __restrict__ abuf, float* __restrict__ h,
                                                      uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws,
-                                                     FusedRoute fr, Handoff ho) {
-  if ((int)blockIdx.x >= ho.nprod) layer1_down<NSD, RP>(a, fr, ho, (int)blockIdx.x - ho.nprod);
-  else layer1_gate_up<NS, EXACT, RP>(a, abuf, h, qws, qsc_ws, fr, ho);
+                                                     FusedRoute fr, Handoff ho, Shared1Args sh) {
+  const int nr = a.k * (a.I / 32);
+  if ((int)blockIdx.x >= ho.nprod)
+    layer1_down<NSD, RP, SH>(a, fr, ho, (int)blockIdx.x - ho.nprod, sh, reinterpret_cast<const uint64_t*>(sh.pbuf));
+  else if (SH && (int)blockIdx.x >= nr)
+    shared1_gate_up8(sh, reinterpret_cast<uint64_t*>(sh.pbuf), ho.tag, (int)blockIdx.x - nr);
+  else
+    layer1_gate_up<NS, EXACT, RP>(a, abuf, h, qws, qsc_ws, fr, ho);
 }
 
 // ========================================================== prefill path ==
@@ -1684,12 +1723,13 @@ static void launch_gu1(int hs, int groute, int gshared, hipStream_t stream, cons
 
 // The single-launch layer of one row: k * I / 32 gate/up workgroups and
 // H / 32 down + combine workgroups in one grid.
-template <int RP, int NSD>
+template <int RP, int NSD, bool SH = false>
 static void launch_layer1(int hs, hipStream_t stream, const FfnArgs& a, float* abuf, float* h, uint8_t* qws,
-                          uint8_t* qsc, const FusedRoute& fr, const Handoff& ho) {
+                          uint8_t* qsc, const FusedRoute& fr, const Handoff& ho, const Shared1Args& sh) {
   const dim3 grid(ho.nprod + a.H / L1_COLS);
-#define MX_L1(NS_, EX_) \
-  hipLaunchKernelGGL((layer1_kernel<NS_, EX_, RP, NSD>), grid, dim3(256), 0, stream, a, abuf, h, qws, qsc, fr, ho)
+#define MX_L1(NS_, EX_)                                                                                            \
+  hipLaunchKernelGGL((layer1_kernel<NS_, EX_, RP, NSD, SH>), grid, dim3(256), 0, stream, a, abuf, h, qws, qsc, fr, \
+                     ho, sh)
   if (hs == 32) MX_L1(32, true);
   else if (hs == 40) MX_L1(40, true);
   else if (hs == 16) MX_L1(16, true);
@@ -1797,19 +1837,25 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       // One launch when the down projection fits a consumer wavefront (k <= 8,
       // I <= 640) and the stream is not being captured (a graph would replay
       // one tag; the two-launch path below has no tags).
+      // With the shared expert (its I <= 640): its gate/up workgroups after
+      // the routed ones, its down projection inside the down workgroups.
       hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-      if (fr && !sh && a.k <= 8 && is <= 5 && g_layer1_onepass.load() &&
+      if (fr && (!sh || sh->I <= 5 * KSTEP) && a.k <= 8 && is <= 5 && g_layer1_onepass.load() &&
           hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
         const Handoff ho{reinterpret_cast<uint64_t*>(base + oo + obytes + 512), reinterpret_cast<uint32_t*>(queue),
-                         next_call_tag(), handoff_limit_ticks(), a.k * (a.I / 32)};
-        if (is <= 2) {
-          if (a.E <= 256) launch_layer1<4, 2>(hs, stream, a, o, h, qws, qsc, *fr, ho);
-          else launch_layer1<16, 2>(hs, stream, a, o, h, qws, qsc, *fr, ho);
+                         next_call_tag(), handoff_limit_ticks(), a.k * (a.I / 32) + (sh ? sh->I / 8 : 0)};
+        if (sh) {
+          if (a.E <= 256) launch_layer1<4, 5, true>(hs, stream, a, o, h, qws, qsc, *fr, ho, *sh);
+          else launch_layer1<16, 5, true>(hs, stream, a, o, h, qws, qsc, *fr, ho, *sh);
+        } else if (is <= 2) {
+          if (a.E <= 256) launch_layer1<4, 2>(hs, stream, a, o, h, qws, qsc, *fr, ho, shv);
+          else launch_layer1<16, 2>(hs, stream, a, o, h, qws, qsc, *fr, ho, shv);
         } else {
-          if (a.E <= 256) launch_layer1<4, 5>(hs, stream, a, o, h, qws, qsc, *fr, ho);
-          else launch_layer1<16, 5>(hs, stream, a, o, h, qws, qsc, *fr, ho);
+          if (a.E <= 256) launch_layer1<4, 5>(hs, stream, a, o, h, qws, qsc, *fr, ho, shv);
+          else launch_layer1<16, 5>(hs, stream, a, o, h, qws, qsc, *fr, ho, shv);
         }
-        *variant = "layer1:gate_up_topk+down_combine (one launch)";
+        *variant = sh ? "layer1_shared:gate_up_topk+shared_gate_up+down_combine+shared_down (one launch)"
+                      : "layer1:gate_up_topk+down_combine (one launch)";
         phase(1, stream);
         phase(2, stream);
         phase(3, stream);

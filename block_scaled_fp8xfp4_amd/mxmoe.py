@@ -105,7 +105,7 @@ def last_variant():
 
 
 def set_layer1_single_launch(on):
-    """1 = moe_layer_decode1 and moe_shared_expert (T = 1) in one launch where it applies, 0 = two launches;
+    """1 = moe_layer_decode1(_shared) and moe_shared_expert (T = 1) in one launch where it applies, 0 = two;
     returns the previous setting."""
     r = load().mx_set_layer1_single_launch(int(on))
     if r < 0:
@@ -235,7 +235,7 @@ def moe_layer_decode1_shared(logits, k, survival, skip_below, x, x_sc, w13, w13_
                              sw13, sw13_sc, sw2, sw2_sc, topk_ids, topk_w, expert_offsets, perm, slot_pos, y,
                              y_shared, ws, stream=None):
     """moe_layer_decode1 plus the row's shared expert (sw13 FP8 [2Is, H], sw2 FP8 [H, Is] + scales) in the
-    same two launches; y_shared [H] fp32 as moe_shared_expert."""
+    same launches (one where moe_layer_decode1 takes one and Is <= 640); y_shared [H] fp32 as moe_shared_expert."""
     H = x.shape[-1]
     Is = sw2.shape[-1]
     _check(load().moe_layer_decode1_shared(_ptr(logits), E, k, _ptr(survival), float(skip_below), _ptr(x), _ptr(x_sc),

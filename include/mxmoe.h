@@ -260,14 +260,21 @@ mx_status moe_layer_decode1(const float* logits, int E, int k, const float* surv
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The whole MoE layer of ONE row, routed and shared experts, in the same two
- * launches: moe_layer_decode1 with the shared expert's tiles carried by its
- * kernels (the shared expert's gate/up parts beside the routed gate/up, its
- * down projection beside the routed down projection and combine), instead of
- * a separate moe_shared_expert call of two more launches (forum thread post
- * #6, "Kernel by kernel against B12X": the shared expert runs beside the
- * routed experts on a side stream; TP4 README, settings table, row
- * "Kernels").  Results, bit for bit: topk_ids, topk_w, expert_offsets, perm,
+ * The whole MoE layer of ONE row, routed and shared experts, in the launches
+ * of moe_layer_decode1 alone, with the shared expert's work carried by its
+ * kernels instead of a separate moe_shared_expert call (forum thread post #6,
+ * "Kernel by kernel against B12X": the shared expert runs beside the routed
+ * experts on a side stream; TP4 README, settings table, row "Kernels").
+ * Where moe_layer_decode1 runs in one launch and Is <= 640, this is ONE
+ * launch too: the shared gate/up workgroups (8 intermediate columns each)
+ * run beside the routed ones and hand their SwiGLU values, as tagged words
+ * in the shared workspace part, to the down workgroups, which run the shared
+ * down projection of their 16 columns beside the routed one; every wait is
+ * bounded, and one that runs out sets bit 0 of the status word at the offset
+ * moe_layer_decode1 documents (in the routed part).  Otherwise two launches
+ * (the shared gate/up K parts beside the routed gate/up, the shared down
+ * tiles beside the routed down projection and combine).  Results, bit for
+ * bit: topk_ids, topk_w, expert_offsets, perm,
  * slot_pos and y as moe_layer_decode1; y_shared [H] fp32 as
  * moe_shared_expert(x, x_sc, T = 1, H, sw13, sw13_sc, sw2, sw2_sc, Is).  The
  * skip mask applies to the routed experts only (a dead row still gets its
@@ -381,8 +388,8 @@ const char* mx_last_variant(void);
 int mx_set_ffn_path(int path);
 
 /*
- * Single-launch forms of moe_layer_decode1 and of moe_shared_expert at T = 1
- * (see there): 1 = used wherever they apply (the default), 0 = always two
+ * Single-launch forms of moe_layer_decode1, moe_layer_decode1_shared and of
+ * moe_shared_expert at T = 1 (see there): 1 = used wherever they apply (the default), 0 = always two
  * launches.  Both give bitwise the same
  * results; this exists so tests can prove it and benchmarks compare them.
  * Process-wide; returns the previous setting, or MX_EINVAL for other values.

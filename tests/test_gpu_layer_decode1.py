@@ -77,11 +77,13 @@ def shared_operands(cfg, H, Is):
     return tuple(dev(t) for t in (q13, s13, q2, s2))
 
 
-def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
-    """moe_layer_decode1_shared against moe_layer_decode1 followed by
-    moe_shared_expert (T = 1): route outputs, y, y_shared and both workspace
-    parts (the routed intermediate and SwiGLU rows; the shared h, q, q_sc and
-    gate/up parts of the shared expert's two-launch form) bit for bit."""
+def run_with_shared(layer, logits, sw, survival=None, skip=0.2, single=True):
+    """moe_layer_decode1_shared (one launch where it applies when `single`,
+    else two) against moe_layer_decode1 followed by moe_shared_expert's
+    two-launch form (T = 1): route outputs, y, y_shared and both workspace
+    parts (the routed intermediate and SwiGLU rows; the shared h, q and q_sc,
+    and with two launches the gate/up parts) bit for bit; the status word of
+    the one-launch form clear."""
     c = layer.cfg
     E, k, H, I = c.E, c.k, c.H, c.I
     sw13, sw13s, sw2, sw2s = sw
@@ -96,6 +98,8 @@ def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
     ref = Route(1, E, k)
     y_ref = torch.empty((1, H), dtype=torch.float32, device="cuda")
     ws_r = torch.full((rws,), 0xFF, dtype=torch.uint8, device="cuda")
+    so = status_offset(H, I, k)
+    ws_r[so:so + 4] = 0                                        # the status word, as in the fused call's workspace
     mxmoe.moe_layer_decode1(lg, k, sv, skip, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], E, I, ref.ids, ref.w,
                             ref.offsets, ref.perm, ref.slot_pos, y_ref, ws_r)
     ys_ref = torch.empty((1, H), dtype=torch.float32, device="cuda")
@@ -115,9 +119,19 @@ def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
     need = mxmoe.moe_layer_decode1_shared_workspace_bytes(H, E, I, k, Is)
     assert need == (rws + 255) // 256 * 256 + sws
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
-    mxmoe.moe_layer_decode1_shared(lg, k, sv, skip, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], E, I,
-                                   sw13, sw13s, sw2, sw2s, fz.ids, fz.w, fz.offsets, fz.perm, fz.slot_pos, y, ys, ws)
-    assert mxmoe.last_variant().startswith("layer1_shared:")
+    ws[so:so + 4] = 0
+    prev = mxmoe.set_layer1_single_launch(1 if single else 0)
+    try:
+        mxmoe.moe_layer_decode1_shared(lg, k, sv, skip, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], E, I,
+                                       sw13, sw13s, sw2, sw2s, fz.ids, fz.w, fz.offsets, fz.perm, fz.slot_pos, y, ys,
+                                       ws)
+        v = mxmoe.last_variant()
+    finally:
+        mxmoe.set_layer1_single_launch(prev)
+    one = single and k <= 8 and I <= 640 and Is <= 640
+    assert v.startswith("layer1_shared:") and ("one launch" in v) == one, v
+    if one:
+        assert int(ws[so:so + 4].view(torch.int32).item()) == 0, "a handoff wait ran out of time"
     for key in ("ids", "w", "offsets", "perm", "slot_pos"):
         assert torch.equal(getattr(fz, key), getattr(ref, key)), key
     assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
@@ -125,35 +139,82 @@ def run_with_shared(layer, logits, sw, survival=None, skip=0.2):
     off = (rws + 255) // 256 * 256
     flags = rws - (k * (((I // 32) * 9 + 1) & ~1) * 8 + 255) // 256 * 256   # the handoff words end the region
     assert torch.equal(ws[:flags], ws_r[:flags]), "routed workspace"
-    assert torch.equal(ws[off:off + sws - 256], ws_s[:sws - 256]), "shared workspace"   # then its status word
+    a256 = lambda b: (b + 255) // 256 * 256
+    hq = a256(2 * Is * 4) + a256(Is) + a256(Is // 32)             # shared h, q, q_sc; then its parts or words
+    assert torch.equal(ws[off:off + hq], ws_s[:hq]), "shared workspace (h, q, q_sc)"
+    if not one:
+        assert torch.equal(ws[off:off + sws - 256], ws_s[:sws - 256]), "shared workspace (gate/up parts)"
     return host(y), host(ys)
 
 
-def test_decode_workload_with_shared_expert_bitwise():
+@pytest.mark.parametrize("single", [True, False], ids=["one_launch", "two_launches"])
+def test_decode_workload_with_shared_expert_bitwise(single):
     from gpu_common import moe_workload
     inp, r, layer = moe_workload("decode")
     c = inp.cfg
-    y, ys = run_with_shared(layer, inp.logits, shared_operands(c, c.H, c.I))
+    y, ys = run_with_shared(layer, inp.logits, shared_operands(c, c.H, c.I), single=single)
     assert np.any(ys) and np.any(y)
-    say("layer_decode1_shared: routed and shared outputs bitwise equal to the two separate calls")
+    say(f"layer_decode1_shared ({'one launch' if single else 'two launches'}): routed and shared outputs "
+        "bitwise equal to the separate calls")
 
 
+@pytest.mark.parametrize("single", [True, False], ids=["one_launch", "two_launches"])
 @pytest.mark.parametrize("shape,Is", [
     (dict(seed=41, T=1, H=256, E=8, k=2, I=64), 64),
     (dict(seed=42, T=1, H=1152, E=384, k=8, I=96), 160),          # K tail in the shared down projection
-    (dict(seed=43, T=1, H=512, E=64, k=16, I=160), 1024),         # the largest shared intermediate
+    (dict(seed=43, T=1, H=512, E=64, k=16, I=160), 1024),         # the largest shared intermediate (two launches)
     (dict(seed=45, T=1, H=2048, E=32, k=4, I=128), 128),          # two K parts of the shared gate/up
+    (dict(seed=46, T=1, H=5120, E=16, k=8, I=640), 640),         # five K parts; routed and shared I at the limit
+    (dict(seed=47, T=1, H=4096, E=24, k=6, I=576), 32),          # one shared block: four producers
+    (dict(seed=48, T=1, H=128, E=16, k=1, I=32), 576),            # shared I above the routed one
 ])
-def test_small_shapes_with_shared_expert(shape, Is):
+def test_small_shapes_with_shared_expert(shape, Is, single):
     inp, r, layer = small_workload(**shape)
-    run_with_shared(layer, inp.logits, shared_operands(layer.cfg, shape["H"], Is))
+    run_with_shared(layer, inp.logits, shared_operands(layer.cfg, shape["H"], Is), single=single)
 
 
-def test_dead_row_still_gets_its_shared_expert():
+@pytest.mark.parametrize("single", [True, False], ids=["one_launch", "two_launches"])
+def test_dead_row_still_gets_its_shared_expert(single):
     inp, r, layer = small_workload(seed=44, T=1, H=256, E=32, k=4, I=64)
-    y, ys = run_with_shared(layer, inp.logits, shared_operands(layer.cfg, 256, 96), np.array([0.1], np.float32), 0.2)
+    y, ys = run_with_shared(layer, inp.logits, shared_operands(layer.cfg, 256, 96), np.array([0.1], np.float32), 0.2,
+                            single=single)
     assert not np.any(y) and not np.any(np.signbit(y))
     assert np.any(ys)
+
+
+def test_shared_layer_alternating_calls_share_one_workspace():
+    """The routed + shared layer in one launch, called on one workspace for
+    two rows in turn (live, then dead), six times: every call bitwise equal to
+    its first result (the per-call tags keep each wait on that call's words)."""
+    inp, r, layer = small_workload(seed=49, T=2, H=4096, E=32, k=8, I=576)
+    c = layer.cfg
+    sw13, sw13s, sw2, sw2s = shared_operands(c, c.H, 576)
+    d = layer.d
+    need = mxmoe.moe_layer_decode1_shared_workspace_bytes(c.H, c.E, c.I, c.k, 576)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    so = status_offset(c.H, c.I, c.k)
+    ws[so:so + 4] = 0
+    firsts = {}
+    for it in range(6):
+        for row, surv in ((0, 1.0), (1, 0.1)):
+            x, xs = d["x"][row:row + 1].contiguous(), d["x_sc"][row:row + 1].contiguous()
+            lg = dev(np.ascontiguousarray(inp.logits[row:row + 1], np.float32))
+            sv = dev(np.array([surv], np.float32))
+            rt = Route(1, c.E, c.k)
+            y = torch.full((1, c.H), 7.0, device="cuda")
+            ys = torch.full((1, c.H), 7.0, device="cuda")
+            mxmoe.moe_layer_decode1_shared(lg, c.k, sv, 0.2, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], c.E,
+                                           c.I, sw13, sw13s, sw2, sw2s, rt.ids, rt.w, rt.offsets, rt.perm,
+                                           rt.slot_pos, y, ys, ws)
+            assert "one launch" in mxmoe.last_variant()
+            out = (host(y), host(ys), host(rt.ids))
+            if row not in firsts:
+                firsts[row] = out
+            for a_, b_ in zip(out, firsts[row]):
+                assert np.array_equal(a_.view(np.uint32), b_.view(np.uint32)), (it, row)
+    assert int(ws[so:so + 4].view(torch.int32).item()) == 0, "a handoff wait ran out of time"
+    assert not np.any(firsts[1][0]) and np.any(firsts[1][1])
+    say("layer_decode1_shared: 12 alternating one-launch calls (live and dead rows) on one workspace, stable")
 
 
 # ---------------------------------------- one launch against two launches
