@@ -151,3 +151,58 @@ def test_single_launch_layer_is_deterministic_beside_other_work():
             ws[oqs:oqs + c.k * c.I // 32]]
     repeat_bitwise(call, outs, "single-launch decode layer", copies=1)
     assert int(ws[so:so + 4].view(torch.int32).item()) == 0, "a handoff wait ran out of time"
+
+
+def test_single_launch_shared_forms_are_deterministic_beside_other_work():
+    """The shared expert of one row in one launch and the routed + shared
+    layer in one launch (their down workgroups wait for the shared gate/up
+    workgroups' SwiGLU words): y, y_shared and the shared h, q, q_sc bit for
+    bit over every repeat, alone and beside the copy stream; the status
+    words stay clear."""
+    from block_scaled_fp8xfp4_amd.layer import Route
+    inp, r, layer = moe_workload("decode")
+    c = inp.cfg
+    d = layer.d
+    x, xs = d["x"][:1].contiguous(), d["x_sc"][:1].contiguous()
+    lg = dev(np.ascontiguousarray(inp.logits[:1], np.float32))
+    w13, w2 = synth.shared_expert_weights(c)
+    q13, s13 = oracle.quantize_e4m3(w13)
+    q2, s2 = oracle.quantize_e4m3(w2)
+    sw = tuple(dev(t) for t in (q13, s13, q2, s2))
+    Is = c.I
+    a256 = lambda b: (b + 255) // 256 * 256
+    hq = a256(2 * Is * 4) + a256(Is) + a256(Is // 32)
+    # the shared expert alone
+    sws = mxmoe.moe_shared_expert_workspace_bytes(1, c.H, Is)
+    ws_s = torch.zeros(sws, dtype=torch.uint8, device="cuda")
+    ys = torch.empty((1, c.H), dtype=torch.float32, device="cuda")
+
+    def call_shared():
+        mxmoe.moe_shared_expert(x, xs, *sw, ys, ws_s)
+
+    call_shared()
+    assert "one launch" in mxmoe.last_variant()
+    repeat_bitwise(call_shared, [ys, ws_s[:hq]], "single-launch shared expert", copies=1)
+    assert int(ws_s[sws - 256:sws - 252].view(torch.int32).item()) == 0, "a handoff wait ran out of time"
+    # the routed + shared layer
+    route = Route(1, c.E, c.k)
+    y = torch.empty((1, c.H), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((1, c.H), dtype=torch.float32, device="cuda")
+    need = mxmoe.moe_layer_decode1_shared_workspace_bytes(c.H, c.E, c.I, c.k, Is)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    rws = mxmoe.moe_expert_ffn_workspace_bytes(1, c.H, c.E, c.I, c.k)
+    off = a256(rws)
+    oq, oqs, oo = mxmoe.moe_ws_layout(1, c.H, c.I, c.k)
+    so = oo + (c.k * max(c.H, c.I) * 4 + 255) // 256 * 256
+
+    def call_layer():
+        mxmoe.moe_layer_decode1_shared(lg, c.k, None, 0.2, x, xs, d["w13"], d["w13_sc"], d["w2"], d["w2_sc"], c.E,
+                                       c.I, *sw, route.ids, route.w, route.offsets, route.perm, route.slot_pos, y, y2,
+                                       ws)
+
+    call_layer()
+    assert "one launch" in mxmoe.last_variant()
+    outs = [y, y2, route.ids, route.w, ws[oq:oq + c.k * c.I], ws[off:off + hq]]
+    repeat_bitwise(call_layer, outs, "single-launch routed + shared layer", copies=1)
+    assert int(ws[so:so + 4].view(torch.int32).item()) == 0, "a handoff wait ran out of time"
+    assert torch.equal(y2, ys), "y_shared differs from the shared expert alone"
