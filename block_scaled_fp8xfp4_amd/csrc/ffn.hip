@@ -1125,9 +1125,13 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
   }
   lds_barrier();
   if (wave == 0 && live) {
+    float ov[8];                                                // every slot's product read at once (k <= 8)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) ov[jj] = olds[jj][lane & (L1_COLS - 1)];
     float acc = 0.f;
-    for (int jj = 0; jj < k; ++jj)
-      acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), jj)), olds[jj][lane & (L1_COLS - 1)], acc);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      if (jj < k) acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), jj)), ov[jj], acc);
     if (lane < L1_COLS) a.y[tile * L1_COLS + lane] = acc;
   }
   if constexpr (SH) {
