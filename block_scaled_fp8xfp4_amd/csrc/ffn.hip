@@ -854,8 +854,9 @@ __global__ __launch_bounds__(256, 2) void down_combine1_kernel(FfnArgs a, const 
 // (Handoff, next_call_tag and handoff_limit_ticks: mx_launch.hpp; here
 // words = [k][l1_slot_words(I)] (payload, tag) words, nprod = k * I / 32.)
 constexpr int L1_HWORDS = 9;                                    // words per block: 8 x four codes, 1 x scale code
-// words per slot: I / 32 blocks of nine, padded to an even count (whole 16-byte reads)
-__host__ __device__ constexpr int l1_slot_words(int I) { return ((I / 32) * L1_HWORDS + 1) & ~1; }
+constexpr int L1_BWORDS = 16;                                   // a block's nine words in a 128-byte line of their own
+constexpr int L1_BCHUNKS = 5;                                   // 16-byte reads that cover a block's nine words
+__host__ __device__ constexpr int l1_slot_words(int I) { return (I / 32) * L1_BWORDS; }
 
 // Gate/up of one block of 32 intermediate columns of slot j: wavefront w
 // computes columns [32 b + 8 w, +8) exactly as gu1_kernel's item does (the
@@ -956,7 +957,7 @@ __device__ void layer1_gate_up(const FfnArgs& a, float* __restrict__ abuf, float
       __builtin_amdgcn_wave_barrier();
       if (lane < L1_HWORDS) {
         const uint32_t pay = lane < 8 ? reinterpret_cast<const uint32_t*>(qb)[lane] : sc;
-        __hip_atomic_store(ho.words + (int64_t)j * l1_slot_words(I) + b * L1_HWORDS + lane, (uint64_t)pay | ((uint64_t)ho.tag << 32),
+        __hip_atomic_store(ho.words + (int64_t)j * l1_slot_words(I) + b * L1_BWORDS + lane, (uint64_t)pay | ((uint64_t)ho.tag << 32),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         if (lane < 8) reinterpret_cast<uint32_t*>(qws + (int64_t)p0 * I + 32 * b)[lane] = pay;
         else qsc_ws[(int64_t)p0 * nb + b] = (uint8_t)sc;
@@ -1050,12 +1051,12 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
   }
   for (int idx = lane; idx < 2 * (NSD * 4 - nb); idx += 64)
     s1[wave + 4 * (idx / (NSD * 4 - nb))][nb + idx % (NSD * 4 - nb)] = 127;
-  // the slots' words, coalesced: a slot's I / 32 * 9 words (<= 180, padded
-  // to an even count so that no 16-byte read straddles the end of the range)
-  // are read as 16-byte chunks, lane l holding words 2 l, 2 l + 1 and
-  // 128 + 2 l, 129 + 2 l; word i is part i % 9 of block i / 9 (parts 0..7:
-  // four codes, part 8: the scale code)
-  const int nwords = nb * L1_HWORDS, nwp = l1_slot_words(I);
+  // the slots' words: a block's nine words sit at the start of its own
+  // 128-byte line and are read as five 16-byte chunks; lane l reads chunks
+  // c = l and c = 64 + l of each slot (block c / 5, parts 2 (c % 5) and
+  // 2 (c % 5) + 1; part 9 is padding; parts 0..7: four codes, part 8: the
+  // scale code)
+  const int nchunks = nb * L1_BCHUNKS, nwp = l1_slot_words(I);
   uint32_t pending = live ? (wave < k ? 1u : 0u) | (wave + 4 < k ? 2u : 0u) : 0u;
   if constexpr (SH) pending |= 4u;                              // this wavefront's share of the shared words
   while (pending) {
@@ -1066,7 +1067,10 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(ho.words + (int64_t)(wave + 4 * u) * nwp), (short)0, bytes, 0x00020000);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) v[u][h] = __builtin_amdgcn_raw_buffer_load_b128(r, (128 * h + 2 * lane) * 8, 0, 17);
+      for (int h = 0; h < 2; ++h) {
+        const int c = 64 * h + lane;
+        v[u][h] = __builtin_amdgcn_raw_buffer_load_b128(r, (c / L1_BCHUNKS) * 128 + (c % L1_BCHUNKS) * 16, 0, 17);
+      }
     }
     u32x4 sv4[2];
     if constexpr (SH) shared1_words_issue(swords, sh.I, (pending & 4u) != 0u, sv4);
@@ -1078,15 +1082,16 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            ok = ok && (128 * h + 2 * lane + e >= nwords || v[u][h][2 * e + 1] == ho.tag);
+            ok = ok && (64 * h + lane >= nchunks || 2 * ((64 * h + lane) % L1_BCHUNKS) + e >= L1_HWORDS ||
+                        v[u][h][2 * e + 1] == ho.tag);
         if (__ballot(ok) == ~0ull) {
           const int jj = wave + 4 * u;
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-              const int wi = 128 * h + 2 * lane + e, blk = wi / L1_HWORDS, part = wi % L1_HWORDS;
-              if (wi < nwords) {
+              const int c = 64 * h + lane, blk = c / L1_BCHUNKS, part = 2 * (c % L1_BCHUNKS) + e;
+              if (c < nchunks && part < L1_HWORDS) {
                 if (part < 8) *reinterpret_cast<uint32_t*>(&q1[jj][32 * blk + 4 * part]) = v[u][h][2 * e];
                 else s1[jj][blk] = (uint8_t)v[u][h][2 * e];
               }

@@ -137,7 +137,7 @@ def run_with_shared(layer, logits, sw, survival=None, skip=0.2, single=True):
     assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
     assert torch.equal(ys.view(torch.int32), ys_ref.view(torch.int32))
     off = (rws + 255) // 256 * 256
-    flags = rws - (k * (((I // 32) * 9 + 1) & ~1) * 8 + 255) // 256 * 256   # the handoff words end the region
+    flags = rws - (k * (I // 32) * 128 + 255) // 256 * 256     # the handoff words (a 128-byte line per block) end the region
     assert torch.equal(ws[:flags], ws_r[:flags]), "routed workspace"
     a256 = lambda b: (b + 255) // 256 * 256
     hq = a256(2 * Is * 4) + a256(Is) + a256(Is // 32)             # shared h, q, q_sc; then its parts or words
