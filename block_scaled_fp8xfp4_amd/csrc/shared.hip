@@ -56,11 +56,12 @@ static size_t a256(size_t b) { return (b + 255) / 256 * 256; }
 static bool one_row_path(int T, int I) { return T == 1 && I <= KPART; }
 
 // [h: T x 2I fp32][q: T x I][q_sc: T x I/32], then on the one-row path
-// [parts: the gate/up parts (two launches) or the I handoff words (one)]
-// [status word, 256 bytes]
+// [parts: the gate/up parts (two launches) or the handoff words, I / 8
+// lines of 128 bytes (one)][status word, 256 bytes]
 size_t shared_ws_bytes(int T, int H, int I) {
   const size_t base = a256((size_t)T * 2 * I * 4) + a256((size_t)T * I) + a256((size_t)T * (I / 32));
-  return base + (one_row_path(T, I) ? a256((size_t)((H + KPART - 1) / KPART) * 2 * I * 4) + 256 : 0);
+  const size_t parts = (size_t)((H + KPART - 1) / KPART) * 2 * I * 4;
+  return base + (one_row_path(T, I) ? a256(parts > shared1_words_bytes(I) ? parts : shared1_words_bytes(I)) + 256 : 0);
 }
 
 Shared1Args shared1_args(const uint8_t* x, const uint8_t* x_sc, int H, const uint8_t* w13, const uint8_t* w13_sc,

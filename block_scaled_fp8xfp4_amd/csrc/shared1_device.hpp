@@ -155,9 +155,12 @@ __device__ __forceinline__ void shared1_down(const Shared1Args& sh, int tile) {
 // ------------------------------------------- one row in one launch: pieces --
 // The single-launch forms (the shared expert alone, and beside the routed
 // experts) hand the SwiGLU row from gate/up workgroups to down workgroups as
-// tagged 8-byte words (payload: the fp32 SwiGLU value of column c at word c;
-// tag: the call's), written with system-scope stores and read with
-// system-scope loads, every wait bounded.
+// tagged 8-byte words (payload: the fp32 SwiGLU value; tag: the call's),
+// written with system-scope stores and read with system-scope loads, every
+// wait bounded.  Columns [8 i, 8 i + 8) sit in the first 64 bytes of their
+// own 128-byte line i (words 16 i + 0..7), so no line takes two gate/up
+// workgroups' stores.
+__host__ __device__ constexpr size_t shared1_words_bytes(int I) { return (size_t)(I / 8) * 128; }
 
 // Gate/up of intermediate columns [8 item, 8 item + 8) over the whole K (256
 // threads): the W13 rows of those 8 gate and 8 up columns, wavefront w
@@ -209,7 +212,7 @@ __device__ __forceinline__ void shared1_gate_up8(const Shared1Args& sh, uint64_t
   if (lane < 16) sh.h[n] = v;
   const float up = __shfl_down(v, 8, 16);                       // lanes 0..7: the gate and up values of column c0 + lane
   if (lane < 8)
-    __hip_atomic_store(words + c0 + lane, (uint64_t)__float_as_uint(swiglu(v, up)) | ((uint64_t)tag << 32),
+    __hip_atomic_store(words + 16 * item + lane, (uint64_t)__float_as_uint(swiglu(v, up)) | ((uint64_t)tag << 32),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
@@ -234,16 +237,20 @@ __device__ __forceinline__ void shared1_w2_rows(const Shared1Args& sh, int tile,
 }
 
 // One read round of the SwiGLU words by one wavefront w (of four): lane l
-// reads 16-byte chunks 64 w + l and 256 + 64 w + l (words 2 c, 2 c + 1; reads
-// past the I words, and every read when `on` is false, return zeros).
+// reads 16-byte chunks c = 64 w + l and 256 + 64 w + l (chunk c: line c / 4,
+// columns 8 (c / 4) + 2 (c % 4) + {0, 1}; reads past the I / 8 lines, and
+// every read when `on` is false, return zeros).
 // shared1_words_take is true when every word of the wavefront's share
 // carries the tag; the values are then in av.  I <= 1024.
 __device__ __forceinline__ void shared1_words_issue(const uint64_t* words, int I, bool on, u32x4 (&v)[2]) {
   const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
   const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)words, (short)0, on ? (uint32_t)I * 8u : 0u, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)words, (short)0, on ? (uint32_t)shared1_words_bytes(I) : 0u, 0x00020000);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) v[h] = __builtin_amdgcn_raw_buffer_load_b128(r, (256 * h + 64 * wave + lane) * 16, 0, 17);
+  for (int h = 0; h < 2; ++h) {
+    const int c = 256 * h + 64 * wave + lane;
+    v[h] = __builtin_amdgcn_raw_buffer_load_b128(r, (c >> 2) * 128 + (c & 3) * 16, 0, 17);
+  }
 }
 __device__ __forceinline__ bool shared1_words_take(const u32x4 (&v)[2], int I, uint32_t tag, float* av) {
   const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
@@ -252,16 +259,16 @@ __device__ __forceinline__ bool shared1_words_take(const u32x4 (&v)[2], int I, u
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int wi = 2 * (256 * h + 64 * wave + lane) + e;
-      ok = ok && (wi >= I || v[h][2 * e + 1] == tag);
+      const int c = 256 * h + 64 * wave + lane;
+      ok = ok && (c >= I / 2 || v[h][2 * e + 1] == tag);        // chunks of lines past I / 8 hold nothing
     }
   if (__ballot(ok) != ~0ull) return false;                      // wavefront-uniform
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int wi = 2 * (256 * h + 64 * wave + lane) + e;
-      if (wi < I) av[wi] = __uint_as_float(v[h][2 * e]);
+      const int c = 256 * h + 64 * wave + lane;
+      if (c < I / 2) av[8 * (c >> 2) + 2 * (c & 3) + e] = __uint_as_float(v[h][2 * e]);
     }
   return true;
 }

@@ -270,15 +270,14 @@ def test_shared_expert_rejects_bad_arguments(lib):
 
 
 def test_shared_expert_one_row_workspace_layout(lib):
-    """One row: h, q, q_sc, then the gate/up parts (two-launch form) or the
-    I handoff words (one-launch form; they fit in the parts' room), then the
-    one-launch form's status word in the last 256 bytes."""
+    """One row: h, q, q_sc, then room for the gate/up parts (two-launch form)
+    or the handoff words (one-launch form: I / 8 lines of 128 bytes), then
+    the one-launch form's status word in the last 256 bytes."""
     a = lambda b: (b + 255) // 256 * 256
-    for H, I in ((4096, 576), (256, 64), (5120, 1024), (128, 32)):
+    for H, I in ((4096, 576), (256, 64), (5120, 1024), (128, 32), (1024, 640)):
         parts = (H + 1023) // 1024
-        assert I * 8 <= parts * 2 * I * 4
         assert lib.moe_shared_expert_workspace_bytes(1, H, I) == \
-            a(2 * I * 4) + a(I) + a(I // 32) + a(parts * 2 * I * 4) + 256
+            a(2 * I * 4) + a(I) + a(I // 32) + a(max(parts * 2 * I * 4, I // 8 * 128)) + 256
     assert lib.moe_shared_expert_workspace_bytes(1, 256, 1056) == a(2 * 1056 * 4) + a(1056) + a(33)
 
 
