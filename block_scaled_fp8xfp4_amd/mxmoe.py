@@ -121,15 +121,27 @@ def set_ffn_path(path):
     return r
 
 
+# Plain ints for the c_void_p arguments: ctypes converts them by the
+# argtypes, which costs less per call than building a c_void_p per argument
+# (at decode sizes the Python side of a call is as long as the kernel).
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = None
 
 
 def _stream(stream):
+    """The given stream handle, else the current torch stream of the current device (its raw handle)."""
+    global _raw_stream
     if stream is not None:
-        return ctypes.c_void_p(stream)
+        return stream
     import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if _raw_stream is None:
+        f = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = (lambda: f(torch.cuda.current_device())) if f is not None else \
+            (lambda: torch.cuda.current_stream().cuda_stream)
+    return _raw_stream()
 
 
 def _check(status, name):
@@ -161,7 +173,7 @@ def moe_router_logits(hidden, w_gate, logits, ws=None, stream=None):
     for t in (hidden, w_gate):
         if t.element_size() != 2 or not t.is_contiguous():
             raise ValueError("moe_router_logits: hidden and w_gate must be contiguous 16-bit (bf16) tensors")
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ws_bytes = 0 if ws is None else ws.nbytes
     _check(load().moe_router_logits(_ptr(hidden), T, H, _ptr(w_gate), E, _ptr(logits), _ptr(ws), ws_bytes,
                                     _stream(stream)), "moe_router_logits")
 
@@ -173,7 +185,7 @@ def moe_route_workspace_bytes(T, E, k):
 def moe_route(logits, k, survival, skip_below, topk_ids, topk_w, expert_offsets, perm, slot_pos, ws, stream=None):
     T, E = logits.shape
     _check(load().moe_route(_ptr(logits), T, E, k, _ptr(survival), float(skip_below), _ptr(topk_ids), _ptr(topk_w),
-                            _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(ws), ws.numel() * ws.element_size(),
+                            _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(ws), ws.nbytes,
                             _stream(stream)), "moe_route")
 
 
@@ -182,7 +194,7 @@ def moe_route_live(logits, k, survival, reuse_below, anchor, topk_ids, topk_w, e
     T, E = logits.shape
     _check(load().moe_route_live(_ptr(logits), T, E, k, _ptr(survival), float(reuse_below), _ptr(anchor),
                                  _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos),
-                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_route_live")
+                                 _ptr(ws), ws.nbytes, _stream(stream)), "moe_route_live")
 
 
 def moe_expert_ffn_workspace_bytes(T, H, E, I, k):
@@ -201,7 +213,7 @@ def moe_expert_ffn(x, x_sc, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_
     T, H = x.shape
     _check(load().moe_expert_ffn(_ptr(x), _ptr(x_sc), T, H, _ptr(topk_w), _ptr(expert_offsets), _ptr(perm),
                                  _ptr(slot_pos), k, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), E, I, _ptr(y),
-                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_expert_ffn")
+                                 _ptr(ws), ws.nbytes, _stream(stream)), "moe_expert_ffn")
 
 
 def moe_expert_ffn_noalloc(x, x_sc, topk_w, expert_offsets, perm, slot_pos, k, w13, w13_sc, w2, w2_sc, E, I, y,
@@ -224,7 +236,7 @@ def moe_layer_decode1(logits, k, survival, skip_below, x, x_sc, w13, w13_sc, w2,
     _check(load().moe_layer_decode1(_ptr(logits), E, k, _ptr(survival), float(skip_below), _ptr(x), _ptr(x_sc), H,
                                     _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I, _ptr(topk_ids), _ptr(topk_w),
                                     _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(y), _ptr(ws),
-                                    ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_decode1")
+                                    ws.nbytes, _stream(stream)), "moe_layer_decode1")
 
 
 def moe_layer_decode1_shared_workspace_bytes(H, E, I, k, Is):
@@ -242,7 +254,7 @@ def moe_layer_decode1_shared(logits, k, survival, skip_below, x, x_sc, w13, w13_
                                            H, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I, _ptr(sw13),
                                            _ptr(sw13_sc), _ptr(sw2), _ptr(sw2_sc), Is, _ptr(topk_ids), _ptr(topk_w),
                                            _ptr(expert_offsets), _ptr(perm), _ptr(slot_pos), _ptr(y), _ptr(y_shared),
-                                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+                                           _ptr(ws), ws.nbytes, _stream(stream)),
            "moe_layer_decode1_shared")
 
 
@@ -265,7 +277,7 @@ def moe_shared_expert(x, x_sc, w13, w13_sc, w2, w2_sc, y, ws, stream=None):
     if tuple(w13.shape) != (2 * I, H) or tuple(y.shape) != (T, H):
         raise ValueError("moe_shared_expert: shape mismatch")
     _check(load().moe_shared_expert(_ptr(x), _ptr(x_sc), T, H, _ptr(w13), _ptr(w13_sc), _ptr(w2), _ptr(w2_sc), I,
-                                    _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+                                    _ptr(y), _ptr(ws), ws.nbytes, _stream(stream)),
            "moe_shared_expert")
 
 
