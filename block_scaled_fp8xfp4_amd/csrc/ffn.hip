@@ -40,6 +40,9 @@
 //                       block's FP8 codes to down + combine workgroups (16
 //                       output columns, two slots per wavefront) through
 //                       tagged words in the workspace; every wait is bounded.
+//                       SH = true (moe_layer_decode1_shared): the shared
+//                       expert's gate/up workgroups join the grid and the
+//                       down workgroups also run its down projection.
 // Prefill path (hundreds of rows per expert, matrix-core bound):
 //   gu_prefill_kernel   expert tile of up to 128 rows x 128 intermediate
 //                       columns (256 W13 rows) per workgroup, 2 x 2
