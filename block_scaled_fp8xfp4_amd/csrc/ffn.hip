@@ -868,7 +868,7 @@ __host__ __device__ constexpr int l1_slot_words(int I) { return (I / 32) * L1_BW
 // maximum, E8M0 code, E4M3 codes: the requant routine of every path) and
 // publishes them; it also writes q, its scale, the fp32 SwiGLU row values
 // and (workgroup 0) the route outputs, as the two-launch path does.
-template <int NS, bool EXACT, int RP>
+template <int NS, bool EXACT, int RP, bool GRAPH>
 __device__ void layer1_gate_up(const FfnArgs& a, float* __restrict__ abuf, float* __restrict__ h,
                                uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws, const FusedRoute& fr,
                                const Handoff& ho) {
@@ -892,6 +892,7 @@ __device__ void layer1_gate_up(const FfnArgs& a, float* __restrict__ abuf, float
   const float sv = fr.survival != nullptr ? fr.survival[0] : 1.0f;   // in flight with the logits
   TopkState<RP> st;
   topk_begin<RP>(st, fr.logits, a.E);
+  const uint32_t ev = handoff_epoch_issue<GRAPH>(ho);          // the graph form's call counter
   const bool live = fr.survival == nullptr || !(sv < fr.skip_below);
   const int j = (int)blockIdx.x / nb, b = (int)blockIdx.x % nb;
   const int c0 = 32 * b + 8 * wave;                             // this wavefront's first intermediate column
@@ -960,7 +961,7 @@ __device__ void layer1_gate_up(const FfnArgs& a, float* __restrict__ abuf, float
       __builtin_amdgcn_wave_barrier();
       if (lane < L1_HWORDS) {
         const uint32_t pay = lane < 8 ? reinterpret_cast<const uint32_t*>(qb)[lane] : sc;
-        __hip_atomic_store(ho.words + (int64_t)j * l1_slot_words(I) + b * L1_BWORDS + lane, (uint64_t)pay | ((uint64_t)ho.tag << 32),
+        __hip_atomic_store(ho.words + (int64_t)j * l1_slot_words(I) + b * L1_BWORDS + lane, (uint64_t)pay | ((uint64_t)handoff_tag<GRAPH>(ho, ev) << 32),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         if (lane < 8) reinterpret_cast<uint32_t*>(qws + (int64_t)p0 * I + 32 * b)[lane] = pay;
         else qsc_ws[(int64_t)p0 * nb + b] = (uint8_t)sc;
@@ -1004,7 +1005,7 @@ __device__ void layer1_gate_up(const FfnArgs& a, float* __restrict__ abuf, float
 // arithmetic: the same bits as the shared expert alone).  A dead row skips
 // the routed work only.  Shared I <= NSD * 128.
 constexpr int L1_COLS = 16;
-template <int NSD, int RP, bool SH = false>
+template <int NSD, int RP, bool SH, bool GRAPH>
 __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handoff& ho, int tile,
                             const Shared1Args& sh = Shared1Args{}, const uint64_t* swords = nullptr) {
   constexpr int QP = NSD * KSTEP + 16;
@@ -1029,6 +1030,7 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
   const float sv = fr.survival != nullptr ? fr.survival[0] : 1.0f;
   TopkState<RP> st;
   topk_begin<RP>(st, fr.logits, a.E);
+  const uint32_t ev = handoff_epoch_issue<GRAPH>(ho);          // the graph form's call counter
   const bool live = fr.survival == nullptr || !(sv < fr.skip_below);
   if (!live) {                                                  // no bucket: +0 (workgroup-uniform)
     if (tid < L1_COLS) a.y[tile * L1_COLS + tid] = 0.f;
@@ -1060,6 +1062,7 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
   // 2 (c % 5) + 1; part 9 is padding; parts 0..7: four codes, part 8: the
   // scale code)
   const int nchunks = nb * L1_BCHUNKS, nwp = l1_slot_words(I);
+  const uint32_t tag = handoff_tag<GRAPH>(ho, ev);
   uint32_t pending = live ? (wave < k ? 1u : 0u) | (wave + 4 < k ? 2u : 0u) : 0u;
   if constexpr (SH) pending |= 4u;                              // this wavefront's share of the shared words
   while (pending) {
@@ -1086,7 +1089,7 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
 #pragma unroll
           for (int e = 0; e < 2; ++e)
             ok = ok && (64 * h + lane >= nchunks || 2 * ((64 * h + lane) % L1_BCHUNKS) + e >= L1_HWORDS ||
-                        v[u][h][2 * e + 1] == ho.tag);
+                        v[u][h][2 * e + 1] == tag);
         if (__ballot(ok) == ~0ull) {
           const int jj = wave + 4 * u;
 #pragma unroll
@@ -1122,7 +1125,7 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
       }
     }
     if constexpr (SH) {
-      if ((pending & 4u) && shared1_words_take(sv4, sh.I, ho.tag, sav)) pending &= ~4u;
+      if ((pending & 4u) && shared1_words_take(sv4, sh.I, tag, sav)) pending &= ~4u;
     }
     if (pending == 0) break;
     if ((long long)(wall_clock64() - t0) > ho.limit) {
@@ -1152,17 +1155,17 @@ __device__ void layer1_down(const FfnArgs& a, const FusedRoute& fr, const Handof
 // Workgroups [0, k I / 32): routed gate/up; SH: [k I / 32, ho.nprod) the
 // shared expert's gate/up (8 intermediate columns each, its words in the
 // shared workspace's parts region); then H / 16 down workgroups.
-template <int NS, bool EXACT, int RP, int NSD, bool SH>
+template <int NS, bool EXACT, int RP, int NSD, bool SH, bool GRAPH>
 __global__ __launch_bounds__(256) void layer1_kernel(FfnArgs a, float* __restrict__ abuf, float* __restrict__ h,
                                                      uint8_t* __restrict__ qws, uint8_t* __restrict__ qsc_ws,
                                                      FusedRoute fr, Handoff ho, Shared1Args sh) {
   const int nr = a.k * (a.I / 32);
   if ((int)blockIdx.x >= ho.nprod)
-    layer1_down<NSD, RP, SH>(a, fr, ho, (int)blockIdx.x - ho.nprod, sh, reinterpret_cast<const uint64_t*>(sh.pbuf));
+    layer1_down<NSD, RP, SH, GRAPH>(a, fr, ho, (int)blockIdx.x - ho.nprod, sh, reinterpret_cast<const uint64_t*>(sh.pbuf));
   else if (SH && (int)blockIdx.x >= nr)
-    shared1_gate_up8(sh, reinterpret_cast<uint64_t*>(sh.pbuf), ho.tag, (int)blockIdx.x - nr);
+    shared1_gate_up8<GRAPH>(sh, reinterpret_cast<uint64_t*>(sh.pbuf), ho, (int)blockIdx.x - nr);
   else
-    layer1_gate_up<NS, EXACT, RP>(a, abuf, h, qws, qsc_ws, fr, ho);
+    layer1_gate_up<NS, EXACT, RP, GRAPH>(a, abuf, h, qws, qsc_ws, fr, ho);
 }
 
 // ========================================================== prefill path ==
@@ -1735,12 +1738,12 @@ static void launch_gu1(int hs, int groute, int gshared, hipStream_t stream, cons
 
 // The single-launch layer of one row: k * I / 32 gate/up workgroups and
 // H / 32 down + combine workgroups in one grid.
-template <int RP, int NSD, bool SH = false>
+template <int RP, int NSD, bool SH = false, bool GRAPH = false>
 static void launch_layer1(int hs, hipStream_t stream, const FfnArgs& a, float* abuf, float* h, uint8_t* qws,
                           uint8_t* qsc, const FusedRoute& fr, const Handoff& ho, const Shared1Args& sh) {
   const dim3 grid(ho.nprod + a.H / L1_COLS);
 #define MX_L1(NS_, EX_)                                                                                            \
-  hipLaunchKernelGGL((layer1_kernel<NS_, EX_, RP, NSD, SH>), grid, dim3(256), 0, stream, a, abuf, h, qws, qsc, fr, \
+  hipLaunchKernelGGL((layer1_kernel<NS_, EX_, RP, NSD, SH, GRAPH>), grid, dim3(256), 0, stream, a, abuf, h, qws, qsc, fr, \
                      ho, sh)
   if (hs == 32) MX_L1(32, true);
   else if (hs == 40) MX_L1(40, true);
@@ -1760,6 +1763,16 @@ bool single_launch_on() { return g_layer1_onepass.load(); }
 
 // A tag no earlier call of this process used (a random start, then +1 per
 // call; unique over 2^32 calls).
+__global__ void handoff_epoch_kernel(uint32_t* epoch) {
+  if (threadIdx.x == 0)
+    __hip_atomic_store(epoch, __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) + 1u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+hipError_t launch_handoff_epoch(uint32_t* epoch, hipStream_t stream) {
+  hipLaunchKernelGGL(handoff_epoch_kernel, dim3(1), dim3(64), 0, stream, epoch);
+  return hipGetLastError();
+}
+
 uint32_t next_call_tag() {
   static std::atomic<uint32_t> next{[] {
     uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^ (uint64_t)(uintptr_t)&next;
@@ -1767,7 +1780,7 @@ uint32_t next_call_tag() {
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     return (uint32_t)(z ^ (z >> 31));
   }()};
-  return next.fetch_add(1);
+  return next.fetch_add(1) & 0x7FFFFFFFu;                      // bit 31 marks the graph form's tags
 }
 
 // Wall-clock ticks in 20 ms on the current device (the limit of one consumer's waits).
@@ -1851,12 +1864,26 @@ hipError_t launch_ffn(const FfnArgs& a, void* ws, int path, hipStream_t stream, 
       // one tag; the two-launch path below has no tags).
       // With the shared expert (its I <= 640): its gate/up workgroups after
       // the routed ones, its down projection inside the down workgroups.
+      // Under graph capture the same launch, preceded by the one-thread
+      // kernel that advances the workspace's call counter (the tag source).
       hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
       if (fr && (!sh || sh->I <= 5 * KSTEP) && a.k <= 8 && is <= 5 && g_layer1_onepass.load() &&
-          hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
-        const Handoff ho{reinterpret_cast<uint64_t*>(base + oo + obytes + 512), reinterpret_cast<uint32_t*>(queue),
-                         next_call_tag(), handoff_limit_ticks(), a.k * (a.I / 32) + (sh ? sh->I / 8 : 0)};
-        if (sh) {
+          hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+          (cap == hipStreamCaptureStatusNone || cap == hipStreamCaptureStatusActive)) {
+        uint32_t* status = reinterpret_cast<uint32_t*>(queue);     // then the call counter
+        const bool graph = cap == hipStreamCaptureStatusActive;
+        if (graph) {
+          const hipError_t e = launch_handoff_epoch(status + 1, stream);
+          if (e != hipSuccess) return e;
+        }
+        const Handoff ho{reinterpret_cast<uint64_t*>(base + oo + obytes + 512), status, graph ? 0u : next_call_tag(),
+                         handoff_limit_ticks(), a.k * (a.I / 32) + (sh ? sh->I / 8 : 0), status + 1, graph ? 1 : 0};
+        if (graph) {                                            // the graph form: one down-step count, NSD = 5
+          if (sh && a.E <= 256) launch_layer1<4, 5, true, true>(hs, stream, a, o, h, qws, qsc, *fr, ho, *sh);
+          else if (sh) launch_layer1<16, 5, true, true>(hs, stream, a, o, h, qws, qsc, *fr, ho, *sh);
+          else if (a.E <= 256) launch_layer1<4, 5, false, true>(hs, stream, a, o, h, qws, qsc, *fr, ho, shv);
+          else launch_layer1<16, 5, false, true>(hs, stream, a, o, h, qws, qsc, *fr, ho, shv);
+        } else if (sh) {
           if (a.E <= 256) launch_layer1<4, 5, true>(hs, stream, a, o, h, qws, qsc, *fr, ho, *sh);
           else launch_layer1<16, 5, true>(hs, stream, a, o, h, qws, qsc, *fr, ho, *sh);
         } else if (is <= 2) {

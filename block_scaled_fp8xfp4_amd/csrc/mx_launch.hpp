@@ -63,16 +63,40 @@ void set_layer1_onepass(bool on);
 // words (payload, then this call's 32-bit tag) with system-scope stores;
 // consumers read them with system-scope loads until every word carries the
 // tag, each wait bounded by `limit` wall-clock ticks (then bit 0 of *status).
+// A launch replayed from a graph cannot carry a fresh host tag; there
+// (graph = 1) a one-thread kernel recorded before it advances the
+// workspace's call counter *epoch, and the call's tag is that count with
+// bit 31 set.  Host tags keep bit 31 clear, so consecutive calls on one
+// workspace never share a tag, whichever form each takes.
 struct Handoff {
   uint64_t* words;                 // the (payload, tag) words
   uint32_t* status;                // bit 0: a wait ran past its limit
-  uint32_t tag;                    // this call's tag
+  uint32_t tag;                    // this call's tag (eager form; bit 31 clear)
   long long limit;                 // wall-clock ticks one consumer may wait in all
   int nprod;                       // producer workgroups (they come first in the grid)
+  const uint32_t* epoch;           // the workspace's call counter (graph form: advanced before the launch)
+  int graph;                       // 1: the graph form (tag = *epoch | 2^31), run by the GRAPH kernels
 };
 bool single_launch_on();           // mx_set_layer1_single_launch
-uint32_t next_call_tag();          // unique per call in the process (a random start, then +1)
+uint32_t next_call_tag();          // unique per call in the process (a random start, then +1), bit 31 clear
 long long handoff_limit_ticks();   // 20 ms of the current device's wall clock
+// Records the epoch advance before a graph-form launch (a kernel: no memset node).
+hipError_t launch_handoff_epoch(uint32_t* epoch, hipStream_t stream);
+
+// The call counter (GRAPH: the kernels built for the graph form; issue early,
+// resolve at first use, so the wait for it lands where the tag is first
+// needed).  An ordinary cached load: an earlier kernel on the stream wrote
+// the counter, which the stream order makes visible.
+template <bool GRAPH>
+__device__ __forceinline__ uint32_t handoff_epoch_issue(const Handoff& ho) {
+  if constexpr (!GRAPH) return 0u;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)ho.epoch, (short)0, 4u, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0);
+}
+template <bool GRAPH>
+__device__ __forceinline__ uint32_t handoff_tag(const Handoff& ho, uint32_t epoch_value) {
+  return GRAPH ? (epoch_value | 0x80000000u) : ho.tag;
+}
 // moe_expert_ffn_noalloc: the library's own device scratch array (per GPU,
 // NOALLOC_SCRATCH_BYTES) in place of a caller workspace; *ptr receives its
 // address on the current device.

@@ -44,10 +44,10 @@ __global__ __launch_bounds__(256) void swiglu_requant_kernel(const float* __rest
 // (shared1_down_wait), which waits on the former's tagged words.  Producers
 // come first in the grid and never wait, so every wait can end; each is
 // bounded by ho.limit.  Same bits as the two-launch form.  H % 128 == 0.
-template <bool TAIL>
+template <bool TAIL, bool GRAPH>
 __global__ __launch_bounds__(256) void shared1_onepass_kernel(Shared1Args sh, Handoff ho) {
-  if ((int)blockIdx.x < ho.nprod) shared1_gate_up8(sh, ho.words, ho.tag, (int)blockIdx.x);
-  else shared1_down_wait<TAIL>(sh, ho, (int)blockIdx.x - ho.nprod);
+  if ((int)blockIdx.x < ho.nprod) shared1_gate_up8<GRAPH>(sh, ho.words, ho, (int)blockIdx.x);
+  else shared1_down_wait<TAIL, GRAPH>(sh, ho, (int)blockIdx.x - ho.nprod);
 }
 
 static size_t a256(size_t b) { return (b + 255) / 256 * 256; }
@@ -85,12 +85,20 @@ hipError_t launch_shared_expert(const uint8_t* x, const uint8_t* x_sc, int T, in
     const Shared1Args sh = shared1_args(x, x_sc, H, w13, w13_sc, w2, w2_sc, I, y, ws);
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (H % KSTEP == 0 && single_launch_on() && hipStreamIsCapturing(stream, &cap) == hipSuccess &&
-        cap == hipStreamCaptureStatusNone) {
-      uint32_t* status = reinterpret_cast<uint32_t*>(base + shared_ws_bytes(1, H, I) - 256);
-      const Handoff ho{reinterpret_cast<uint64_t*>(sh.pbuf), status, next_call_tag(), handoff_limit_ticks(), I / 8};
+        (cap == hipStreamCaptureStatusNone || cap == hipStreamCaptureStatusActive)) {
+      uint32_t* status = reinterpret_cast<uint32_t*>(base + shared_ws_bytes(1, H, I) - 256);   // then the call counter
+      const bool graph = cap == hipStreamCaptureStatusActive;   // captured: the counter advance is recorded first
+      if (graph) {
+        const hipError_t e = launch_handoff_epoch(status + 1, stream);
+        if (e != hipSuccess) return e;
+      }
+      const Handoff ho{reinterpret_cast<uint64_t*>(sh.pbuf), status, graph ? 0u : next_call_tag(), handoff_limit_ticks(),
+                       I / 8, status + 1, graph ? 1 : 0};
       const dim3 grid(I / 8 + H / 16);
-      if (I % KSTEP) hipLaunchKernelGGL(shared1_onepass_kernel<true>, grid, dim3(256), 0, stream, sh, ho);
-      else hipLaunchKernelGGL(shared1_onepass_kernel<false>, grid, dim3(256), 0, stream, sh, ho);
+      if (graph && I % KSTEP) hipLaunchKernelGGL((shared1_onepass_kernel<true, true>), grid, dim3(256), 0, stream, sh, ho);
+      else if (graph) hipLaunchKernelGGL((shared1_onepass_kernel<false, true>), grid, dim3(256), 0, stream, sh, ho);
+      else if (I % KSTEP) hipLaunchKernelGGL((shared1_onepass_kernel<true, false>), grid, dim3(256), 0, stream, sh, ho);
+      else hipLaunchKernelGGL((shared1_onepass_kernel<false, false>), grid, dim3(256), 0, stream, sh, ho);
       *variant = "shared:decode1_onepass(gate_up+down_requant, one launch)";
       return hipGetLastError();
     }

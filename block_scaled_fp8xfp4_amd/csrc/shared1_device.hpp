@@ -168,10 +168,12 @@ __host__ __device__ constexpr size_t shared1_words_bytes(int I) { return (size_t
 // shared1_part's); wavefront 0 adds the parts in part order (shared1_down's
 // sum), writes the 16 h values, and publishes the 8 SwiGLU values as words[c].
 // H % 128 == 0, H <= 16384.
-__device__ __forceinline__ void shared1_gate_up8(const Shared1Args& sh, uint64_t* __restrict__ words, uint32_t tag,
+template <bool GRAPH>
+__device__ __forceinline__ void shared1_gate_up8(const Shared1Args& sh, uint64_t* __restrict__ words, const Handoff& ho,
                                                  int item) {
   constexpr int MAXP = 16;                                      // K parts: H <= 16384
   __shared__ float ps[MAXP][16];
+  const uint32_t ev = handoff_epoch_issue<GRAPH>(ho);           // the graph form's call counter
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
   const int H = sh.H, I = sh.I, nparts = shared1_nparts(H), nsteps = H / KSTEP;
   const int c0 = 8 * item;
@@ -212,7 +214,8 @@ __device__ __forceinline__ void shared1_gate_up8(const Shared1Args& sh, uint64_t
   if (lane < 16) sh.h[n] = v;
   const float up = __shfl_down(v, 8, 16);                       // lanes 0..7: the gate and up values of column c0 + lane
   if (lane < 8)
-    __hip_atomic_store(words + 16 * item + lane, (uint64_t)__float_as_uint(swiglu(v, up)) | ((uint64_t)tag << 32),
+    __hip_atomic_store(words + 16 * item + lane,
+                       (uint64_t)__float_as_uint(swiglu(v, up)) | ((uint64_t)handoff_tag<GRAPH>(ho, ev) << 32),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
@@ -332,7 +335,7 @@ __device__ __forceinline__ void shared1_chain(const Shared1Args& sh, int tile, c
 // expert's own single launch: wavefront 0 requests its 16 W2 rows first; the
 // four wavefronts wait for their shares of the I words, then the requant
 // (tile 0 writes q and q_sc) and wavefront 0's chain.  I <= 1024.
-template <bool TAIL>
+template <bool TAIL, bool GRAPH>
 __device__ void shared1_down_wait(const Shared1Args& sh, const Handoff& ho, int tile) {
   constexpr int NSD = KPART_STEPS;                              // steps of K = I <= 1024
   __shared__ __attribute__((aligned(16))) float av[NSD * KSTEP];
@@ -340,10 +343,12 @@ __device__ void shared1_down_wait(const Shared1Args& sh, const Handoff& ho, int 
   __shared__ uint8_t s1[NSD * 4];
   const uint64_t t0 = wall_clock64();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t ev = handoff_epoch_issue<GRAPH>(ho);           // the graph form's call counter
   u32x4 blo[NSD], bhi[NSD];
   uint32_t bs[NSD];
   if (wave == 0) shared1_w2_rows<TAIL, NSD>(sh, tile, blo, bhi, bs);
-  while (!shared1_words_round(ho.words, sh.I, ho.tag, av)) {
+  const uint32_t tag = handoff_tag<GRAPH>(ho, ev);
+  while (!shared1_words_round(ho.words, sh.I, tag, av)) {
     if ((long long)(wall_clock64() - t0) > ho.limit) {
       if (lane == 0) __hip_atomic_fetch_or(ho.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       break;

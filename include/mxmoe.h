@@ -225,21 +225,23 @@ mx_status moe_expert_ffn_noalloc(const uint8_t* x, const uint8_t* x_sc, int T, i
  * The routed-expert layer of ONE row in one launch (or two): moe_route and
  * moe_expert_ffn for T = 1 fused, the top-k gate running inside every
  * workgroup (each ranks the row's E logits itself, so the experts' weight
- * loads start without waiting for a route kernel).  With k <= 8, I <= 640
- * and a stream that is not being captured into a graph, gate/up and the
- * down projection + combine run in ONE launch: each gate/up workgroup
- * requantizes one block of 32 intermediate values and hands the block's FP8
- * and scale codes to the down workgroups through the workspace, every 8-byte
- * word carrying a per-call tag beside its payload, while the down
- * workgroups stream their W2 rows.  Nothing in the workspace needs to be
- * cleared first (tags are a per-process 32-bit count, so a stale word could
- * only pass for a fresh one after 2^32 calls that all left it unwritten).
- * Every wait in that handoff is bounded (20 ms); one that runs out sets bit
- * 0 of the 32-bit status word at byte offset off_o + k * max(H, I) * 4
- * rounded up to 256 of ws (off_o from moe_ws_layout(1, H, I, k); never
- * expected, and that call's y is then undefined); callers may clear and
- * check that word.  Otherwise (and under graph capture) the layer runs as
- * two launches.  Both forms give the same bits, and the same arguments and
+ * loads start without waiting for a route kernel).  With k <= 8 and
+ * I <= 640, gate/up and the down projection + combine run in ONE launch:
+ * each gate/up workgroup requantizes one block of 32 intermediate values and
+ * hands the block's FP8 and scale codes to the down workgroups through the
+ * workspace, every 8-byte word carrying a per-call tag beside its payload,
+ * while the down workgroups stream their W2 rows.  Nothing in the workspace
+ * needs to be cleared first: an eager call's tag is a per-process count
+ * (bit 31 clear), so a stale word could only pass for a fresh one after 2^31
+ * calls that all left it unwritten; under graph capture a one-thread kernel
+ * recorded before the launch advances a call counter kept in the workspace
+ * (the 32-bit word after the status word below), and each replay's tag is
+ * that count with bit 31 set.  Every wait in that handoff is bounded
+ * (20 ms); one that runs out sets bit 0 of the 32-bit status word at byte
+ * offset off_o + k * max(H, I) * 4 rounded up to 256 of ws (off_o from
+ * moe_ws_layout(1, H, I, k); never expected, and that call's y is then
+ * undefined); callers may clear and check that word.  Otherwise the layer
+ * runs as two launches.  Both forms give the same bits, and the same arguments and
  * results as moe_route (T = 1, skip mode) followed by moe_expert_ffn (T = 1):
  * topk_ids, topk_w, expert_offsets, perm, slot_pos are written as moe_route
  * writes them, y as moe_expert_ffn, and the workspace's q, its scales and
@@ -334,12 +336,15 @@ mx_status fp8_block_gemm(const uint8_t* a, const uint8_t* a_sc,
  * (256-byte aligned, contents ignored): the fp32 gate/up values
  * [T][2I], then the FP8 intermediate [T][I] and its scales [T][I/32], each
  * 256-byte aligned.  Asynchronous on stream.
- * One row (T = 1, I <= 1024) has decode forms of its own: with H % 128 == 0
- * and a stream that is not being captured, ONE launch, whose gate/up workgroups (8 intermediate columns
- * each, all of K) hand their SwiGLU values to the down workgroups through
- * the workspace as 8-byte words that carry a per-call tag (nothing needs
- * clearing first); each wait is bounded (20 ms) and one that runs out sets
- * bit 0 of the 32-bit status word in the workspace's last 256 bytes (offset
+ * One row (T = 1, I <= 1024) has decode forms of its own: with H % 128 == 0,
+ * ONE launch, whose gate/up workgroups (8 intermediate columns each, all of
+ * K) hand their SwiGLU values to the down workgroups through the workspace
+ * as 8-byte words that carry a per-call tag (nothing needs clearing first;
+ * under graph capture the tag comes from a call counter in the workspace,
+ * the 32-bit word after the status word, advanced by a one-thread kernel
+ * recorded before the launch, as moe_layer_decode1 describes); each wait is
+ * bounded (20 ms) and one that runs out sets bit 0 of the 32-bit status
+ * word in the workspace's last 256 bytes (offset
  * moe_shared_expert_workspace_bytes(1, H, I) - 256; never expected, and that
  * call's y is then undefined; callers may clear and check it).  Otherwise
  * two launches (gate/up K parts, then the down projection with the SwiGLU
