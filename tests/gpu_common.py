@@ -255,3 +255,18 @@ def small_workload(seed, T, H, E, k, I, skip=0.0, logits="normal"):
     inp = synth.small_moe(seed, T, H, E, k, I, logits=logits, skip_frac=skip)
     r = oracle.route(inp.logits, k, inp.survival)
     return inp, r, Layer(inp)
+
+
+def shared_operands(cfg, H, Is):
+    """The shared expert's FP8 weights (quantized by the oracle) on the device."""
+    w13, w2 = synth.shared_expert_weights(cfg, H, Is)
+    q13, s13 = oracle.quantize_e4m3(w13)
+    q2, s2 = oracle.quantize_e4m3(w2)
+    return tuple(dev(t) for t in (q13, s13, q2, s2))
+
+
+def status_offset(H, I, k):
+    """Byte offset of the single-launch layer's handoff status word in its
+    workspace (the 32-bit call counter of the graph form follows it)."""
+    off_o = mxmoe.moe_ws_layout(1, H, I, k)[2]
+    return off_o + (k * max(H, I) * 4 + 255) // 256 * 256

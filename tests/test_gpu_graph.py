@@ -9,7 +9,7 @@ import torch
 
 from block_scaled_fp8xfp4_amd import mxmoe, synth
 from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route, quantize
-from gpu_common import dev, host, moe_workload, say
+from gpu_common import dev, host, moe_workload, say, shared_operands, status_offset
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +65,6 @@ def test_graph_single_launch_forms_take_fresh_tags():
     between replays, and must equal the eager calls on its row bit for bit
     (a stale word from the call before could only pass with a repeated tag);
     the status words stay clear."""
-    from test_gpu_layer_decode1 import shared_operands, status_offset
     inp, r, layer = moe_workload("verify")
     c = inp.cfg
     E, k, H, I = c.E, c.k, c.H, c.I

@@ -9,7 +9,7 @@ import torch
 import oracle
 from block_scaled_fp8xfp4_amd import mxmoe, synth
 from block_scaled_fp8xfp4_amd.layer import ExpertFFN, Route, quantize
-from gpu_common import Layer, assert_close, dev, host, say, small_workload
+from gpu_common import Layer, assert_close, dev, host, say, shared_operands, small_workload, status_offset
 
 pytestmark = pytest.mark.gpu
 
@@ -69,14 +69,6 @@ def test_dead_row_and_ties():
 
 
 # ------------------------------------------- routed + shared experts, one row
-def shared_operands(cfg, H, Is):
-    """The shared expert's FP8 weights (quantized by the oracle) on the device."""
-    w13, w2 = synth.shared_expert_weights(cfg, H, Is)
-    q13, s13 = oracle.quantize_e4m3(w13)
-    q2, s2 = oracle.quantize_e4m3(w2)
-    return tuple(dev(t) for t in (q13, s13, q2, s2))
-
-
 def run_with_shared(layer, logits, sw, survival=None, skip=0.2, single=True):
     """moe_layer_decode1_shared (one launch where it applies when `single`,
     else two) against moe_layer_decode1 followed by moe_shared_expert's
@@ -218,12 +210,6 @@ def test_shared_layer_alternating_calls_share_one_workspace():
 
 
 # ---------------------------------------- one launch against two launches
-def status_offset(H, I, k):
-    """Byte offset of the single-launch handoff status word in the workspace."""
-    off_o = mxmoe.moe_ws_layout(1, H, I, k)[2]
-    return off_o + (k * max(H, I) * 4 + 255) // 256 * 256
-
-
 def layer1_call(layer, lg, sv, skip, x, xs, ws, single):
     c = layer.cfg
     d = layer.d
